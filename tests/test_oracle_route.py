@@ -1,0 +1,87 @@
+"""Pins for the oracle's routing and grouping (CPU only).
+
+Routing ("Red Metal dev8 — resident routed top-k layer": positive router weights that
+sum to about one; top-10 of 512 per "Red Lite dev9", section "Inspect the real
+Qwen3-Next model"): the selected ids equal a brute-force full sort by (logit
+descending, id ascending); the weights equal scipy's softmax over all E logits
+renormalised over the selected set; relabelling the experts relabels the selection.
+Grouping: numpy's stable argsort of the ids.
+"""
+import numpy as np
+import pytest
+from scipy.special import softmax
+
+import oracle as O
+import synth
+
+
+def brute_topk(l, k):
+    order = np.lexsort((np.arange(len(l)), -l.astype(np.float64)))
+    return order[:k]
+
+
+@pytest.mark.parametrize("E,k", [(16, 4), (16, 16), (8, 1), (512, 10), (513, 17)])
+def test_route_matches_full_sort_and_softmax(E, k):
+    T = 32
+    lg = synth.logits(T, E, tag=f"rt{E}")
+    ids, w = O.route(lg, k, add_shared=False)
+    for t in range(T):
+        np.testing.assert_array_equal(ids[t], brute_topk(lg[t], k))
+        p = softmax(lg[t].astype(np.float64))
+        ref = p[ids[t]] / p[ids[t]].sum()
+        np.testing.assert_allclose(w[t], ref, rtol=4 * k * 2.0 ** -24, atol=0)
+        assert abs(float(w[t].astype(np.float64).sum()) - 1.0) <= k * 2.0 ** -24 + 2.0 ** -24
+        assert np.all(w[t] > 0)
+
+
+def test_route_ties_go_to_lower_id():
+    l = np.array([[1.0, 3.0, 3.0, 0.5, 3.0, 2.0, 2.0, -1.0]], dtype=np.float32)
+    ids, w = O.route(l, 5, add_shared=False)
+    np.testing.assert_array_equal(ids[0], [1, 2, 4, 5, 6])
+    assert w[0, 0] == w[0, 1] == w[0, 2] and w[0, 3] == w[0, 4]
+
+
+def test_route_relabel_invariance():
+    T, E, k = 16, 64, 10
+    lg = synth.logits(T, E, tag="relabel")
+    perm = np.argsort(synth.u64(3, "perm", E), kind="stable")   # new column j holds old expert perm[j]
+    ids, w = O.route(lg, k, False)
+    ids2, w2 = O.route(lg[:, perm], k, False)
+    inv = np.empty(E, dtype=np.int64)
+    inv[perm] = np.arange(E)
+    # distinct logits, so the selection is unique
+    np.testing.assert_array_equal(perm[ids2], ids)
+    np.testing.assert_array_equal(w2, w)
+
+
+def test_route_shared_slot():
+    lg = synth.logits(3, 512, tag="shared")
+    ids, w = O.route(lg, 10, add_shared=True)
+    assert ids.shape == (3, 11)
+    assert np.all(ids[:, 10] == 512) and np.all(w[:, 10] == 1.0)
+    ids0, w0 = O.route(lg, 10, add_shared=False)
+    np.testing.assert_array_equal(ids[:, :10], ids0)
+    np.testing.assert_array_equal(w[:, :10], w0)
+
+
+def test_route_fp64_twin_close():
+    lg = synth.logits(8, 512, tag="r64")
+    ids, w = O.route(lg, 10, True)
+    ids64, w64 = O.route_f64(lg, 10, True)
+    np.testing.assert_array_equal(ids, ids64)
+    np.testing.assert_allclose(w, w64, rtol=4e-7)
+
+
+@pytest.mark.parametrize("T,E,k,shared", [(1, 512, 10, True), (8, 512, 10, True), (256, 512, 10, False),
+                                          (37, 16, 4, False), (64, 40, 16, True)])
+def test_group_is_stable_sort(T, E, k, shared):
+    lg = synth.logits(T, E, tag=f"grp{T}")
+    ids, _ = O.route(lg, k, shared)
+    n_ids = E + int(shared)
+    counts, offsets, ss, sp = O.group(ids, n_ids)
+    flat = ids.ravel()
+    np.testing.assert_array_equal(counts, np.bincount(flat, minlength=n_ids))
+    np.testing.assert_array_equal(offsets, np.concatenate([[0], np.cumsum(counts)]))
+    np.testing.assert_array_equal(ss, np.argsort(flat, kind="stable"))
+    np.testing.assert_array_equal(sp[ss], np.arange(len(flat)))
+    assert offsets[-1] == T * (k + int(shared))
