@@ -47,6 +47,7 @@ def lib():
         i32 = C.c_int
         sig = {
             "orc_f16_to_f32": (C.c_float, [C.c_uint16]),
+            "orc_set_threads": (None, [i32]),
             "orc_grids_expand": (i32, [P, P, P]),
             "orc_weight": (C.c_float, [P, P, i32, i32]),
             "orc_weight_f64": (C.c_double, [P, P, i32, i32]),
@@ -81,6 +82,10 @@ def _p(a):
 def _chk(rc, what):
     if rc != 0:
         raise ValueError(f"{what} failed with {rc}")
+
+
+def set_threads(n: int) -> None:
+    lib().orc_set_threads(n)
 
 
 def f16_to_f32(h: int) -> float:

@@ -10,6 +10,9 @@
 
 static int g_threads = 1;
 
+/* Threads used by orc_matvec for independent rows (results do not depend on it). */
+void orc_set_threads(int n) { g_threads = n > 1 ? n : 1; }
+
 /* ------------------------------------------------------------------ binary16 */
 
 float orc_f16_to_f32(uint16_t h) {

@@ -47,6 +47,9 @@ typedef struct {
 
 float orc_f16_to_f32(uint16_t h);
 
+/* Threads for the row loop of orc_matvec; every output is computed the same way. */
+void orc_set_threads(int n);
+
 /* Compact rows (symbol j in bits 2j..2j+1) -> value rows.  -1 if a symbol is 3. */
 int orc_grids_expand(const uint16_t *compact_iq2, const uint16_t *compact_iq1, orc_grids *g);
 
