@@ -1,0 +1,200 @@
+"""Routed top-k MoE expert layer on codebook-quantized experts, for MI355X (gfx950).
+
+A thin ctypes binding of ``libmoe.so`` (declared in include/moe.h).  Every function
+here only marshals arguments: torch tensors are passed as device pointers and torch's
+current HIP stream as the stream, and all the work runs in the library's kernels.  The
+library must be built (``python codebook_quantized_routed_amd/_build.py``); importing
+this package without it raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+IQ2XS_LIKE = 1
+IQ1M_LIKE = 2
+MAX_BANKS = 4
+MAX_K = 16
+MAX_IDS = 1024
+
+STATUS = {0: "MOE_OK", -1: "MOE_E_NULL", -2: "MOE_E_SHAPE", -3: "MOE_E_QTYPE", -4: "MOE_E_ALIGN",
+          -5: "MOE_E_WORKSPACE", -6: "MOE_E_HIP"}
+
+EXPORTS = ["moe_abi_version", "moe_status_string", "moe_last_hip_error", "moe_last_hip_error_string", "moe_grids_bytes", "moe_grids_expand", "moe_workspace_bytes",
+           "moe_route_group", "moe_expert_ffn_q", "moe_expert_gateup_q", "moe_expert_down_q",
+           "moe_expert_down_accumulate_q", "moe_accumulate", "moe_dequant_f32", "moe_rmsnorm"]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {STATUS.get(status, status)} ({msg})")
+        self.status = status
+
+
+class Bank(C.Structure):
+    _fields_ = [("qtype", C.c_int32), ("first_expert", C.c_int32), ("n_experts", C.c_int32),
+                ("reserved", C.c_int32), ("gate", C.c_void_p * 3), ("up", C.c_void_p * 3), ("down", C.c_void_p * 3)]
+
+
+class Layer(C.Structure):
+    _fields_ = [("hidden", C.c_int32), ("inter", C.c_int32), ("n_experts", C.c_int32), ("has_shared", C.c_int32),
+                ("n_banks", C.c_int32), ("reserved", C.c_int32), ("banks", Bank * MAX_BANKS), ("grids", C.c_void_p)]
+
+
+def _load():
+    # torch ships its own HIP runtime with the same soname as /opt/rocm's.  Loading torch
+    # first makes libmoe bind to that already-mapped runtime; loading libmoe first would
+    # map a second runtime next to torch's, and the two do not share devices.
+    import torch  # noqa: F401
+
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python codebook_quantized_routed_amd/_build.py`")
+    L = C.CDLL(LIB_PATH)
+    P, i32, sz = C.c_void_p, C.c_int32, C.c_size_t
+    sig = {
+        "moe_abi_version": (i32, []),
+        "moe_status_string": (C.c_char_p, [C.c_int]),
+        "moe_last_hip_error": (i32, []),
+        "moe_last_hip_error_string": (C.c_char_p, []),
+        "moe_grids_bytes": (sz, []),
+        "moe_grids_expand": (C.c_int, [P, P, P, P]),
+        "moe_workspace_bytes": (sz, [i32, i32, i32, i32]),
+        "moe_route_group": (C.c_int, [P, i32, i32, i32, i32, P, P, P, P, P, P, P, P]),
+        "moe_expert_ffn_q": (C.c_int, [P, P, i32, i32, P, P, P, P, sz, P]),
+        "moe_expert_gateup_q": (C.c_int, [P, P, i32, i32, P, P, P, P]),
+        "moe_expert_down_q": (C.c_int, [P, P, i32, i32, P, P, P]),
+        "moe_expert_down_accumulate_q": (C.c_int, [P, P, i32, i32, P, P, P, P, P]),
+        "moe_accumulate": (C.c_int, [P, P, P, P, i32, i32, i32, P, P]),
+        "moe_dequant_f32": (C.c_int, [i32, i32, i32, P, P, P, P, P, P]),
+        "moe_rmsnorm": (C.c_int, [P, i32, i32, C.c_float, P, P]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype, f.argtypes = res, args
+    return L
+
+
+lib = _load()
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(fn, st):
+    if st != 0:
+        msg = lib.moe_status_string(st).decode()
+        if st == -6:
+            msg += f": hipError {lib.moe_last_hip_error()} {lib.moe_last_hip_error_string().decode()}"
+        raise MoeError(fn, st, msg)
+
+
+def abi_version() -> int:
+    return lib.moe_abi_version()
+
+
+def grids_bytes() -> int:
+    return lib.moe_grids_bytes()
+
+
+def workspace_bytes(T: int, kprime: int, hidden: int, inter: int) -> int:
+    return lib.moe_workspace_bytes(T, kprime, hidden, inter)
+
+
+def grids_expand(compact_iq2, compact_iq1, grids, stream=None):
+    _check("moe_grids_expand", lib.moe_grids_expand(_ptr(compact_iq2), _ptr(compact_iq1), _ptr(grids),
+                                                    _stream(stream)))
+
+
+def work_ints(n_ids: int) -> int:
+    """Length (int32 elements) of the work list written by route_group."""
+    return 4 * (n_ids + 1)
+
+
+def route_group(logits, T, E, k, add_shared, ids, w, counts, offsets, sorted_slot, slot_pos, work, stream=None):
+    _check("moe_route_group", lib.moe_route_group(_ptr(logits), T, E, k, int(add_shared), _ptr(ids), _ptr(w),
+                                                  _ptr(counts), _ptr(offsets), _ptr(sorted_slot), _ptr(slot_pos),
+                                                  _ptr(work), _stream(stream)))
+
+
+def expert_ffn_q(layer: Layer, x, T, kprime, sorted_slot, work, y, ws, stream=None):
+    _check("moe_expert_ffn_q", lib.moe_expert_ffn_q(C.byref(layer), _ptr(x), T, kprime, _ptr(sorted_slot),
+                                                    _ptr(work), _ptr(y), _ptr(ws), ws.numel() * ws.element_size(),
+                                                    _stream(stream)))
+
+
+def expert_gateup_q(layer: Layer, x, T, kprime, sorted_slot, work, h, stream=None):
+    _check("moe_expert_gateup_q", lib.moe_expert_gateup_q(C.byref(layer), _ptr(x), T, kprime, _ptr(sorted_slot),
+                                                          _ptr(work), _ptr(h), _stream(stream)))
+
+
+def expert_down_q(layer: Layer, h, T, kprime, work, y, stream=None):
+    _check("moe_expert_down_q", lib.moe_expert_down_q(C.byref(layer), _ptr(h), T, kprime, _ptr(work), _ptr(y),
+                                                      _stream(stream)))
+
+
+def expert_down_accumulate_q(layer: Layer, h, T, kprime, ids, w, slot_pos, acc, stream=None):
+    _check("moe_expert_down_accumulate_q",
+           lib.moe_expert_down_accumulate_q(C.byref(layer), _ptr(h), T, kprime, _ptr(ids), _ptr(w), _ptr(slot_pos),
+                                            _ptr(acc), _stream(stream)))
+
+
+def accumulate(y, w, ids, slot_pos, T, kprime, hidden, acc, stream=None):
+    _check("moe_accumulate", lib.moe_accumulate(_ptr(y), _ptr(w), _ptr(ids), _ptr(slot_pos), T, kprime, hidden,
+                                                _ptr(acc), _stream(stream)))
+
+
+def dequant_f32(qtype, rows, cols, s0, s1, s2, grids, out, stream=None):
+    _check("moe_dequant_f32", lib.moe_dequant_f32(qtype, rows, cols, _ptr(s0), _ptr(s1), _ptr(s2), _ptr(grids),
+                                                  _ptr(out), _stream(stream)))
+
+
+def rmsnorm(h, T, hidden, eps, x, stream=None):
+    _check("moe_rmsnorm", lib.moe_rmsnorm(_ptr(h), T, hidden, eps, _ptr(x), _stream(stream)))
+
+
+# ----------------------------------------------------------------------------- device data
+
+class DeviceLayer:
+    """A routed layer resident in device memory.
+
+    ``banks`` is a sequence of objects with ``qtype``, ``first``, ``n`` and ``gate``,
+    ``up``, ``down`` (each three host byte arrays [n][stream bytes]).  The streams are
+    copied once to device tensors; ``self.desc`` is the ``moe_layer`` for the calls.
+    """
+
+    def __init__(self, hidden, inter, n_experts, has_shared, banks, grids, device="cuda"):
+        import torch
+        if len(banks) > MAX_BANKS:
+            raise ValueError("too many banks")
+        self.tensors = []
+        d = Layer()
+        d.hidden, d.inter, d.n_experts, d.has_shared = hidden, inter, n_experts, int(has_shared)
+        d.n_banks = len(banks)
+        d.grids = grids.data_ptr()
+        self.grids = grids
+        self.bytes = 0
+        for i, b in enumerate(banks):
+            bd = d.banks[i]
+            bd.qtype, bd.first_expert, bd.n_experts = b.qtype, b.first, b.n
+            for name in ("gate", "up", "down"):
+                arr = getattr(bd, name)
+                for j, host in enumerate(getattr(b, name)):
+                    t = torch.from_numpy(host.reshape(-1)).to(device)
+                    self.tensors.append(t)
+                    self.bytes += t.numel()
+                    arr[j] = t.data_ptr()
+        self.desc = d
+
+    def __del__(self):
+        self.tensors = []

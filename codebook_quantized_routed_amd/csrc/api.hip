@@ -1,0 +1,221 @@
+// extern "C" entry points: argument validation on the host, then kernel launches on the
+// caller's stream.  No allocation, no host<->device copies, no synchronization.
+#include <initializer_list>
+
+#include "common.hpp"
+
+using namespace moe;
+
+namespace {
+
+// HIP error of this thread's last failed launch (reported by moe_last_hip_error).
+thread_local hipError_t t_last_hip = hipSuccess;
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Column counts the per-lane 32-column chunking supports.
+bool width_ok(int cols) { return cols == 256 || cols == 512 || cols == 1024 || cols == 2048; }
+
+moe_status from_hip(hipError_t e) {
+  if (e == hipSuccess) return MOE_OK;
+  t_last_hip = e;
+  return MOE_E_HIP;
+}
+
+// An error left pending by earlier, unrelated runtime calls of this thread would
+// otherwise be picked up by the launch check; clear it once validation has passed.
+void clear_pending() { (void)hipGetLastError(); }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+moe_status check_layer(const moe_layer *layer, LayerArgs *out) {
+  if (!layer || !layer->grids) return MOE_E_NULL;
+  if (!aligned16(layer->grids)) return MOE_E_ALIGN;
+  const int H = layer->hidden, I = layer->inter;
+  if (!width_ok(H) || !width_ok(I)) return MOE_E_SHAPE;
+  if (layer->n_experts < 1 || layer->has_shared < 0 || layer->has_shared > 1) return MOE_E_SHAPE;
+  const int n_ids = layer->n_experts + layer->has_shared;
+  if (n_ids > MOE_MAX_IDS) return MOE_E_SHAPE;
+  if (layer->n_banks < 1 || layer->n_banks > MOE_MAX_BANKS) return MOE_E_SHAPE;
+  out->hidden = H;
+  out->inter = I;
+  out->n_banks = layer->n_banks;
+  out->pad = 0;
+  out->grids = (const uint8_t *)layer->grids;
+  int next = 0;
+  for (int b = 0; b < MOE_MAX_BANKS; b++) {
+    BankArgs &d = out->banks[b];
+    d = BankArgs{};
+    if (b >= layer->n_banks) continue;
+    const moe_bank &s = layer->banks[b];
+    if (s.qtype != MOE_Q_IQ2XS_LIKE && s.qtype != MOE_Q_IQ1M_LIKE) return MOE_E_QTYPE;
+    if (s.first_expert != next || s.n_experts < 1) return MOE_E_SHAPE;
+    next += s.n_experts;
+    d.qtype = s.qtype;
+    d.first = s.first_expert;
+    d.n = s.n_experts;
+    for (int i = 0; i < 3; i++) {
+      if (!s.gate[i] || !s.up[i] || !s.down[i]) return MOE_E_NULL;
+      if (!aligned16(s.gate[i]) || !aligned16(s.up[i]) || !aligned16(s.down[i])) return MOE_E_ALIGN;
+      d.gate[i] = (const uint8_t *)s.gate[i];
+      d.up[i] = (const uint8_t *)s.up[i];
+      d.down[i] = (const uint8_t *)s.down[i];
+    }
+  }
+  if (next != n_ids) return MOE_E_SHAPE;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+int32_t moe_last_hip_error(void) { return (int32_t)t_last_hip; }
+
+const char *moe_last_hip_error_string(void) { return hipGetErrorString(t_last_hip); }
+
+const char *moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_E_NULL: return "null pointer";
+    case MOE_E_SHAPE: return "size out of range or inconsistent";
+    case MOE_E_QTYPE: return "unknown quantization type";
+    case MOE_E_ALIGN: return "device pointer not 16-byte aligned";
+    case MOE_E_WORKSPACE: return "workspace too small";
+    case MOE_E_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+size_t moe_grids_bytes(void) { return kGridBytes; }
+
+moe_status moe_grids_expand(const uint16_t *d_compact_iq2, const uint16_t *d_compact_iq1, void *d_grids,
+                            hipStream_t stream) {
+  if (!d_compact_iq2 || !d_compact_iq1 || !d_grids) return MOE_E_NULL;
+  if (!aligned16(d_compact_iq2) || !aligned16(d_compact_iq1) || !aligned16(d_grids)) return MOE_E_ALIGN;
+  clear_pending();
+  return from_hip(launch_grids_expand(d_compact_iq2, d_compact_iq1, (uint8_t *)d_grids, stream));
+}
+
+size_t moe_workspace_bytes(int32_t T, int32_t kprime, int32_t hidden, int32_t inter) {
+  if (T < 1 || kprime < 1 || !width_ok(hidden) || !width_ok(inter)) return 0;
+  return round_up((size_t)T * kprime * inter * sizeof(float), 256);
+}
+
+moe_status moe_route_group(const float *d_logits, int32_t T, int32_t E, int32_t k, int32_t add_shared,
+                           int32_t *d_ids, float *d_w, int32_t *d_counts, int32_t *d_offsets,
+                           int32_t *d_sorted_slot, int32_t *d_slot_pos, int32_t *d_work, hipStream_t stream) {
+  if (!d_ids || !d_w || !d_counts || !d_offsets || !d_sorted_slot || !d_slot_pos || !d_work) return MOE_E_NULL;
+  if (T < 1 || T > 65536 || E < 1 || k < 1 || k > MOE_MAX_K || k > E || add_shared < 0 || add_shared > 1)
+    return MOE_E_SHAPE;
+  if (E + add_shared > MOE_MAX_IDS) return MOE_E_SHAPE;
+  const void *ptrs[] = {d_ids, d_w, d_counts, d_offsets, d_sorted_slot, d_slot_pos, d_work};
+  for (const void *p : ptrs)
+    if (!aligned16(p)) return MOE_E_ALIGN;
+  if (d_logits && !aligned16(d_logits)) return MOE_E_ALIGN;
+  clear_pending();
+  if (d_logits)
+    return from_hip(launch_route_group(d_logits, T, E, k, add_shared, d_ids, d_w, d_counts, d_offsets, d_sorted_slot,
+                                       d_slot_pos, (WorkRec *)d_work, stream));
+  return from_hip(launch_group_explicit(T, E, k, add_shared, d_ids, d_w, d_counts, d_offsets, d_sorted_slot,
+                                        d_slot_pos, (WorkRec *)d_work, stream));
+}
+
+namespace {
+
+moe_status check_ffn_common(const moe_layer *layer, LayerArgs *L, int32_t T, int32_t kprime,
+                            std::initializer_list<const void *> ptrs) {
+  moe_status st = check_layer(layer, L);
+  if (st != MOE_OK) return st;
+  for (const void *p : ptrs)
+    if (!p) return MOE_E_NULL;
+  for (const void *p : ptrs)
+    if (!aligned16(p)) return MOE_E_ALIGN;
+  if (T < 1 || T > 65536 || kprime < 1 || kprime > MOE_MAX_K + 1) return MOE_E_SHAPE;
+  return MOE_OK;
+}
+
+}  // namespace
+
+moe_status moe_expert_gateup_q(const moe_layer *layer, const float *d_x, int32_t T, int32_t kprime,
+                               const int32_t *d_sorted_slot, const int32_t *d_work, float *d_h, hipStream_t stream) {
+  LayerArgs L;
+  moe_status st = check_ffn_common(layer, &L, T, kprime, {d_x, d_sorted_slot, d_work, d_h});
+  if (st != MOE_OK) return st;
+  const int n_ids = layer->n_experts + layer->has_shared;
+  clear_pending();
+  return from_hip(launch_gateup_gemv(L, d_x, T, kprime, d_sorted_slot, (const WorkRec *)d_work, n_ids, 1 << 30, d_h,
+                                     stream));
+}
+
+moe_status moe_expert_down_q(const moe_layer *layer, const float *d_h, int32_t T, int32_t kprime,
+                             const int32_t *d_work, float *d_y, hipStream_t stream) {
+  LayerArgs L;
+  moe_status st = check_ffn_common(layer, &L, T, kprime, {d_h, d_work, d_y});
+  if (st != MOE_OK) return st;
+  const int n_ids = layer->n_experts + layer->has_shared;
+  clear_pending();
+  return from_hip(launch_down_gemv(L, d_h, T, kprime, (const WorkRec *)d_work, n_ids, 1 << 30, d_y, stream));
+}
+
+moe_status moe_expert_down_accumulate_q(const moe_layer *layer, const float *d_h, int32_t T, int32_t kprime,
+                                        const int32_t *d_ids, const float *d_w, const int32_t *d_slot_pos,
+                                        float *d_acc, hipStream_t stream) {
+  LayerArgs L;
+  moe_status st = check_ffn_common(layer, &L, T, kprime, {d_h, d_ids, d_w, d_slot_pos, d_acc});
+  if (st != MOE_OK) return st;
+  clear_pending();
+  return from_hip(launch_down_accumulate(L, d_h, T, kprime, d_ids, d_w, d_slot_pos, d_acc, stream));
+}
+
+moe_status moe_expert_ffn_q(const moe_layer *layer, const float *d_x, int32_t T, int32_t kprime,
+                            const int32_t *d_sorted_slot, const int32_t *d_work, float *d_y, void *d_ws,
+                            size_t ws_bytes, hipStream_t stream) {
+  LayerArgs L;
+  moe_status st = check_ffn_common(layer, &L, T, kprime, {d_x, d_sorted_slot, d_work, d_y, d_ws});
+  if (st != MOE_OK) return st;
+  if (ws_bytes < moe_workspace_bytes(T, kprime, L.hidden, L.inter)) return MOE_E_WORKSPACE;
+  const int n_ids = layer->n_experts + layer->has_shared;
+  const WorkRec *work = (const WorkRec *)d_work;
+  float *h = (float *)d_ws;
+  clear_pending();
+  hipError_t err = launch_gateup_gemv(L, d_x, T, kprime, d_sorted_slot, work, n_ids, 1 << 30, h, stream);
+  if (err != hipSuccess) return from_hip(err);
+  return from_hip(launch_down_gemv(L, h, T, kprime, work, n_ids, 1 << 30, d_y, stream));
+}
+
+moe_status moe_accumulate(const float *d_y, const float *d_w, const int32_t *d_ids, const int32_t *d_slot_pos,
+                          int32_t T, int32_t kprime, int32_t hidden, float *d_acc, hipStream_t stream) {
+  if (!d_y || !d_w || !d_ids || !d_slot_pos || !d_acc) return MOE_E_NULL;
+  const void *ptrs[] = {d_y, d_w, d_ids, d_slot_pos, d_acc};
+  for (const void *p : ptrs)
+    if (!aligned16(p)) return MOE_E_ALIGN;
+  if (T < 1 || T > 65536 || kprime < 1 || kprime > MOE_MAX_K + 1 || hidden < 1 || hidden % 256) return MOE_E_SHAPE;
+  clear_pending();
+  return from_hip(launch_accumulate(d_y, d_w, d_ids, d_slot_pos, T, kprime, hidden, d_acc, stream));
+}
+
+moe_status moe_dequant_f32(int32_t qtype, int32_t rows, int32_t cols, const void *d_s0, const void *d_s1,
+                           const void *d_s2, const void *d_grids, float *d_out, hipStream_t stream) {
+  if (!d_s0 || !d_s1 || !d_s2 || !d_grids || !d_out) return MOE_E_NULL;
+  if (qtype != MOE_Q_IQ2XS_LIKE && qtype != MOE_Q_IQ1M_LIKE) return MOE_E_QTYPE;
+  if (rows < 1 || cols < 256 || cols % 256 || rows % 8) return MOE_E_SHAPE;
+  const void *ptrs[] = {d_s0, d_s1, d_s2, d_grids, d_out};
+  for (const void *p : ptrs)
+    if (!aligned16(p)) return MOE_E_ALIGN;
+  QMat m{(const uint8_t *)d_s0, (const uint8_t *)d_s1, (const uint8_t *)d_s2};
+  clear_pending();
+  return from_hip(launch_dequant(qtype, rows, cols, m, (const uint8_t *)d_grids, d_out, stream));
+}
+
+moe_status moe_rmsnorm(const float *d_h, int32_t T, int32_t hidden, float eps, float *d_x, hipStream_t stream) {
+  if (!d_h || !d_x) return MOE_E_NULL;
+  if (!aligned16(d_h) || !aligned16(d_x)) return MOE_E_ALIGN;
+  if (T < 1 || hidden < 1 || !(eps >= 0.0f)) return MOE_E_SHAPE;
+  clear_pending();
+  return from_hip(launch_rmsnorm(d_h, T, hidden, eps, d_x, stream));
+}
+
+}  // extern "C"

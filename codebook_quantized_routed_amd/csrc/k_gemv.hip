@@ -1,0 +1,739 @@
+// Fused dequantize + mat-vec kernels for experts with few tokens.
+//
+// "Red Metal dev8 — resident routed top-k layer", step 4: each selected expert runs
+// gate, up, SiLU(gate) * up and down from its resident weights.  The weights stay
+// quantized in HBM and are decoded in registers.
+//
+// Lane layout: a lane owns a 64-column chunk of a row (8 groups of 8 weights): one
+// 16-byte load brings its IQ2 codes (8-byte + 4-byte loads its IQ1 index streams);
+// cols/64 lanes share a row and reduce through DPP.  A wave handles one "pass" (64/LPR
+// rows of one expert; gate and up together in the first kernel) at a time and loops
+// over passes on its own; the only workgroup barrier follows the LDS table build.
+//
+// Decode arithmetic: the grid values are held in LDS as fp16 (8, 25, 43 and -1, 0, +1
+// are exact) and each weight enters one mixed-precision multiply-add (fp16 value times
+// fp32 activation plus fp32 accumulator, v_fma_mix_f32):
+//  IQ2_XS-like: the 7 explicit sign bits of a group select a row of a 128-entry table
+//    of fp16 sign masks (the 8th sign is their parity), applied with one XOR per pair
+//    of weights; d * (2s+1) / 8 scales each 32-column sub-block sum.
+//  IQ1_M-like: sum_j (G_j + delta) x_j = sum_j G_j x_j + delta * sum_j x_j, the group
+//    sums of x formed once per activation row; d * (2s+1) scales each 16-column
+//    sub-block sum.
+// Every dequantized weight is exact; products and sums are rounded in fp32.
+#include "decode.hpp"
+
+namespace moe {
+
+// ----------------------------------------------------------------------------- loads
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Streaming loads of the code streams (each byte is read once per launch).
+__device__ __forceinline__ uint4 load_stream16(const uint8_t *p) {
+  const u32x4 v = __builtin_nontemporal_load((const u32x4 *)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 load_stream8(const uint8_t *p) {
+  const u32x2 v = __builtin_nontemporal_load((const u32x2 *)p);
+  return make_uint2(v.x, v.y);
+}
+
+// A lane's slice of one row.  IQ2: a = 8 codes, b = (sc word, d bits).
+// IQ1: a.xy = 8 ql bytes, a.z = 4 qh bytes, b = the 64-bit sd word.
+struct RowRaw {
+  uint4 a;
+  uint2 b;
+};
+
+// Hides a row's codes from loop-invariant code motion, which would otherwise decode
+// the row once before a token loop and keep every decoded weight live.
+__device__ __forceinline__ void opaque(RowRaw &R) {
+  asm volatile("" : "+v"(R.a.x), "+v"(R.a.y), "+v"(R.a.z), "+v"(R.a.w), "+v"(R.b.x), "+v"(R.b.y));
+}
+
+template <int QT>
+__device__ __forceinline__ RowRaw load_row(const QMat &m, int cols, int r, int q) {
+  const int ng = cols >> 3, nb = cols >> 8, b = q >> 2;
+  RowRaw R;
+  if constexpr (QT == MOE_Q_IQ2XS_LIKE) {
+    R.a = load_stream16(m.s0 + ((size_t)r * ng + 8 * q) * 2);
+    R.b.x = ((const uint32_t *)m.s1)[(size_t)r * nb + b];
+    R.b.y = ((const uint16_t *)m.s2)[(size_t)r * nb + b];
+  } else {
+    const uint2 ql = load_stream8(m.s0 + (size_t)r * ng + 8 * q);
+    const uint32_t qh = __builtin_nontemporal_load((const uint32_t *)(m.s1 + (size_t)r * (ng / 2) + 4 * q));
+    R.a = make_uint4(ql.x, ql.y, qh, 0u);
+    R.b = *(const uint2 *)(m.s2 + ((size_t)r * nb + b) * 8);
+  }
+  return R;
+}
+
+// Activation slice of a lane: 64 floats, plus the 8 group sums times 1/8 (IQ1 only).
+struct XChunk {
+  float v[64];
+  float gs8[8];
+};
+
+template <int QT>
+__device__ __forceinline__ void load_x(const float *p, XChunk &X) {
+  const float4 *p4 = (const float4 *)p;
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    const float4 f = p4[i];
+    X.v[4 * i] = f.x;
+    X.v[4 * i + 1] = f.y;
+    X.v[4 * i + 2] = f.z;
+    X.v[4 * i + 3] = f.w;
+  }
+  if constexpr (QT == MOE_Q_IQ1M_LIKE) {
+#pragma unroll
+    for (int g = 0; g < 8; g++) {
+      float s = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; j++) s += X.v[8 * g + j];
+      X.gs8[g] = s * 0.125f;
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------- LDS tables
+// fp16 grid rows (8 values, 16 bytes per row) and the IQ2 sign-mask rows: entry s (the
+// 7 explicit sign bits) holds, per pair of weights, 0x8000 in each half whose weight is
+// negative, the 8th sign being the parity of the 7.
+struct TableLayout {
+  int iq2h, iq2m, iq1h, bytes;  // byte offsets in dynamic LDS
+};
+
+__host__ __device__ inline TableLayout table_layout(int formats) {
+  TableLayout t{0, 0, 0, 0};
+  if (formats & MOE_Q_IQ2XS_LIKE) {
+    t.iq2h = t.bytes;
+    t.bytes += kIq2Rows * 16;
+    t.iq2m = t.bytes;
+    t.bytes += 128 * 16;
+  }
+  if (formats & MOE_Q_IQ1M_LIKE) {
+    t.iq1h = t.bytes;
+    t.bytes += kIq1Rows * 16;
+  }
+  return t;
+}
+
+__device__ __forceinline__ uint32_t f16_bits(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
+
+__device__ __forceinline__ uint4 expand_row_f16(uint32_t c, uint32_t h0, uint32_t h1, uint32_t h2) {
+  uint32_t h[8];
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    const uint32_t s = (c >> (2 * j)) & 3u;
+    h[j] = s == 0 ? h0 : (s == 1 ? h1 : h2);
+  }
+  return make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+}
+
+// Builds the tables of the formats present from the compact rows (1 KB / 4 KB reads),
+// in two steps: tables_load issues the global loads (call it before the loads that wait
+// on HBM, so the table build does not queue behind them), tables_store expands into LDS
+// and synchronizes the workgroup.  Thread t expands rows t, t + blockDim, ...
+constexpr int kTableRowsPerThread = kIq1Rows / 256;  // for workgroups of >= 256 threads
+
+struct TableRegs {
+  uint32_t c2[kIq2Rows / 256];
+  uint32_t c1[kTableRowsPerThread];
+};
+
+__device__ __forceinline__ TableRegs tables_load(const uint8_t *grids, int formats) {
+  TableRegs tr;
+  const uint16_t *c2 = (const uint16_t *)(grids + kGridIq2CompactOff);
+  const uint16_t *c1 = (const uint16_t *)(grids + kGridIq1CompactOff);
+#pragma unroll
+  for (int i = 0; i < kIq2Rows / 256; i++) {
+    const int r = threadIdx.x + i * blockDim.x;
+    tr.c2[i] = (formats & MOE_Q_IQ2XS_LIKE) && r < kIq2Rows ? c2[r] : 0u;
+  }
+#pragma unroll
+  for (int i = 0; i < kTableRowsPerThread; i++) {
+    const int r = threadIdx.x + i * blockDim.x;
+    tr.c1[i] = (formats & MOE_Q_IQ1M_LIKE) && r < kIq1Rows ? c1[r] : 0u;
+  }
+  return tr;
+}
+
+__device__ __forceinline__ void tables_store(const TableRegs &tr, int formats, const TableLayout &TL, uint8_t *lds) {
+  if (formats & MOE_Q_IQ2XS_LIKE) {
+    const uint32_t h0 = f16_bits((float)kIq2SymVal[0]), h1 = f16_bits((float)kIq2SymVal[1]),
+                   h2 = f16_bits((float)kIq2SymVal[2]);
+    uint4 *rows = (uint4 *)(lds + TL.iq2h);
+#pragma unroll
+    for (int i = 0; i < kIq2Rows / 256; i++) {
+      const int r = threadIdx.x + i * blockDim.x;
+      if (r < kIq2Rows) rows[r] = expand_row_f16(tr.c2[i], h0, h1, h2);
+    }
+    uint4 *masks = (uint4 *)(lds + TL.iq2m);
+    for (int s = threadIdx.x; s < 128; s += blockDim.x) {
+      const uint32_t S = (uint32_t)s | ((__builtin_popcount(s) & 1u) << 7);
+      uint32_t m[4];
+#pragma unroll
+      for (int p = 0; p < 4; p++) m[p] = (((S >> (2 * p)) & 1u) << 15) | (((S >> (2 * p + 1)) & 1u) << 31);
+      masks[s] = make_uint4(m[0], m[1], m[2], m[3]);
+    }
+  }
+  if (formats & MOE_Q_IQ1M_LIKE) {
+    const uint32_t h0 = f16_bits((float)kIq1SymVal[0]), h1 = f16_bits((float)kIq1SymVal[1]),
+                   h2 = f16_bits((float)kIq1SymVal[2]);
+    uint4 *rows = (uint4 *)(lds + TL.iq1h);
+#pragma unroll
+    for (int i = 0; i < kTableRowsPerThread; i++) {
+      const int r = threadIdx.x + i * blockDim.x;
+      if (r < kIq1Rows) rows[r] = expand_row_f16(tr.c1[i], h0, h1, h2);
+    }
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ void build_tables(const uint8_t *grids, int formats, const TableLayout &TL, uint8_t *lds) {
+  const TableRegs tr = tables_load(grids, formats);
+  tables_store(tr, formats, TL, lds);
+}
+
+// ----------------------------------------------------------------------------- dot
+__device__ __forceinline__ float lo16(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w).x; }
+__device__ __forceinline__ float hi16(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w).y; }
+
+// 8 weights (4 packed fp16 pairs) times 8 activations added into two accumulation
+// chains (even and odd columns); each step is one v_fma_mix_f32.
+__device__ __forceinline__ void dot8(const uint4 &w, const float *x, float &a, float &b) {
+  a = fmaf(lo16(w.x), x[0], a);
+  b = fmaf(hi16(w.x), x[1], b);
+  a = fmaf(lo16(w.y), x[2], a);
+  b = fmaf(hi16(w.y), x[3], b);
+  a = fmaf(lo16(w.z), x[4], a);
+  b = fmaf(hi16(w.z), x[5], b);
+  a = fmaf(lo16(w.w), x[6], a);
+  b = fmaf(hi16(w.w), x[7], b);
+}
+
+// Dot product of a lane's 64-column slice of one row with its activation slice.
+template <int QT>
+__device__ __forceinline__ float dot_chunk(const RowRaw &R, int q, const uint8_t *lds, const TableLayout &TL,
+                                           const XChunk &X) {
+  if constexpr (QT == MOE_Q_IQ2XS_LIKE) {
+    const uint4 *rows = (const uint4 *)(lds + TL.iq2h);
+    const uint4 *masks = (const uint4 *)(lds + TL.iq2m);
+    float a[2] = {0.0f, 0.0f}, b[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int g = 0; g < 8; g++) {
+      const uint32_t w32 = g < 2 ? R.a.x : (g < 4 ? R.a.y : (g < 6 ? R.a.z : R.a.w));
+      const uint32_t code = (g & 1) ? (w32 >> 16) : (w32 & 0xFFFFu);
+      uint4 v = rows[code & 0x1FFu];
+      const uint4 m = masks[(code >> 9) & 0x7Fu];
+      v.x ^= m.x;
+      v.y ^= m.y;
+      v.z ^= m.z;
+      v.w ^= m.w;
+      dot8(v, X.v + 8 * g, a[g >> 2], b[g >> 2]);
+    }
+    const float acc[2] = {a[0] + b[0], a[1] + b[1]};
+    const int sb = 2 * (q & 3);
+    return fmaf(acc[1], iq2_factor(R.b.x, R.b.y, sb + 1), acc[0] * iq2_factor(R.b.x, R.b.y, sb));
+  } else {
+    const uint4 *rows = (const uint4 *)(lds + TL.iq1h);
+    float a[4] = {0.0f, 0.0f, 0.0f, 0.0f}, b[4] = {0.0f, 0.0f, 0.0f, 0.0f}, ds[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int g = 0; g < 8; g++) {
+      const uint32_t ql8 = ((g < 4 ? R.a.x : R.a.y) >> (8 * (g & 3))) & 0xFFu;
+      const uint32_t nib = (R.a.z >> (4 * g)) & 15u;
+      const uint4 v = rows[ql8 | ((nib & 7u) << 8)];
+      ds[g >> 1] += (nib & 8u) ? -X.gs8[g] : X.gs8[g];
+      dot8(v, X.v + 8 * g, a[g >> 1], b[g >> 1]);
+    }
+    float acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) acc[i] = (a[i] + b[i]) + ds[i];
+    const uint64_t sd = ((uint64_t)R.b.y << 32) | R.b.x;
+    const int sb = 4 * (q & 3);
+    float r = acc[0] * iq1_factor(sd, sb);
+    r = fmaf(acc[1], iq1_factor(sd, sb + 1), r);
+    r = fmaf(acc[2], iq1_factor(sd, sb + 2), r);
+    return fmaf(acc[3], iq1_factor(sd, sb + 3), r);
+  }
+}
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+
+__host__ __device__ inline int layer_formats(const LayerArgs &L) {
+  int f = 0;
+  for (int b = 0; b < L.n_banks; b++) f |= L.banks[b].qtype;
+  return f;
+}
+
+__device__ __forceinline__ WorkRec load_work(const WorkRec *w, int i) {
+  const int4 v = *(const int4 *)(w + i);
+  return WorkRec{uniform(v.x), uniform(v.y), uniform(v.z), uniform(v.w)};
+}
+
+// ----------------------------------------------------------------------------- gate + up
+// A pass = rows [rp*RPP, rp*RPP + RPP) of one active expert, gate and up together.  A
+// wave issues the loads of its next pass (work record, then the two rows and the first
+// token's activations) before it does anything else, so the first pass's loads are in
+// flight while the workgroup builds its LDS tables.
+struct GatePass {
+  WorkRec W;
+  RowRaw g, u;
+  XChunk X;
+  int r, qt;
+};
+
+template <int LPR>
+__device__ __forceinline__ void gateup_issue(const LayerArgs &L, GatePass &P, int a, int rp, int q, int sub,
+                                             int kprime, const float *x) {
+  constexpr int RPP = 64 / LPR;
+  const int H = L.hidden, I = L.inter;
+  const BankArgs &B = bank_of(L, P.W.e);
+  P.qt = B.qtype;
+  P.r = rp * RPP + sub;
+  const QMat Wg = expert_mat(B, P.W.e, kGate, I, H), Wu = expert_mat(B, P.W.e, kUp, I, H);
+  if (P.qt == MOE_Q_IQ2XS_LIKE) {
+    P.g = load_row<MOE_Q_IQ2XS_LIKE>(Wg, H, P.r, q);
+    P.u = load_row<MOE_Q_IQ2XS_LIKE>(Wu, H, P.r, q);
+  } else {
+    P.g = load_row<MOE_Q_IQ1M_LIKE>(Wg, H, P.r, q);
+    P.u = load_row<MOE_Q_IQ1M_LIKE>(Wu, H, P.r, q);
+  }
+  load_x<MOE_Q_IQ2XS_LIKE>(x + (size_t)(P.W.slot0 / kprime) * H + 64 * q, P.X);  // values only
+  (void)a;
+}
+
+template <int QT, int LPR>
+__device__ __forceinline__ void gateup_run(const LayerArgs &L, GatePass &P, int q, int kprime, const float *x,
+                                           const int32_t *sorted_slot, const uint8_t *lds, const TableLayout &TL,
+                                           float *h) {
+  const int H = L.hidden, I = L.inter;
+  for (int p = P.W.p0; p < P.W.p1; p++) {
+    if (p > P.W.p0) load_x<QT>(x + (size_t)(uniform(sorted_slot[p]) / kprime) * H + 64 * q, P.X);
+    else if constexpr (QT == MOE_Q_IQ1M_LIKE) {
+#pragma unroll
+      for (int g = 0; g < 8; g++) {
+        float s = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; j++) s += P.X.v[8 * g + j];
+        P.X.gs8[g] = s * 0.125f;
+      }
+    }
+    RowRaw g = P.g, u = P.u;
+    opaque(g);
+    opaque(u);
+    float vg = dot_chunk<QT>(g, q, lds, TL, P.X);
+    float vu = dot_chunk<QT>(u, q, lds, TL, P.X);
+    vg = group_sum_first<LPR>(vg);
+    vu = group_sum_first<LPR>(vu);
+    if (q == 0) h[(size_t)p * I + P.r] = silu(vg) * vu;
+  }
+}
+
+template <int LPR>
+__global__ void __launch_bounds__(256) k_gateup(LayerArgs L, const float *__restrict__ x, int kprime,
+                                                const int32_t *__restrict__ sorted_slot,
+                                                const WorkRec *__restrict__ work, int max_tokens, int n_ids,
+                                                float *__restrict__ h) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  constexpr int RPP = 64 / LPR;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, q = lane % LPR, sub = lane / LPR;
+  const int formats = layer_formats(L);
+  const TableLayout TL = table_layout(formats);
+  const int ppe = L.inter / RPP, stride = gridDim.x * 4;
+  int pass = blockIdx.x * 4 + wave;
+  // the record index stays within the n_ids + 1 records even before the count is known
+  const int a0 = min(pass / ppe, n_ids - 1);
+  const int4 rec0 = *(const int4 *)(work + 1 + a0);
+  const int total = uniform(work[0].e) * ppe;
+  GatePass P;
+  bool have = pass < total;
+  if (have) {
+    P.W = WorkRec{uniform(rec0.x), uniform(rec0.y), uniform(rec0.z), uniform(rec0.w)};
+    gateup_issue<LPR>(L, P, a0, pass - a0 * ppe, q, sub, kprime, x);
+  }
+  build_tables(L.grids, formats, TL, lds);
+  while (have) {
+    if (P.W.p1 - P.W.p0 <= max_tokens) {
+      if (P.qt == MOE_Q_IQ2XS_LIKE)
+        gateup_run<MOE_Q_IQ2XS_LIKE, LPR>(L, P, q, kprime, x, sorted_slot, lds, TL, h);
+      else
+        gateup_run<MOE_Q_IQ1M_LIKE, LPR>(L, P, q, kprime, x, sorted_slot, lds, TL, h);
+    }
+    pass += stride;
+    have = pass < total;
+    if (have) {
+      const int a = pass / ppe;
+      P.W = load_work(work, 1 + a);
+      gateup_issue<LPR>(L, P, a, pass - a * ppe, q, sub, kprime, x);
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------- gate + up, hidden 2048
+// Decode layout for hidden = 2048: a whole wave covers one row (32 columns per lane), so
+// a lane's activation slice is 32 floats with no copy shared between lanes, loaded once
+// per wave while the wave's items keep the same token.  An item is kWideRows rows of one
+// expert, gate and up.  Issue order: compact-table loads, work record (scalar), row and
+// activation loads, then the table build; compute waits only for what it uses.
+constexpr int kWideRows = 2;
+
+struct Row32 {  // IQ2: x = codes 0-1, y = codes 2-3, z = sc word, w = d bits.
+  uint4 v;      // IQ1: x = 4 ql bytes, y = 4 qh nibbles (16 bits), z/w = the sd word.
+};
+
+__device__ __forceinline__ void opaque(Row32 &R) { asm volatile("" : "+v"(R.v.x), "+v"(R.v.y), "+v"(R.v.z), "+v"(R.v.w)); }
+
+template <int QT>
+__device__ __forceinline__ Row32 load_row32(const QMat &m, int cols, int r, int q) {
+  const int ng = cols >> 3, nb = cols >> 8, b = q >> 3;
+  Row32 R;
+  if constexpr (QT == MOE_Q_IQ2XS_LIKE) {
+    const uint2 c = load_stream8(m.s0 + ((size_t)r * ng + 4 * q) * 2);
+    R.v = make_uint4(c.x, c.y, ((const uint32_t *)m.s1)[(size_t)r * nb + b], ((const uint16_t *)m.s2)[(size_t)r * nb + b]);
+  } else {
+    const uint32_t ql = __builtin_nontemporal_load((const uint32_t *)(m.s0 + (size_t)r * ng + 4 * q));
+    const uint32_t qh = __builtin_nontemporal_load((const uint16_t *)(m.s1 + (size_t)r * (ng / 2) + 2 * q));
+    const uint2 sd = *(const uint2 *)(m.s2 + ((size_t)r * nb + b) * 8);
+    R.v = make_uint4(ql, qh, sd.x, sd.y);
+  }
+  return R;
+}
+
+struct X32 {
+  float v[32];
+  float gs8[4];
+};
+
+template <int QT>
+__device__ __forceinline__ float dot32(const Row32 &R, int q, const uint8_t *lds, const TableLayout &TL, const X32 &X) {
+  if constexpr (QT == MOE_Q_IQ2XS_LIKE) {
+    const uint4 *rows = (const uint4 *)(lds + TL.iq2h);
+    const uint4 *masks = (const uint4 *)(lds + TL.iq2m);
+    float a = 0.0f, b = 0.0f;
+#pragma unroll
+    for (int g = 0; g < 4; g++) {
+      const uint32_t w32 = g < 2 ? R.v.x : R.v.y;
+      const uint32_t code = (g & 1) ? (w32 >> 16) : (w32 & 0xFFFFu);
+      uint4 v = rows[code & 0x1FFu];
+      const uint4 m = masks[(code >> 9) & 0x7Fu];
+      v.x ^= m.x;
+      v.y ^= m.y;
+      v.z ^= m.z;
+      v.w ^= m.w;
+      dot8(v, X.v + 8 * g, a, b);
+    }
+    return (a + b) * iq2_factor(R.v.z, R.v.w, q & 7);
+  } else {
+    const uint4 *rows = (const uint4 *)(lds + TL.iq1h);
+    float a[2] = {0.0f, 0.0f}, b[2] = {0.0f, 0.0f}, ds[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int g = 0; g < 4; g++) {
+      const uint32_t ql8 = (R.v.x >> (8 * g)) & 0xFFu;
+      const uint32_t nib = (R.v.y >> (4 * g)) & 15u;
+      const uint4 v = rows[ql8 | ((nib & 7u) << 8)];
+      ds[g >> 1] += (nib & 8u) ? -X.gs8[g] : X.gs8[g];
+      dot8(v, X.v + 8 * g, a[g >> 1], b[g >> 1]);
+    }
+    const uint64_t sd = ((uint64_t)R.v.w << 32) | R.v.z;
+    const int sb = 2 * (q & 7);
+    return fmaf((a[1] + b[1]) + ds[1], iq1_factor(sd, sb + 1), ((a[0] + b[0]) + ds[0]) * iq1_factor(sd, sb));
+  }
+}
+
+__device__ __forceinline__ void load_x32(const float *p, X32 &X) {
+  const float4 *p4 = (const float4 *)p;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const float4 f = p4[i];
+    X.v[4 * i] = f.x;
+    X.v[4 * i + 1] = f.y;
+    X.v[4 * i + 2] = f.z;
+    X.v[4 * i + 3] = f.w;
+  }
+}
+
+__device__ __forceinline__ void group_sums32(X32 &X) {
+#pragma unroll
+  for (int g = 0; g < 4; g++) {
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; j++) s += X.v[8 * g + j];
+    X.gs8[g] = s * 0.125f;
+  }
+}
+
+struct WideItem {
+  WorkRec W;
+  Row32 g[kWideRows], u[kWideRows];
+  int r0, qt;
+};
+
+__device__ __forceinline__ void wide_issue(const LayerArgs &L, WideItem &It, int rb, int q) {
+  const int H = L.hidden, I = L.inter;
+  const BankArgs &B = bank_of(L, It.W.e);
+  It.qt = B.qtype;
+  It.r0 = rb * kWideRows;
+  const QMat Wg = expert_mat(B, It.W.e, kGate, I, H), Wu = expert_mat(B, It.W.e, kUp, I, H);
+#pragma unroll
+  for (int i = 0; i < kWideRows; i++) {
+    if (It.qt == MOE_Q_IQ2XS_LIKE) {
+      It.g[i] = load_row32<MOE_Q_IQ2XS_LIKE>(Wg, H, It.r0 + i, q);
+      It.u[i] = load_row32<MOE_Q_IQ2XS_LIKE>(Wu, H, It.r0 + i, q);
+    } else {
+      It.g[i] = load_row32<MOE_Q_IQ1M_LIKE>(Wg, H, It.r0 + i, q);
+      It.u[i] = load_row32<MOE_Q_IQ1M_LIKE>(Wu, H, It.r0 + i, q);
+    }
+  }
+}
+
+template <int QT>
+__device__ __forceinline__ void wide_run(const LayerArgs &L, WideItem &It, X32 &X, int &cur_tok, int q, int kprime,
+                                         const float *x, const int32_t *sorted_slot, const uint8_t *lds,
+                                         const TableLayout &TL, float *h) {
+  const int H = L.hidden, I = L.inter;
+  for (int p = It.W.p0; p < It.W.p1; p++) {
+    const int tok = (p == It.W.p0 ? It.W.slot0 : uniform(sorted_slot[p])) / kprime;
+    if (tok != cur_tok) {
+      load_x32(x + (size_t)tok * H + 32 * q, X);
+      if constexpr (QT == MOE_Q_IQ1M_LIKE) group_sums32(X);
+      cur_tok = tok;
+    }
+#pragma unroll
+    for (int i = 0; i < kWideRows; i++) {
+      Row32 g = It.g[i], u = It.u[i];
+      opaque(g);
+      opaque(u);
+      float vg = dot32<QT>(g, q, lds, TL, X);
+      float vu = dot32<QT>(u, q, lds, TL, X);
+      vg = group_sum_first<64>(vg);
+      vu = group_sum_first<64>(vu);
+      if (q == 0) h[(size_t)p * I + It.r0 + i] = silu(vg) * vu;
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256) k_gateup_wide(LayerArgs L, const float *__restrict__ x, int kprime,
+                                                     const int32_t *__restrict__ sorted_slot,
+                                                     const WorkRec *__restrict__ work, int max_tokens, int n_ids,
+                                                     float *__restrict__ h) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int q = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int formats = layer_formats(L);
+  const TableLayout TL = table_layout(formats);
+  const TableRegs tr = tables_load(L.grids, formats);
+  const int ipe = L.inter / kWideRows, stride = gridDim.x * 4;
+  int item = blockIdx.x * 4 + wave;
+  const int a0 = min(item / ipe, n_ids - 1);  // within the n_ids + 1 records before the count is known
+  const int4 rec0 = *(const int4 *)(work + 1 + a0);
+  const int total = uniform(work[0].e) * ipe;
+  WideItem It;
+  X32 X;
+  int cur_tok = -1;
+  bool have = item < total;
+  if (have) {
+    It.W = WorkRec{uniform(rec0.x), uniform(rec0.y), uniform(rec0.z), uniform(rec0.w)};
+    wide_issue(L, It, item - a0 * ipe, q);
+    const int tok = It.W.slot0 / kprime;
+    load_x32(x + (size_t)tok * L.hidden + 32 * q, X);
+    cur_tok = tok;
+    if (It.qt == MOE_Q_IQ1M_LIKE) group_sums32(X);
+  }
+  tables_store(tr, formats, TL, lds);
+  while (have) {
+    if (It.W.p1 - It.W.p0 <= max_tokens) {
+      if (It.qt == MOE_Q_IQ2XS_LIKE)
+        wide_run<MOE_Q_IQ2XS_LIKE>(L, It, X, cur_tok, q, kprime, x, sorted_slot, lds, TL, h);
+      else
+        wide_run<MOE_Q_IQ1M_LIKE>(L, It, X, cur_tok, q, kprime, x, sorted_slot, lds, TL, h);
+    }
+    item += stride;
+    have = item < total;
+    if (have) {
+      const int a = item / ipe;
+      const int prev_qt = It.qt;
+      It.W = load_work(work, 1 + a);
+      wide_issue(L, It, item - a * ipe, q);
+      if (It.qt != prev_qt) cur_tok = -1;  // group sums depend on the format
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------- down
+template <int QT, int LPR>
+__device__ __forceinline__ void down_pass(const LayerArgs &L, const WorkRec &W, int r, int q, const float *h,
+                                          const uint8_t *lds, const TableLayout &TL, float *y) {
+  const int H = L.hidden, I = L.inter;
+  const BankArgs &B = bank_of(L, W.e);
+  const RowRaw rd = load_row<QT>(expert_mat(B, W.e, kDown, H, I), I, r, q);
+  for (int p = W.p0; p < W.p1; p++) {
+    RowRaw d = rd;
+    opaque(d);
+    XChunk X;
+    load_x<QT>(h + (size_t)p * I + 64 * q, X);
+    const float v = group_sum_first<LPR>(dot_chunk<QT>(d, q, lds, TL, X));
+    if (q == 0) y[(size_t)p * H + r] = v;
+  }
+}
+
+template <int LPR>
+__global__ void __launch_bounds__(256) k_down(LayerArgs L, const float *__restrict__ h,
+                                              const WorkRec *__restrict__ work, int max_tokens,
+                                              float *__restrict__ y) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  constexpr int RPP = 64 / LPR;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, q = lane % LPR, sub = lane / LPR;
+  const int formats = layer_formats(L);
+  const TableLayout TL = table_layout(formats);
+  const int ppe = L.hidden / RPP;
+  const int total = uniform(work[0].e) * ppe;
+  build_tables(L.grids, formats, TL, lds);
+  for (int pass = blockIdx.x * 4 + wave; pass < total; pass += gridDim.x * 4) {
+    const int a = pass / ppe, rp = pass - a * ppe;
+    const WorkRec W = load_work(work, 1 + a);
+    if (W.p1 - W.p0 > max_tokens) continue;
+    const int r = rp * RPP + sub;
+    if (bank_of(L, W.e).qtype == MOE_Q_IQ2XS_LIKE)
+      down_pass<MOE_Q_IQ2XS_LIKE, LPR>(L, W, r, q, h, lds, TL, y);
+    else
+      down_pass<MOE_Q_IQ1M_LIKE, LPR>(L, W, r, q, h, lds, TL, y);
+  }
+}
+
+// ----------------------------------------------------------------------------- down + accumulate
+// One workgroup of 16 waves per (token, block of RPP output rows); wave j takes slot j
+// (and j + 16): the down rows of that slot's expert are dotted with its h, and the RPP
+// outputs are accumulated as acc += w * y in ascending expert id ("Red Metal dev8",
+// step 5), one rounded multiply and one rounded add per slot, so the result equals the
+// separate accumulation exactly.
+constexpr int kDownAccWaves = 16;
+
+template <int QT, int LPR>
+__device__ __forceinline__ float down_slot_dot(const RowRaw &R, const float *hrow, int q, const uint8_t *lds,
+                                               const TableLayout &TL) {
+  XChunk X;
+  load_x<QT>(hrow + 64 * q, X);
+  return group_sum_first<LPR>(dot_chunk<QT>(R, q, lds, TL, X));
+}
+
+template <int LPR>
+__global__ void __launch_bounds__(1024) k_down_acc(LayerArgs L, const float *__restrict__ h, int kprime,
+                                                   const int32_t *__restrict__ ids, const float *__restrict__ w,
+                                                   const int32_t *__restrict__ slot_pos, float *__restrict__ acc) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  constexpr int RPP = 64 / LPR;
+  __shared__ float ydot[MOE_MAX_K + 1][RPP];
+  __shared__ int order[MOE_MAX_K + 1];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, q = lane % LPR, sub = lane / LPR;
+  const int H = L.hidden, I = L.inter, tiles = H / RPP;
+  const int t = blockIdx.x / tiles, tile = blockIdx.x - t * tiles;
+  const int r = tile * RPP + sub;
+  const int32_t *tok_ids = ids + (size_t)t * kprime;
+  const int formats = layer_formats(L);
+  const TableLayout TL = table_layout(formats);
+
+  RowRaw R[2];
+  int qt[2] = {0, 0}, p[2] = {0, 0};
+#pragma unroll
+  for (int i = 0; i < 2; i++) {
+    const int j = wave + kDownAccWaves * i;
+    if (j < kprime) {
+      const int e = uniform(tok_ids[j]);
+      p[i] = uniform(slot_pos[(size_t)t * kprime + j]);
+      const BankArgs &B = bank_of(L, e);
+      const QMat Wd = expert_mat(B, e, kDown, H, I);
+      qt[i] = B.qtype;
+      R[i] = B.qtype == MOE_Q_IQ2XS_LIKE ? load_row<MOE_Q_IQ2XS_LIKE>(Wd, I, r, q)
+                                         : load_row<MOE_Q_IQ1M_LIKE>(Wd, I, r, q);
+    }
+  }
+  float acc_in = 0.0f;
+  if (threadIdx.x < RPP) acc_in = acc[(size_t)t * H + tile * RPP + threadIdx.x];
+  if (threadIdx.x < kprime) {
+    const int j = threadIdx.x, me = tok_ids[j];
+    int rank = 0;
+    for (int i = 0; i < kprime; i++) {
+      const int o = tok_ids[i];
+      rank += (o < me || (o == me && i < j)) ? 1 : 0;
+    }
+    order[rank] = j;
+  }
+  build_tables(L.grids, formats, TL, lds);
+
+#pragma unroll
+  for (int i = 0; i < 2; i++) {
+    const int j = wave + kDownAccWaves * i;
+    if (j < kprime) {
+      const float *hrow = h + (size_t)p[i] * I;
+      const float v = qt[i] == MOE_Q_IQ2XS_LIKE ? down_slot_dot<MOE_Q_IQ2XS_LIKE, LPR>(R[i], hrow, q, lds, TL)
+                                                : down_slot_dot<MOE_Q_IQ1M_LIKE, LPR>(R[i], hrow, q, lds, TL);
+      if (q == 0) ydot[j][sub] = v;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < RPP) {
+    float a = acc_in;
+    for (int o = 0; o < kprime; o++) {
+      const int j = order[o];
+      a = __fadd_rn(a, __fmul_rn(w[(size_t)t * kprime + j], ydot[j][threadIdx.x]));
+    }
+    acc[(size_t)t * H + tile * RPP + threadIdx.x] = a;
+  }
+}
+
+// ----------------------------------------------------------------------------- launch
+static int lanes_per_row(int cols) { return cols / 64; }
+
+#define MOE_LPR_DISPATCH(LPR_VAL, KERNEL, ...)                    \
+  do {                                                            \
+    switch (LPR_VAL) {                                            \
+      case 32: hipLaunchKernelGGL(KERNEL<32>, __VA_ARGS__); break; \
+      case 16: hipLaunchKernelGGL(KERNEL<16>, __VA_ARGS__); break; \
+      case 8: hipLaunchKernelGGL(KERNEL<8>, __VA_ARGS__); break;   \
+      default: hipLaunchKernelGGL(KERNEL<4>, __VA_ARGS__); break;  \
+    }                                                             \
+  } while (0)
+
+// Workgroups for a bound on passes: one pass per wave up to the cap, then waves loop.
+static unsigned grid_for_passes(long passes) {
+  long wgs = (passes + 3) / 4;
+  return (unsigned)(wgs < 1 ? 1 : (wgs < 2048 ? wgs : 2048));
+}
+
+hipError_t launch_gateup_gemv(const LayerArgs &L, const float *x, int T, int kprime, const int32_t *sorted_slot,
+                              const WorkRec *work, int n_ids, int max_tokens, float *h, hipStream_t s) {
+  const int lpr = lanes_per_row(L.hidden), rpp = 64 / lpr;
+  const long max_active = n_ids < (long)T * kprime ? n_ids : (long)T * kprime;
+  const size_t shmem = table_layout(layer_formats(L)).bytes;
+  if (L.hidden == 2048) {
+    hipLaunchKernelGGL(k_gateup_wide, dim3(grid_for_passes(max_active * (L.inter / kWideRows))), dim3(256), shmem, s,
+                       L, x, kprime, sorted_slot, work, max_tokens, n_ids, h);
+    return hipGetLastError();
+  }
+  MOE_LPR_DISPATCH(lpr, k_gateup, dim3(grid_for_passes(max_active * (L.inter / rpp))), dim3(256), shmem, s, L, x,
+                   kprime, sorted_slot, work, max_tokens, n_ids, h);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_gemv(const LayerArgs &L, const float *h, int T, int kprime, const WorkRec *work, int n_ids,
+                            int max_tokens, float *y, hipStream_t s) {
+  const int lpr = lanes_per_row(L.inter), rpp = 64 / lpr;
+  const long max_active = n_ids < (long)T * kprime ? n_ids : (long)T * kprime;
+  const size_t shmem = table_layout(layer_formats(L)).bytes;
+  MOE_LPR_DISPATCH(lpr, k_down, dim3(grid_for_passes(max_active * (L.hidden / rpp))), dim3(256), shmem, s, L, h,
+                   work, max_tokens, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_accumulate(const LayerArgs &L, const float *h, int T, int kprime, const int32_t *ids,
+                                  const float *w, const int32_t *slot_pos, float *acc, hipStream_t s) {
+  const int lpr = lanes_per_row(L.inter), rpp = 64 / lpr;
+  const size_t shmem = table_layout(layer_formats(L)).bytes;
+  MOE_LPR_DISPATCH(lpr, k_down_acc, dim3((unsigned)(T * (L.hidden / rpp))), dim3(64 * kDownAccWaves), shmem, s, L,
+                   h, kprime, ids, w, slot_pos, acc);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,205 @@
+/* moe.h — C ABI of the routed top-k MoE expert layer on codebook-quantized experts,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What the layer computes ("Red Metal dev8 — resident routed top-k layer", steps 4-6;
+ * "Red Lite dev10 — standalone native Metal path", sections "What is native in dev10"
+ * and "Quant grids"): for each token, the router selects k experts; every selected
+ * expert decodes its 2-bit-class codebook weights, runs gate and up, SiLU(gate) * up
+ * and down, and its output is accumulated as acc += router_weight * expert_output.
+ * Every expert stays resident in device memory; nothing is streamed from the host.
+ *
+ * Conventions for every entry point:
+ *  - Pointers named d_* are device memory, allocated and owned by the caller.  The
+ *    library never allocates, frees, copies to or from the host, or synchronizes.
+ *  - Arguments are validated on the host before anything is enqueued; a rejected call
+ *    enqueues nothing and returns a negative moe_status.  On MOE_OK the kernels have
+ *    been enqueued on `stream` (0 = the null stream) and run asynchronously: device
+ *    faults surface at the caller's next synchronization.
+ *  - Every d_* pointer must be 16-byte aligned (MOE_E_ALIGN otherwise).
+ *  - The library keeps no mutable global state: calls on different streams with
+ *    different buffers may run concurrently.  Calls that share an output or workspace
+ *    buffer must be ordered by the caller.
+ *  - Results are deterministic: no floating-point atomics; a repeated call on the
+ *    same inputs writes the same bits.
+ *
+ * Quantized matrix layouts (rows x cols, cols % 256 == 0, rows % 8 == 0; blocks run
+ * along cols; NB = cols/256 super-blocks, NG = cols/8 groups of 8 weights), three
+ * streams per matrix, each row-major by matrix row:
+ *
+ *  MOE_Q_IQ2XS_LIKE, 70 bytes / 256 weights:
+ *    s0 = qs u16[rows][NG]: bits 0-8 grid index (0..511); bits 9-15 sign of weights
+ *         0..6 of the group (1 = negative); weight 7 is negative iff bits 9-15 hold an
+ *         odd number of ones (the group has an even number of negatives)
+ *    s1 = sc u32[rows][NB]: nibble i = scale s of the 32-weight sub-block i
+ *    s2 = d  u16[rows][NB]: IEEE binary16 super-block scale
+ *    weight = d * (2s + 1) / 8 * (+/- iq2_grid[index][j]),  grid values 8, 25, 43
+ *  MOE_Q_IQ1M_LIKE, 56 bytes / 256 weights:
+ *    s0 = ql u8[rows][NG]: grid index bits 0-7
+ *    s1 = qh u8[rows][NG/2]: group g uses nibble (g & 1) of byte g/2: bits 0-2 = grid
+ *         index bits 8-10, bit 3 = delta sign (1 = minus)
+ *    s2 = sd u64[rows][NB]: bits 0-15 binary16 d; bits 16+3i..18+3i = scale s of the
+ *         16-weight sub-block i
+ *    weight = d * (2s + 1) * (iq1_grid[index][j] +/- 1/8),  grid values -1, 0, +1
+ *  Both products are exact in fp32.
+ *
+ * Compact grids ("Red Lite dev10", section "Quant grids"): one u16 per grid row,
+ * symbol j in bits 2j..2j+1; IQ2_XS-like 512 rows with symbols 0,1,2 standing for
+ * 0x08, 0x19, 0x2b; IQ1_M-like 2048 rows with symbols standing for -1, 0, +1.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+#define MOE_MAX_BANKS 4
+#define MOE_MAX_K 16        /* routed experts per token */
+#define MOE_MAX_IDS 1024    /* E + has_shared */
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_E_NULL = -1,      /* a required pointer is NULL */
+  MOE_E_SHAPE = -2,     /* a size is out of range or inconsistent */
+  MOE_E_QTYPE = -3,     /* unknown quantization type */
+  MOE_E_ALIGN = -4,     /* a device pointer is not 16-byte aligned */
+  MOE_E_WORKSPACE = -5, /* workspace smaller than moe_workspace_bytes() */
+  MOE_E_HIP = -6        /* the HIP runtime reported an error at launch */
+} moe_status;
+
+typedef enum { MOE_Q_IQ2XS_LIKE = 1, MOE_Q_IQ1M_LIKE = 2 } moe_qtype;
+
+/* Experts [first_expert, first_expert + n_experts) of a layer, all in one format.
+ * Expert i of the bank has its gate (inter x hidden), up (inter x hidden) and down
+ * (hidden x inter) streams at base + i * (that stream's size for that shape). */
+typedef struct {
+  int32_t qtype;
+  int32_t first_expert;
+  int32_t n_experts;
+  int32_t reserved;
+  const void *gate[3];
+  const void *up[3];
+  const void *down[3];
+} moe_bank;
+
+/* One routed layer ("Red Lite dev16 — complete full-attention parity": top-10 routed
+ * MoE plus shared expert).  Routed experts have ids 0..E-1; with has_shared the shared
+ * expert has id E.  The banks must cover ids 0..E-1+has_shared without overlap.
+ * hidden and inter are multiples of 256.  Host memory; read during the call only. */
+typedef struct {
+  int32_t hidden;
+  int32_t inter;
+  int32_t n_experts;
+  int32_t has_shared;
+  int32_t n_banks;
+  int32_t reserved;
+  moe_bank banks[MOE_MAX_BANKS];
+  const void *grids; /* device buffer filled by moe_grids_expand */
+} moe_layer;
+
+int32_t moe_abi_version(void);
+const char *moe_status_string(moe_status s);
+
+/* The hipError_t of the calling thread's last call that returned MOE_E_HIP, and its
+ * name.  Errors left pending by the caller's own earlier runtime calls are cleared,
+ * not reported, when a call passes validation. */
+int32_t moe_last_hip_error(void);
+const char *moe_last_hip_error_string(void);
+
+/* Size of the expanded-grid buffer (the grid values of both formats, plus derived
+ * tables the kernels read). */
+size_t moe_grids_bytes(void);
+
+/* Expands the compact grids once ("Red Lite dev10", section "Quant grids": the runtime
+ * expands the compact tables once before use).  d_compact_iq2: u16[512],
+ * d_compact_iq1: u16[2048], d_grids: moe_grids_bytes() bytes.  Symbol value 3 is not
+ * allowed; it expands to grid value 0 (the caller's contract). */
+moe_status moe_grids_expand(const uint16_t *d_compact_iq2, const uint16_t *d_compact_iq1, void *d_grids,
+                            hipStream_t stream);
+
+/* Workspace needed by moe_expert_ffn_q for T tokens with kprime slots each. */
+size_t moe_workspace_bytes(int32_t T, int32_t kprime, int32_t hidden, int32_t inter);
+
+/* Router and grouping ("Red Metal dev8", steps 3-4: every selected expert of the layer
+ * is made resident and run; default validation uses positive router weights that sum
+ * to about one).  Per token t:
+ *   - with d_logits ([T][E] fp32, finite): the k largest logits, ties to the lower id,
+ *     in descending order, weights softmax(logits) renormalised over the selected set;
+ *   - with d_logits == NULL: d_ids[t][0..k-1] and d_w[t][0..k-1] are inputs (k distinct
+ *     ids in [0, E) per token) and only the shared slot and the grouping are written;
+ *   - with add_shared: slot k is (E, 1.0).  kprime = k + add_shared.
+ * Outputs (device): d_ids, d_w [T][kprime]; d_counts [E + add_shared]; d_offsets
+ * [E + add_shared + 1] (exclusive scan of counts); d_sorted_slot [T*kprime]: slots
+ * s = t*kprime + j ordered by (expert id, s); d_slot_pos: its inverse; d_work
+ * [4 * (E + add_shared + 1)]: the work list of the FFN calls, 4 ints per record:
+ * record 0 = (number of experts with a nonzero count, T*kprime, 0, 0); record 1+a for
+ * the a-th such expert in ascending id = (expert id, offsets[e], offsets[e+1],
+ * d_sorted_slot[offsets[e]]).
+ * Limits: 1 <= T <= 65536, 1 <= k <= min(E, MOE_MAX_K), E + add_shared <= MOE_MAX_IDS. */
+moe_status moe_route_group(const float *d_logits, int32_t T, int32_t E, int32_t k, int32_t add_shared,
+                           int32_t *d_ids, float *d_w, int32_t *d_counts, int32_t *d_offsets,
+                           int32_t *d_sorted_slot, int32_t *d_slot_pos, int32_t *d_work,
+                           hipStream_t stream);
+
+/* Expert FFNs ("Red Metal dev8", step 4: gate, up, SiLU(gate) * up and down per
+ * selected expert).  For every sorted position p (0 <= p < T*kprime) with slot
+ * s = d_sorted_slot[p] of token t = s / kprime and expert e (offsets[e] <= p <
+ * offsets[e+1]):  d_y[p] = Wd_e (SiLU(Wg_e x_t) * (Wu_e x_t)).
+ * d_x [T][hidden] fp32; d_sorted_slot and d_work from moe_route_group;
+ * d_y [T*kprime][hidden] fp32 in sorted order.  d_ws: at least
+ * moe_workspace_bytes(T, kprime, hidden, inter) bytes of scratch (holds h).  Runs
+ * moe_expert_gateup_q then moe_expert_down_q.  Accuracy: max |error| <= 2e-5 * ||y_p||_2
+ * against an fp32 reference.  Limits: 1 <= T <= 65536, 1 <= kprime <= MOE_MAX_K + 1. */
+moe_status moe_expert_ffn_q(const moe_layer *layer, const float *d_x, int32_t T, int32_t kprime,
+                            const int32_t *d_sorted_slot, const int32_t *d_work, float *d_y, void *d_ws,
+                            size_t ws_bytes, hipStream_t stream);
+
+/* Gate and up with the SiLU epilogue ("Red Metal dev8", step 4, first half): for every
+ * sorted position p as above, d_h[p] = SiLU(Wg_e x_t) * (Wu_e x_t), fp32
+ * [T*kprime][inter].  One kernel: each weight row is decoded in registers and applied
+ * to every token of its expert. */
+moe_status moe_expert_gateup_q(const moe_layer *layer, const float *d_x, int32_t T, int32_t kprime,
+                               const int32_t *d_sorted_slot, const int32_t *d_work, float *d_h, hipStream_t stream);
+
+/* Down projection ("Red Metal dev8", step 4, second half): d_y[p] = Wd_e d_h[p], fp32
+ * [T*kprime][hidden] in sorted order. */
+moe_status moe_expert_down_q(const moe_layer *layer, const float *d_h, int32_t T, int32_t kprime,
+                             const int32_t *d_work, float *d_y, hipStream_t stream);
+
+/* Down projection fused with the weighted accumulation ("Red Metal dev8", steps 4-5):
+ * d_acc[t][c] += w * (Wd_e d_h[slot_pos[s]])[c] over the slots s of token t in ascending
+ * expert id, one fp32 multiply and one fp32 add per slot -- bit-identical to
+ * moe_expert_down_q followed by moe_accumulate.  d_h is in sorted order (as written by
+ * moe_expert_gateup_q).  Reads each selected expert's down matrix once per token, so it
+ * is meant for decode (few tokens); for many tokens per expert use the separate calls. */
+moe_status moe_expert_down_accumulate_q(const moe_layer *layer, const float *d_h, int32_t T, int32_t kprime,
+                                        const int32_t *d_ids, const float *d_w, const int32_t *d_slot_pos,
+                                        float *d_acc, hipStream_t stream);
+
+/* Weighted accumulation ("Red Metal dev8", step 5: accumulator += router_weight *
+ * expert_output after each expert).  d_acc[t][c] (in/out) gets w * y added for each
+ * slot of token t, taken in ascending expert id (the shared expert, id E, last), as
+ * one fp32 multiply and one fp32 add per slot.  d_y is in sorted order; d_slot_pos
+ * maps a slot to its sorted position. */
+moe_status moe_accumulate(const float *d_y, const float *d_w, const int32_t *d_ids, const int32_t *d_slot_pos,
+                          int32_t T, int32_t kprime, int32_t hidden, float *d_acc, hipStream_t stream);
+
+/* Bit-exact dequantization of one matrix to fp32, row-major rows x cols (debug/test). */
+moe_status moe_dequant_f32(int32_t qtype, int32_t rows, int32_t cols, const void *d_s0, const void *d_s1,
+                           const void *d_s2, const void *d_grids, float *d_out, hipStream_t stream);
+
+/* Unit-weight RMSNorm, x = h / sqrt(mean(h^2) + eps) per row ("Red Lite dev16": the
+ * routed MoE of a block reads the post-attention RMSNorm of the hidden state).
+ * d_h, d_x: [T][hidden] fp32 (may alias). */
+moe_status moe_rmsnorm(const float *d_h, int32_t T, int32_t hidden, float eps, float *d_x, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

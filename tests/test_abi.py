@@ -1,0 +1,133 @@
+"""The C-ABI library loads, exports every function include/moe.h declares, and rejects
+bad arguments on the host before anything is enqueued (CPU only: every call here fails
+validation, so no HIP call is made)."""
+import ctypes as C
+import glob
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+moe = pytest.importorskip("codebook_quantized_routed_amd")
+lib = moe.lib
+
+A = 0x10000          # an aligned fake device address: never dereferenced, validation fails first
+MIS = 0x10004        # misaligned
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        src = open(h).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names |= set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src))
+    return names
+
+
+def test_exports_every_declared_function():
+    names = declared_functions()
+    assert "moe_route_group" in names and "moe_expert_ffn_q" in names and "moe_accumulate" in names
+    for n in sorted(names):
+        assert hasattr(lib, n), n
+    assert set(moe.EXPORTS) == names
+
+
+def test_version_strings_sizes():
+    assert moe.abi_version() == 1
+    for st in moe.STATUS:
+        assert lib.moe_status_string(st)
+    assert moe.grids_bytes() >= 512 * 8 + 2048 * 8
+    assert moe.workspace_bytes(1, 11, 2048, 512) == 11 * 512 * 4
+    assert moe.workspace_bytes(0, 11, 2048, 512) == 0
+    assert moe.workspace_bytes(1, 11, 2048, 300) == 0
+
+
+def rg(**kw):
+    a = dict(logits=A, T=1, E=512, k=10, add_shared=1, ids=A, w=A, counts=A, offsets=A, ss=A, sp=A, act=A)
+    a.update(kw)
+    return lib.moe_route_group(a["logits"], a["T"], a["E"], a["k"], a["add_shared"], a["ids"], a["w"], a["counts"],
+                               a["offsets"], a["ss"], a["sp"], a["act"], None)
+
+
+def test_route_group_rejects():
+    assert rg(ids=None) == -1
+    assert rg(act=None) == -1
+    assert rg(k=0) == -2
+    assert rg(k=17) == -2
+    assert rg(E=8, k=9) == -2
+    assert rg(T=0) == -2
+    assert rg(E=1024, add_shared=1) == -2
+    assert rg(add_shared=2) == -2
+    assert rg(w=MIS) == -4
+    assert rg(logits=MIS) == -4
+
+
+def layer(**kw):
+    d = moe.Layer()
+    d.hidden, d.inter, d.n_experts, d.has_shared, d.n_banks = 2048, 512, 512, 1, 1
+    d.grids = A
+    b = d.banks[0]
+    b.qtype, b.first_expert, b.n_experts = 1, 0, 513
+    for name in ("gate", "up", "down"):
+        arr = getattr(b, name)
+        for j in range(3):
+            arr[j] = A
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def ffn(d, ws_bytes=1 << 30, **kw):
+    a = dict(x=A, T=1, kp=11, ss=A, work=A, y=A, ws=A)
+    a.update(kw)
+    return lib.moe_expert_ffn_q(C.byref(d), a["x"], a["T"], a["kp"], a["ss"], a["work"], a["y"], a["ws"],
+                                ws_bytes, None)
+
+
+def test_expert_ffn_rejects():
+    assert lib.moe_expert_ffn_q(None, A, 1, 11, A, A, A, A, 1 << 30, None) == -1
+    assert lib.moe_expert_gateup_q(C.byref(layer()), A, 1, 11, A, None, A, None) == -1
+    assert lib.moe_expert_down_q(C.byref(layer()), A, 1, 11, A, MIS, None) == -4
+    assert lib.moe_expert_down_accumulate_q(C.byref(layer()), A, 1, 0, A, A, A, A, None) == -2
+    assert ffn(layer(), x=None) == -1
+    assert ffn(layer(grids=None)) == -1
+    assert ffn(layer(hidden=300)) == -2
+    assert ffn(layer(inter=4096)) == -2
+    assert ffn(layer(n_banks=0)) == -2
+    assert ffn(layer(n_experts=600)) == -2          # banks no longer cover E + shared
+    assert ffn(layer(), T=0) == -2
+    assert ffn(layer(), kp=18) == -2
+    assert ffn(layer(), ws_bytes=100) == -5
+    assert ffn(layer(), y=MIS) == -4
+    assert ffn(layer(grids=MIS)) == -4
+    d = layer()
+    d.banks[0].qtype = 3
+    assert ffn(d) == -3
+    d = layer()
+    d.banks[0].up[1] = None
+    assert ffn(d) == -1
+    d = layer()
+    d.banks[0].down[2] = MIS
+    assert ffn(d) == -4
+    d = layer()
+    d.banks[0].first_expert = 1
+    assert ffn(d) == -2
+
+
+def test_other_rejects():
+    assert lib.moe_accumulate(None, A, A, A, 1, 11, 2048, A, None) == -1
+    assert lib.moe_accumulate(A, A, A, A, 1, 11, 2000, A, None) == -2
+    assert lib.moe_accumulate(A, A, A, A, 1, 18, 2048, A, None) == -2
+    assert lib.moe_accumulate(A, A, A, MIS, 1, 11, 2048, A, None) == -4
+    assert lib.moe_dequant_f32(3, 8, 256, A, A, A, A, A, None) == -3
+    assert lib.moe_dequant_f32(1, 8, 100, A, A, A, A, A, None) == -2
+    assert lib.moe_dequant_f32(1, 7, 256, A, A, A, A, A, None) == -2
+    assert lib.moe_dequant_f32(1, 8, 256, A, A, None, A, A, None) == -1
+    assert lib.moe_dequant_f32(1, 8, 256, A, A, A, A, MIS, None) == -4
+    assert lib.moe_rmsnorm(None, 1, 2048, 1e-6, A, None) == -1
+    assert lib.moe_rmsnorm(A, 0, 2048, 1e-6, A, None) == -2
+    assert lib.moe_rmsnorm(A, 1, 2048, float("nan"), A, None) == -2
+    assert lib.moe_grids_expand(A, None, A, None) == -1
+    assert lib.moe_grids_expand(A, A, MIS, None) == -4

@@ -1,0 +1,252 @@
+"""GPU parity: the HIP path through the C ABI against the oracle on the same seeded bytes.
+
+Bit-exact: expanded grids, dequantized weights, routing ids and grouping arrays, and
+the accumulation given the same y and w.  Tolerance (max |error| <= 2e-5 * ||ref||_2 per
+output row): expert outputs y and layer outputs acc.  Router weights: a few ulp (the
+device exp differs from libm's by rounding only).
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+try:
+    import codebook_quantized_routed_amd as moe  # noqa: E402
+except ImportError:
+    if torch.cuda.device_count() > 0:
+        raise                      # on a GPU machine a missing library is an error
+    pytest.skip("HIP library not built (CPU-only machine)", allow_module_level=True)
+import oracle as O  # noqa: E402
+import synth  # noqa: E402
+from gpu_util import (Run, assert_rows_close, dev, device_grids, device_layer, log, run_layer,  # noqa: E402
+                      y_in_slot_order)
+
+IQ2, IQ1 = synth.QTYPE_IQ2XS, synth.QTYPE_IQ1M
+
+
+@pytest.fixture(scope="module")
+def grids(grids_compact):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return device_grids(*grids_compact)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def oracle_threads():
+    O.set_threads(8)
+    yield
+    O.set_threads(1)
+
+
+def test_grids_expand_bit_exact(grids, ogrids, grids_compact):
+    g = grids.cpu().numpy()
+    np.testing.assert_array_equal(g[:4096].reshape(512, 8), ogrids.iq2_array())
+    np.testing.assert_array_equal(g[4096:20480].view(np.int8).reshape(2048, 8), ogrids.iq1_array())
+
+    # the compact rows the mat-vec kernels build their LDS tables from
+    c2, c1 = grids_compact
+    np.testing.assert_array_equal(g[20480:21504].view(np.uint16), c2)
+    np.testing.assert_array_equal(g[21504:25600].view(np.uint16), c1)
+    assert g.size == moe.grids_bytes() == 25600
+
+
+def _dequant_gpu(qt, rows, cols, streams, grids):
+    out = torch.empty((rows, cols), dtype=torch.float32, device="cuda")
+    moe.dequant_f32(qt, rows, cols, dev(streams[0]), dev(streams[1]), dev(streams[2]), grids, out)
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("qt,rows,cols", [(IQ2, 512, 2048), (IQ2, 2048, 512), (IQ1, 512, 2048), (IQ1, 2048, 512),
+                                          (IQ2, 8, 256), (IQ1, 24, 768)])
+def test_dequant_bit_exact_seeded(grids, ogrids, qt, rows, cols):
+    log(f"dequant qt={qt} {rows}x{cols}")
+    streams = [a[0] for a in synth.qbank(qt, 1, rows, cols, 9, f"dq/{qt}/{rows}/{cols}")]
+    got = _dequant_gpu(qt, rows, cols, streams, grids)
+    ref = O.dequant(O.qmat(qt, rows, cols, streams), ogrids)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_dequant_bit_exact_every_code(grids, ogrids):
+    """Every IQ2 code under every scale and every IQ1 code under every scale."""
+    from test_oracle_dequant import encode_iq1, encode_iq2
+    rows, cols = 4096, 2048
+    ng, nb = cols // 8, cols // 256
+    code = np.arange(rows * ng, dtype=np.int64).reshape(rows, ng) % 65536
+    r_, b_, i_ = np.arange(rows)[:, None, None], np.arange(nb)[None, :, None], np.arange(8)[None, None, :]
+    d = synth.uniform(1, "dq/d", rows * nb).reshape(rows, nb)
+    d16 = (1e-3 * (0.5 + d)).astype(np.float16).view(np.uint16)
+    s2 = encode_iq2(code & 511, code >> 9, (r_ // 256 + b_ + i_ + r_) % 16, d16)
+    got = _dequant_gpu(IQ2, rows, cols, s2, grids)
+    ref = O.dequant(O.qmat(IQ2, rows, cols, s2), ogrids)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    rows = 128
+    code = np.arange(rows * ng, dtype=np.int64).reshape(rows, ng) % 4096
+    r_, i_ = np.arange(rows)[:, None, None], np.arange(16)[None, None, :]
+    s1 = encode_iq1(code & 2047, code >> 11, (r_ // 16 + b_ + i_ + r_) % 8, d16[:rows])
+    got = _dequant_gpu(IQ1, rows, cols, s1, grids)
+    ref = O.dequant(O.qmat(IQ1, rows, cols, s1), ogrids)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+ROUTE_CASES = [  # T, E, k, shared, zipf
+    (1, 512, 10, True, 0.0), (8, 512, 10, True, 0.0), (256, 512, 10, False, 0.0), (256, 512, 10, False, 1.1),
+    (1024, 512, 10, True, 0.0), (1, 16, 4, False, 0.0), (33, 16, 16, True, 0.0), (5, 1023, 16, True, 0.0),
+    (3, 64, 1, False, 0.0), (2000, 100, 7, True, 0.0),
+]
+
+
+@pytest.mark.parametrize("T,E,k,shared,zipf", ROUTE_CASES)
+def test_route_group_bit_exact(T, E, k, shared, zipf):
+    log(f"route_group T={T} E={E} k={k} shared={shared} zipf={zipf}")
+    lg = synth.logits(T, E, tag=f"rg/{T}/{E}", zipf_alpha=zipf)
+    r = Run(T, E, k, shared, 256, 256)
+    r.route(dev(lg))
+    g = r.host()
+    ids, w = O.route(lg, k, shared)
+    np.testing.assert_array_equal(g["ids"], ids)
+    np.testing.assert_allclose(g["w"], w, rtol=8 * 2.0 ** -24, atol=0)
+    counts, offsets, ss, sp = O.group(ids, E + int(shared))
+    np.testing.assert_array_equal(g["counts"], counts)
+    np.testing.assert_array_equal(g["offsets"], offsets)
+    np.testing.assert_array_equal(g["sorted_slot"], ss)
+    np.testing.assert_array_equal(g["slot_pos"], sp)
+    check_work(g["work"], counts, offsets, ss)
+
+
+def check_work(work, counts, offsets, ss):
+    """Work records: (n_active, n, 0, 0), then (e, offsets[e], offsets[e+1], first slot)."""
+    act = np.flatnonzero(counts)
+    rec = work.reshape(-1, 4)
+    np.testing.assert_array_equal(rec[0], [len(act), offsets[-1], 0, 0])
+    want = np.stack([act, offsets[act], offsets[act + 1], ss[offsets[act]]], axis=1)
+    np.testing.assert_array_equal(rec[1:1 + len(act)], want)
+
+
+def test_route_ties_and_explicit_mode():
+    l = np.array([[1.0, 3.0, 3.0, 0.5, 3.0, 2.0, 2.0, -1.0]], dtype=np.float32)
+    r = Run(1, 8, 5, True, 256, 256)
+    r.route(dev(l))
+    g = r.host()
+    np.testing.assert_array_equal(g["ids"][0], [1, 2, 4, 5, 6, 8])
+    # explicit ids / weights: only the shared slot and the grouping are written
+    ids = np.array([[7, 0, 3], [3, 1, 0]], np.int32)
+    w = np.array([[0.5, 0.3, 0.2], [0.6, 0.3, 0.1]], np.float32)
+    r = Run(2, 8, 3, True, 256, 256)
+    r.route(None, ids, w)
+    g = r.host()
+    np.testing.assert_array_equal(g["ids"][:, :3], ids)
+    np.testing.assert_array_equal(g["ids"][:, 3], [8, 8])
+    np.testing.assert_array_equal(g["w"][:, :3], w)
+    full = np.concatenate([ids, [[8], [8]]], axis=1)
+    counts, offsets, ss, sp = O.group(full, 9)
+    np.testing.assert_array_equal(g["sorted_slot"], ss)
+    np.testing.assert_array_equal(g["offsets"], offsets)
+    check_work(g["work"], counts, offsets, ss)
+
+
+# ------------------------------------------------------------------------- whole layer
+
+LAYER_CASES = {
+    # name: (banks, H, I, E, shared, T, k, zipf)
+    "tiny16_top4_iq2": ([(IQ2, 16)], 2048, 512, 16, 0, 1, 4, 0.0),
+    "decode_iq2_top10_shared": ([(IQ2, 512)], 2048, 512, 512, 1, 1, 10, 0.0),
+    "decode8_iq1_top10_shared": ([(IQ1, 512)], 2048, 512, 512, 1, 8, 10, 0.0),
+    "small_mixed_ragged": ([(IQ2, 12), (IQ1, 20)], 512, 256, 32, 1, 19, 6, 0.0),
+    "small_mixed_many_tokens": ([(IQ1, 8), (IQ2, 8)], 256, 512, 16, 0, 96, 5, 0.0),
+    "mixed_h2048_t24_zipf": ([(IQ2, 24), (IQ1, 40)], 2048, 512, 64, 1, 24, 8, 1.0),
+}
+
+
+@pytest.fixture(scope="module")
+def layers(grids):
+    cache = {}
+
+    def get(name):
+        if name not in cache:
+            banks, H, I, E, shared, *_ = LAYER_CASES[name]
+            sl = synth.make_layer(banks, hidden=H, inter=I, n_experts=E, has_shared=shared, tag=f"L/{name}")
+            cache[name] = (sl, O.ExpertTable(sl), device_layer(sl, grids))
+        return cache[name]
+    return get
+
+
+@pytest.mark.parametrize("name", list(LAYER_CASES))
+def test_layer_matches_oracle(layers, ogrids, name):
+    banks, H, I, E, shared, T, k, zipf = LAYER_CASES[name]
+    log(f"layer {name}: T={T} E={E} k={k} H={H} I={I}")
+    sl, tab, dl = layers(name)
+    x = synth.activations(T, H, tag=f"L/{name}/x")
+    lg = synth.logits(T, E, tag=f"L/{name}/l", zipf_alpha=zipf)
+    acc0 = synth.activations(T, H, tag=f"L/{name}/acc") if T > 1 else None
+    g = run_layer(dl, x, k, shared, logits=lg, acc=acc0)
+    ref = O.moe_layer(tab, ogrids, x, k, shared, logits=lg, acc=acc0)
+    np.testing.assert_array_equal(g["ids"], ref["ids"])
+    assert_rows_close(y_in_slot_order(g), ref["y"], f"{name} y")
+    assert_rows_close(g["acc"], ref["acc"], f"{name} acc")
+    # accumulation is exactly defined given y and w: feed the oracle the GPU's y and w
+    acc_in = np.zeros((T, H), np.float32) if acc0 is None else acc0
+    np.testing.assert_array_equal(g["acc"], O.accumulate(y_in_slot_order(g), g["w"], g["ids"], acc_in))
+
+
+@pytest.mark.parametrize("name", list(LAYER_CASES))
+def test_decode_path_matches_split_path(layers, name):
+    """gate/up + fused down-accumulate == ffn_q + accumulate, bit for bit; and
+    ffn_q == gate/up followed by down."""
+    banks, H, I, E, shared, T, k, zipf = LAYER_CASES[name]
+    log(f"decode path {name}: T={T}")
+    sl, tab, dl = layers(name)
+    x = synth.activations(T, H, tag=f"D/{name}/x")
+    lg = synth.logits(T, E, tag=f"D/{name}/l", zipf_alpha=zipf)
+    acc0 = synth.activations(T, H, tag=f"D/{name}/acc")
+    a = run_layer(dl, x, k, shared, logits=lg, acc=acc0)
+    b = run_layer(dl, x, k, shared, logits=lg, acc=acc0, decode=True)
+    assert np.array_equal(a["acc"].view(np.uint32), b["acc"].view(np.uint32))
+    r = Run(T, E, k, shared, H, I)
+    r.route(dev(lg))
+    h = torch.zeros((T * r.kp, I), dtype=torch.float32, device="cuda")
+    r.gateup(dl, dev(x), h)
+    y2 = torch.zeros_like(r.y)
+    moe.expert_down_q(dl.desc, h, T, r.kp, r.work, y2)
+    r.ffn(dl, dev(x))
+    torch.cuda.synchronize()
+    assert torch.equal(r.y, y2)
+
+
+def test_permutation_invariance_and_determinism(layers):
+    sl, tab, dl = layers("small_mixed_ragged")
+    T, k = 7, 6
+    x = synth.activations(T, 512, tag="perm/x")
+    ids = np.stack([np.argsort(synth.u64(5, f"perm/{t}", 32), kind="stable")[:k] for t in range(T)]).astype(np.int32)
+    w = synth.uniform(5, "perm/w", T * k).reshape(T, k).astype(np.float32)
+    base = run_layer(dl, x, k, True, ids=ids, w=w)["acc"]
+    again = run_layer(dl, x, k, True, ids=ids, w=w)["acc"]
+    assert np.array_equal(base.view(np.uint32), again.view(np.uint32))
+    for s in range(3):
+        p = np.stack([np.argsort(synth.u64(s, f"pp/{t}", k), kind="stable") for t in range(T)])
+        got = run_layer(dl, x, k, True, ids=np.take_along_axis(ids, p, 1), w=np.take_along_axis(w, p, 1))["acc"]
+        assert np.array_equal(got.view(np.uint32), base.view(np.uint32))
+
+
+def test_single_expert_weight_one(layers, ogrids):
+    sl, tab, dl = layers("small_mixed_ragged")
+    x = synth.activations(3, 512, tag="one/x")
+    ids = np.array([[3], [20], [31]], np.int32)
+    g = run_layer(dl, x, 1, False, ids=ids, w=np.ones((3, 1), np.float32))
+    for t in range(3):
+        ref = O.expert_ffn(tab, int(ids[t, 0]), ogrids, x[t])
+        assert_rows_close(g["acc"][t], ref, f"single expert {ids[t, 0]}")
+        # 0 + 1.0 * y == y exactly on the device too
+        np.testing.assert_array_equal(g["acc"][t], y_in_slot_order(g)[t])
+
+
+def test_rmsnorm_matches_oracle():
+    h = synth.activations(33, 2048, tag="rms/h") * 3.0
+    out = torch.empty((33, 2048), dtype=torch.float32, device="cuda")
+    moe.rmsnorm(dev(h), 33, 2048, 1e-6, out)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(out.cpu().numpy(), O.rmsnorm(h, 1e-6), rtol=4e-6, atol=1e-7)
+    hd = dev(h)
+    moe.rmsnorm(hd, 33, 2048, 1e-6, hd)  # in place
+    np.testing.assert_array_equal(hd.cpu().numpy(), out.cpu().numpy())
