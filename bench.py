@@ -15,6 +15,7 @@ Prints one JSON line.  Usage: python bench.py [--steps K] [--warmup W] [--gpus 1
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -35,12 +36,45 @@ WORKLOADS = {
                                 "as prefill_mixed_t256 with Zipf(1.1)-skewed router logits"),
 }
 METRIC = "tokens/sec per routed MoE layer + achieved HBM GB/s (% of peak) at top-10/512"
+ROOT = os.path.dirname(os.path.abspath(__file__))
+# Sources that define the mat-vec kernels; the counter summary below records their digest.
+KERNEL_SOURCES = ("codebook_quantized_routed_amd/csrc/common.hpp", "codebook_quantized_routed_amd/csrc/decode.hpp",
+                  "codebook_quantized_routed_amd/csrc/k_gemv.hip")
+TRAFFIC_FILES = {"decode_iq2": "profiles/hbm_traffic_decode_iq2_t1.txt"}
 HBM_PEAK_GBS = 8000.0
 H, I, E = 2048, 512, 512
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_digest() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` (FETCH_SIZE + WRITE_SIZE counters, each scaled by
+    the reading of the same counter for a copy of known size) from the committed counter
+    summary of this workload; None when there is none or the kernel sources changed after
+    the counters were taken."""
+    rel = TRAFFIC_FILES.get(workload)
+    if rel is None or not os.path.exists(os.path.join(ROOT, rel)):
+        return None
+    kv = {}
+    with open(os.path.join(ROOT, rel)) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith((" ", "#", "\t")):
+                key, val = line.split(":", 1)
+                kv[key.strip()] = val.strip()
+    if kv.get("kernel_sources_sha256") != kernel_digest():
+        return None
+    v = kv.get(f"{kernel}.traffic_bytes_per_launch")
+    return int(v) if v else None
 
 
 def main():
@@ -143,17 +177,53 @@ def main():
         bytes_per_step.append(gu + dn)
     bytes_step = float(np.mean(bytes_per_step))
 
-    # ---- per-kernel timing: events on the launch stream bracket the gate/up kernel and
-    # the down + accumulate kernel of every step
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    for j in range(args.steps):
-        step(args.warmup + j, evs[j])
-    torch.cuda.synchronize()
-    gu_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    dn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    # ---- per-kernel timing.  Every timed step is routed first into buffers of its own;
+    # then each kernel runs once per step, back to back, queued behind a GPU sleep so the
+    # host never starves the queue, between two events on the launch stream.  The same
+    # launches appear in a kernel trace of this command.
+    K = args.steps
+    per = []
+    for j in range(K):
+        b = dict(ids=torch.zeros((T, kp), **i32), w=torch.zeros((T, kp), dtype=torch.float32, device=dev),
+                 counts=torch.zeros(n_ids, **i32), offsets=torch.zeros(n_ids + 1, **i32),
+                 ss=torch.zeros(T * kp, **i32), sp=torch.zeros(T * kp, **i32),
+                 work=torch.zeros(moe.work_ints(n_ids), **i32),
+                 h=torch.zeros((T * kp, I), dtype=torch.float32, device=dev))
+        per.append(b)
+    acc_k = torch.zeros((K, T, H), dtype=torch.float32, device=dev)
+
+    def rg_k(j):
+        b = per[j]
+        moe.route_group(lgs[args.warmup + j], T, E, k, shared, b["ids"], b["w"], b["counts"], b["offsets"], b["ss"],
+                        b["sp"], b["work"])
+
+    def gu_k(j):
+        b = per[j]
+        moe.expert_gateup_q(layers[(args.warmup + j) % len(layers)].desc, xs[args.warmup + j], T, kp, b["ss"],
+                            b["work"], b["h"])
+
+    def dn_k(j):
+        b = per[j]
+        moe.expert_down_accumulate_q(layers[(args.warmup + j) % len(layers)].desc, b["h"], T, kp, b["ids"], b["w"],
+                                     b["sp"], acc_k[j])
+
+    def back_to_back(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(50_000_000)
+        e0.record()
+        for j in range(K):
+            fn(j)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K
+
+    for j in range(K):
+        rg_k(j)
+    back_to_back(gu_k)  # warm: code objects and first touches
+    rg_ms = back_to_back(rg_k)
+    gu_ms = back_to_back(gu_k)
+    dn_ms = back_to_back(dn_k)
 
     # ---- whole-step timing
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -212,10 +282,12 @@ def main():
         "algorithmic_bytes_per_step": int(bytes_step),
         "roofline": {"bound": "hbm", "kernel": "k_gateup (dequant gate/up mat-vec + SiLU*up)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(args.workload, "k_gateup_wide"),
                      "bytes_per_launch": int(gu_b), "launch_us": round(gu_ms * 1e3, 3)},
         "down_accumulate": {"achieved_gbs": round(dn_b / (dn_ms * 1e-3) / 1e9, 1), "bytes_per_launch": int(dn_b),
                             "launch_us": round(dn_ms * 1e3, 3)},
+        "route_group": {"launch_us": round(rg_ms * 1e3, 3)},
         "parity": parity,
     }
     if not args.no_cpu:
@@ -251,8 +323,8 @@ def cpu_baseline(layer, c2, c1, xs, lgs, k, shared, T, budget_s):
     tab = O.ExpertTable(layer)
     t0 = time.time()
     n = 0
-    while n < len(xs) and (n < 2 or time.time() - t0 < budget_s):
-        O.moe_layer(tab, g, xs[n], k, shared, logits=lgs[n], n_threads=cores)
+    while n < 2 or time.time() - t0 < budget_s:  # cycles over the steps' inputs
+        O.moe_layer(tab, g, xs[n % len(xs)], k, shared, logits=lgs[n % len(lgs)], n_threads=cores)
         n += 1
     dt = time.time() - t0
     return {"value": round(n * T / dt, 3), "unit": "tokens/s/layer", "cores": cores, "kind": "oracle",

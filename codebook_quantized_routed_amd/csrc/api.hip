@@ -40,7 +40,7 @@ moe_status check_layer(const moe_layer *layer, LayerArgs *out) {
   out->hidden = H;
   out->inter = I;
   out->n_banks = layer->n_banks;
-  out->pad = 0;
+  out->formats = 0;
   out->grids = (const uint8_t *)layer->grids;
   int next = 0;
   for (int b = 0; b < MOE_MAX_BANKS; b++) {
@@ -52,6 +52,7 @@ moe_status check_layer(const moe_layer *layer, LayerArgs *out) {
     if (s.first_expert != next || s.n_experts < 1) return MOE_E_SHAPE;
     next += s.n_experts;
     d.qtype = s.qtype;
+    out->formats |= s.qtype;
     d.first = s.first_expert;
     d.n = s.n_experts;
     for (int i = 0; i < 3; i++) {

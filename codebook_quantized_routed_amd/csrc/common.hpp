@@ -57,8 +57,9 @@ struct BankArgs {
 };
 
 // The layer, passed by value as a kernel argument (no device-side descriptor loads).
+// formats = OR of the banks' qtypes, set on the host.
 struct LayerArgs {
-  int hidden, inter, n_banks, pad;
+  int hidden, inter, n_banks, formats;
   BankArgs banks[MOE_MAX_BANKS];
   const uint8_t *grids;
 };
@@ -68,6 +69,19 @@ enum Which { kGate = 0, kUp = 1, kDown = 2 };
 // A value every lane of the wave holds: moved to a scalar register, so that what is
 // computed from it (bank choice, matrix bases) stays scalar too.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Load of a value the whole wave shares, through the scalar cache: the address must be
+// wave-uniform and the memory must not change while the kernel runs (it was written by
+// an earlier launch).  Scalar loads wait on their own counter, so a wave can use the
+// result without waiting for its outstanding vector loads.
+template <typename T>
+__device__ __forceinline__ T sload(const T *p) {
+  return *(const __attribute__((address_space(4))) T *)p;
+}
+__device__ __forceinline__ WorkRec sload(const WorkRec *p) {
+  const __attribute__((address_space(4))) int *q = (const __attribute__((address_space(4))) int *)p;
+  return WorkRec{q[0], q[1], q[2], q[3]};
+}
 
 // Bank lookup for expert e (uniform across a workgroup).
 __device__ inline const BankArgs &bank_of(const LayerArgs &L, int e) {

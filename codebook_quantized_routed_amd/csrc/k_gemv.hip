@@ -262,15 +262,11 @@ __device__ __forceinline__ float dot_chunk(const RowRaw &R, int q, const uint8_t
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
-__host__ __device__ inline int layer_formats(const LayerArgs &L) {
-  int f = 0;
-  for (int b = 0; b < L.n_banks; b++) f |= L.banks[b].qtype;
-  return f;
-}
+__host__ __device__ inline int layer_formats(const LayerArgs &L) { return L.formats; }
 
+// i must be wave-uniform.
 __device__ __forceinline__ WorkRec load_work(const WorkRec *w, int i) {
-  const int4 v = *(const int4 *)(w + i);
-  return WorkRec{uniform(v.x), uniform(v.y), uniform(v.z), uniform(v.w)};
+  return sload(w + i);
 }
 
 // ----------------------------------------------------------------------------- gate + up
@@ -311,7 +307,7 @@ __device__ __forceinline__ void gateup_run(const LayerArgs &L, GatePass &P, int 
                                            float *h) {
   const int H = L.hidden, I = L.inter;
   for (int p = P.W.p0; p < P.W.p1; p++) {
-    if (p > P.W.p0) load_x<QT>(x + (size_t)(uniform(sorted_slot[p]) / kprime) * H + 64 * q, P.X);
+    if (p > P.W.p0) load_x<QT>(x + (size_t)(sload(sorted_slot + p) / kprime) * H + 64 * q, P.X);
     else if constexpr (QT == MOE_Q_IQ1M_LIKE) {
 #pragma unroll
       for (int g = 0; g < 8; g++) {
@@ -339,19 +335,19 @@ __global__ void __launch_bounds__(256) k_gateup(LayerArgs L, const float *__rest
                                                 float *__restrict__ h) {
   extern __shared__ __align__(16) uint8_t lds[];
   constexpr int RPP = 64 / LPR;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, q = lane % LPR, sub = lane / LPR;
+  const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6), q = lane % LPR, sub = lane / LPR;
   const int formats = layer_formats(L);
   const TableLayout TL = table_layout(formats);
   const int ppe = L.inter / RPP, stride = gridDim.x * 4;
   int pass = blockIdx.x * 4 + wave;
   // the record index stays within the n_ids + 1 records even before the count is known
   const int a0 = min(pass / ppe, n_ids - 1);
-  const int4 rec0 = *(const int4 *)(work + 1 + a0);
-  const int total = uniform(work[0].e) * ppe;
+  const WorkRec rec0 = load_work(work, 1 + a0);
+  const int total = sload(&work[0].e) * ppe;
   GatePass P;
   bool have = pass < total;
   if (have) {
-    P.W = WorkRec{uniform(rec0.x), uniform(rec0.y), uniform(rec0.z), uniform(rec0.w)};
+    P.W = rec0;
     gateup_issue<LPR>(L, P, a0, pass - a0 * ppe, q, sub, kprime, x);
   }
   build_tables(L.grids, formats, TL, lds);
@@ -490,16 +486,20 @@ __device__ __forceinline__ void wide_issue(const LayerArgs &L, WideItem &It, int
 }
 
 template <int QT>
-__device__ __forceinline__ void wide_run(const LayerArgs &L, WideItem &It, X32 &X, int &cur_tok, int q, int kprime,
-                                         const float *x, const int32_t *sorted_slot, const uint8_t *lds,
+__device__ __forceinline__ void wide_run(const LayerArgs &L, WideItem &It, X32 &X, int &cur_tok, bool &gs_ok, int q,
+                                         int kprime, const float *x, const int32_t *sorted_slot, const uint8_t *lds,
                                          const TableLayout &TL, float *h) {
   const int H = L.hidden, I = L.inter;
   for (int p = It.W.p0; p < It.W.p1; p++) {
-    const int tok = (p == It.W.p0 ? It.W.slot0 : uniform(sorted_slot[p])) / kprime;
+    const int tok = (p == It.W.p0 ? It.W.slot0 : sload(sorted_slot + p)) / kprime;
     if (tok != cur_tok) {
       load_x32(x + (size_t)tok * H + 32 * q, X);
-      if constexpr (QT == MOE_Q_IQ1M_LIKE) group_sums32(X);
       cur_tok = tok;
+      gs_ok = false;
+    }
+    if constexpr (QT == MOE_Q_IQ1M_LIKE) {  // group sums of the current activations, once
+      if (!gs_ok) group_sums32(X);
+      gs_ok = true;
     }
 #pragma unroll
     for (int i = 0; i < kWideRows; i++) {
@@ -520,43 +520,40 @@ __global__ void __launch_bounds__(256) k_gateup_wide(LayerArgs L, const float *_
                                                      const WorkRec *__restrict__ work, int max_tokens, int n_ids,
                                                      float *__restrict__ h) {
   extern __shared__ __align__(16) uint8_t lds[];
-  const int q = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int q = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
   const int formats = layer_formats(L);
   const TableLayout TL = table_layout(formats);
   const TableRegs tr = tables_load(L.grids, formats);
   const int ipe = L.inter / kWideRows, stride = gridDim.x * 4;
   int item = blockIdx.x * 4 + wave;
   const int a0 = min(item / ipe, n_ids - 1);  // within the n_ids + 1 records before the count is known
-  const int4 rec0 = *(const int4 *)(work + 1 + a0);
-  const int total = uniform(work[0].e) * ipe;
+  const WorkRec rec0 = load_work(work, 1 + a0);
+  const int total = sload(&work[0].e) * ipe;
   WideItem It;
   X32 X;
   int cur_tok = -1;
+  bool gs_ok = false;
   bool have = item < total;
   if (have) {
-    It.W = WorkRec{uniform(rec0.x), uniform(rec0.y), uniform(rec0.z), uniform(rec0.w)};
+    It.W = rec0;
     wide_issue(L, It, item - a0 * ipe, q);
-    const int tok = It.W.slot0 / kprime;
-    load_x32(x + (size_t)tok * L.hidden + 32 * q, X);
-    cur_tok = tok;
-    if (It.qt == MOE_Q_IQ1M_LIKE) group_sums32(X);
+    cur_tok = It.W.slot0 / kprime;
+    load_x32(x + (size_t)cur_tok * L.hidden + 32 * q, X);
   }
   tables_store(tr, formats, TL, lds);
   while (have) {
     if (It.W.p1 - It.W.p0 <= max_tokens) {
       if (It.qt == MOE_Q_IQ2XS_LIKE)
-        wide_run<MOE_Q_IQ2XS_LIKE>(L, It, X, cur_tok, q, kprime, x, sorted_slot, lds, TL, h);
+        wide_run<MOE_Q_IQ2XS_LIKE>(L, It, X, cur_tok, gs_ok, q, kprime, x, sorted_slot, lds, TL, h);
       else
-        wide_run<MOE_Q_IQ1M_LIKE>(L, It, X, cur_tok, q, kprime, x, sorted_slot, lds, TL, h);
+        wide_run<MOE_Q_IQ1M_LIKE>(L, It, X, cur_tok, gs_ok, q, kprime, x, sorted_slot, lds, TL, h);
     }
     item += stride;
     have = item < total;
     if (have) {
       const int a = item / ipe;
-      const int prev_qt = It.qt;
       It.W = load_work(work, 1 + a);
       wide_issue(L, It, item - a * ipe, q);
-      if (It.qt != prev_qt) cur_tok = -1;  // group sums depend on the format
     }
   }
 }
@@ -584,11 +581,11 @@ __global__ void __launch_bounds__(256) k_down(LayerArgs L, const float *__restri
                                               float *__restrict__ y) {
   extern __shared__ __align__(16) uint8_t lds[];
   constexpr int RPP = 64 / LPR;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, q = lane % LPR, sub = lane / LPR;
+  const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6), q = lane % LPR, sub = lane / LPR;
   const int formats = layer_formats(L);
   const TableLayout TL = table_layout(formats);
   const int ppe = L.hidden / RPP;
-  const int total = uniform(work[0].e) * ppe;
+  const int total = sload(&work[0].e) * ppe;
   build_tables(L.grids, formats, TL, lds);
   for (int pass = blockIdx.x * 4 + wave; pass < total; pass += gridDim.x * 4) {
     const int a = pass / ppe, rp = pass - a * ppe;
@@ -603,45 +600,74 @@ __global__ void __launch_bounds__(256) k_down(LayerArgs L, const float *__restri
 }
 
 // ----------------------------------------------------------------------------- down + accumulate
-// One workgroup of 16 waves per (token, block of RPP output rows); wave j takes slot j
-// (and j + 16): the down rows of that slot's expert are dotted with its h, and the RPP
-// outputs are accumulated as acc += w * y in ascending expert id ("Red Metal dev8",
-// step 5), one rounded multiply and one rounded add per slot, so the result equals the
-// separate accumulation exactly.
-constexpr int kDownAccWaves = 16;
+// One workgroup of 4 waves per (token, block of RPP output rows); wave w takes the
+// token's slots w, w + 4, ...: the down rows of each slot's expert are dotted with its
+// h, and the RPP outputs are accumulated as acc += w * y in ascending expert id ("Red
+// Metal dev8", step 5), one rounded multiply and one rounded add per slot, so the
+// result equals the separate accumulation exactly.
+//
+// Every global load is issued before the first wait: LDS tables, the slots' h rows
+// (when STAGE, copied whole into the wave's LDS area in coalesced 16-byte pieces, each
+// 64-float chunk padded to 68 floats so the lanes of different chunks hit different
+// banks), the slots' weight rows, acc and w.  The slot scalars come through the scalar
+// cache, so issuing the weight loads never waits on a vector load.
+constexpr int kDaWaves = 4;
+constexpr int kDaSlots = (MOE_MAX_K + 1 + kDaWaves - 1) / kDaWaves;  // slots per wave, at most
+constexpr int kChunkPad = 68;
+
+__host__ __device__ inline size_t down_acc_stage_bytes(int lpr) { return (size_t)kDaWaves * kDaSlots * lpr * kChunkPad * 4; }
 
 template <int QT, int LPR>
 __device__ __forceinline__ float down_slot_dot(const RowRaw &R, const float *hrow, int q, const uint8_t *lds,
                                                const TableLayout &TL) {
   XChunk X;
-  load_x<QT>(hrow + 64 * q, X);
+  load_x<QT>(hrow, X);
   return group_sum_first<LPR>(dot_chunk<QT>(R, q, lds, TL, X));
 }
 
-template <int LPR>
-__global__ void __launch_bounds__(1024) k_down_acc(LayerArgs L, const float *__restrict__ h, int kprime,
-                                                   const int32_t *__restrict__ ids, const float *__restrict__ w,
-                                                   const int32_t *__restrict__ slot_pos, float *__restrict__ acc) {
+template <int LPR, bool STAGE>
+__global__ void __launch_bounds__(256) k_down_acc(LayerArgs L, const float *__restrict__ h, int kprime,
+                                                  const int32_t *__restrict__ ids, const float *__restrict__ w,
+                                                  const int32_t *__restrict__ slot_pos, float *__restrict__ acc) {
   extern __shared__ __align__(16) uint8_t lds[];
-  constexpr int RPP = 64 / LPR;
+  constexpr int RPP = 64 / LPR, HS = LPR * kChunkPad, F4 = LPR * 16;  // F4: float4 pieces of one h row
   __shared__ float ydot[MOE_MAX_K + 1][RPP];
+  __shared__ float wsorted[MOE_MAX_K + 1];
   __shared__ int order[MOE_MAX_K + 1];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, q = lane % LPR, sub = lane / LPR;
+  const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6), q = lane % LPR, sub = lane / LPR;
   const int H = L.hidden, I = L.inter, tiles = H / RPP;
   const int t = blockIdx.x / tiles, tile = blockIdx.x - t * tiles;
   const int r = tile * RPP + sub;
-  const int32_t *tok_ids = ids + (size_t)t * kprime;
   const int formats = layer_formats(L);
   const TableLayout TL = table_layout(formats);
+  float *hs = (float *)(lds + TL.bytes) + wave * kDaSlots * HS;
+  const TableRegs tr = tables_load(L.grids, formats);
+  const int32_t *tok_ids = ids + (size_t)t * kprime;
+  const int32_t *tok_pos = slot_pos + (size_t)t * kprime;
 
-  RowRaw R[2];
-  int qt[2] = {0, 0}, p[2] = {0, 0};
+  // h rows first (L2 / MALL resident), then the weight rows (HBM)
+  u32x4 hv[STAGE ? kDaSlots : 1][STAGE ? (F4 + 63) / 64 : 1];
+  int p[kDaSlots];
 #pragma unroll
-  for (int i = 0; i < 2; i++) {
-    const int j = wave + kDownAccWaves * i;
+  for (int i = 0; i < kDaSlots; i++) {
+    const int j = wave + kDaWaves * i;
+    p[i] = j < kprime ? sload(tok_pos + j) : 0;
+    if constexpr (STAGE) {
+      if (j < kprime) {
+        const u32x4 *src = (const u32x4 *)(h + (size_t)p[i] * I);
+#pragma unroll
+        for (int v = 0; v < (F4 + 63) / 64; v++) hv[i][v] = src[min(v * 64 + lane, F4 - 1)];
+      }
+    }
+  }
+  RowRaw R[kDaSlots];
+  int qt[kDaSlots];
+#pragma unroll
+  for (int i = 0; i < kDaSlots; i++) {
+    const int j = wave + kDaWaves * i;
+    qt[i] = 0;
     if (j < kprime) {
-      const int e = uniform(tok_ids[j]);
-      p[i] = uniform(slot_pos[(size_t)t * kprime + j]);
+      const int e = sload(tok_ids + j);
       const BankArgs &B = bank_of(L, e);
       const QMat Wd = expert_mat(B, e, kDown, H, I);
       qt[i] = B.qtype;
@@ -653,20 +679,35 @@ __global__ void __launch_bounds__(1024) k_down_acc(LayerArgs L, const float *__r
   if (threadIdx.x < RPP) acc_in = acc[(size_t)t * H + tile * RPP + threadIdx.x];
   if (threadIdx.x < kprime) {
     const int j = threadIdx.x, me = tok_ids[j];
+    const float wj = w[(size_t)t * kprime + j];
     int rank = 0;
     for (int i = 0; i < kprime; i++) {
       const int o = tok_ids[i];
       rank += (o < me || (o == me && i < j)) ? 1 : 0;
     }
     order[rank] = j;
+    wsorted[rank] = wj;
   }
-  build_tables(L.grids, formats, TL, lds);
+  if constexpr (STAGE) {
+#pragma unroll
+    for (int i = 0; i < kDaSlots; i++) {
+      const int j = wave + kDaWaves * i;
+      if (j < kprime) {
+#pragma unroll
+        for (int v = 0; v < (F4 + 63) / 64; v++) {
+          const int f = v * 64 + lane;  // float4 piece f: floats 4f..4f+3 of the row
+          if (f < F4) *(u32x4 *)(hs + i * HS + (f >> 4) * kChunkPad + (f & 15) * 4) = hv[i][v];
+        }
+      }
+    }
+  }
+  tables_store(tr, formats, TL, lds);  // ends with the workgroup barrier
 
 #pragma unroll
-  for (int i = 0; i < 2; i++) {
-    const int j = wave + kDownAccWaves * i;
+  for (int i = 0; i < kDaSlots; i++) {
+    const int j = wave + kDaWaves * i;
     if (j < kprime) {
-      const float *hrow = h + (size_t)p[i] * I;
+      const float *hrow = STAGE ? hs + i * HS + q * kChunkPad : h + (size_t)p[i] * I + 64 * q;
       const float v = qt[i] == MOE_Q_IQ2XS_LIKE ? down_slot_dot<MOE_Q_IQ2XS_LIKE, LPR>(R[i], hrow, q, lds, TL)
                                                 : down_slot_dot<MOE_Q_IQ1M_LIKE, LPR>(R[i], hrow, q, lds, TL);
       if (q == 0) ydot[j][sub] = v;
@@ -675,10 +716,7 @@ __global__ void __launch_bounds__(1024) k_down_acc(LayerArgs L, const float *__r
   __syncthreads();
   if (threadIdx.x < RPP) {
     float a = acc_in;
-    for (int o = 0; o < kprime; o++) {
-      const int j = order[o];
-      a = __fadd_rn(a, __fmul_rn(w[(size_t)t * kprime + j], ydot[j][threadIdx.x]));
-    }
+    for (int o = 0; o < kprime; o++) a = __fadd_rn(a, __fmul_rn(wsorted[o], ydot[order[o]][threadIdx.x]));
     acc[(size_t)t * H + tile * RPP + threadIdx.x] = a;
   }
 }
@@ -730,9 +768,25 @@ hipError_t launch_down_gemv(const LayerArgs &L, const float *h, int T, int kprim
 hipError_t launch_down_accumulate(const LayerArgs &L, const float *h, int T, int kprime, const int32_t *ids,
                                   const float *w, const int32_t *slot_pos, float *acc, hipStream_t s) {
   const int lpr = lanes_per_row(L.inter), rpp = 64 / lpr;
-  const size_t shmem = table_layout(layer_formats(L)).bytes;
-  MOE_LPR_DISPATCH(lpr, k_down_acc, dim3((unsigned)(T * (L.hidden / rpp))), dim3(64 * kDownAccWaves), shmem, s, L,
-                   h, kprime, ids, w, slot_pos, acc);
+  const size_t tables = table_layout(layer_formats(L)).bytes;
+  const dim3 grid((unsigned)(T * (L.hidden / rpp))), block(64 * kDaWaves);
+  // h is staged in LDS for inter <= 512 (at most 43.5 KB per workgroup)
+  switch (lpr) {
+    case 4:
+      hipLaunchKernelGGL((k_down_acc<4, true>), grid, block, tables + down_acc_stage_bytes(4), s, L, h, kprime, ids, w,
+                         slot_pos, acc);
+      break;
+    case 8:
+      hipLaunchKernelGGL((k_down_acc<8, true>), grid, block, tables + down_acc_stage_bytes(8), s, L, h, kprime, ids, w,
+                         slot_pos, acc);
+      break;
+    case 16:
+      hipLaunchKernelGGL((k_down_acc<16, false>), grid, block, tables, s, L, h, kprime, ids, w, slot_pos, acc);
+      break;
+    default:
+      hipLaunchKernelGGL((k_down_acc<32, false>), grid, block, tables, s, L, h, kprime, ids, w, slot_pos, acc);
+      break;
+  }
   return hipGetLastError();
 }
 

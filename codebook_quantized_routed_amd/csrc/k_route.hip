@@ -45,15 +45,15 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
 // orderable keys, sorted in the lane (descending key, ascending id on ties).
 //
 // Fast path: tau = the k-th largest of the 64 lane maxima is a lower bound on the k-th
-// largest key (those k maxima are k keys >= tau), so every selected key is >= tau.  The
-// few keys >= tau (about k to 2k for N(0,1) logits) are gathered in LDS and ranked
-// exactly against each other by (key descending, id ascending); rank < k is selected.
-// If more than kCand keys reach tau (heavy ties), the selection falls back to k rounds
-// of a wave-wide arg-max over the lanes' sorted lists.  Both give the same result.
-constexpr int kCand = 128;
+// largest key (those k maxima are k keys >= tau), so every selected key is >= tau.
+// tau comes from a bitwise search over ballots; the few keys >= tau (about k to 2k for
+// N(0,1) logits) are packed into LDS, one per lane, and each is ranked against the
+// others by (key descending, id ascending) through lane reads; rank < k is selected.
+// If more than 64 keys reach tau (heavy ties), the selection falls back to k rounds of
+// a wave-wide arg-max over the lanes' sorted lists.  Both give the same result.
+constexpr int kCand = 64;
 
 struct TopkLds {
-  uint32_t lane_max[64];
   uint32_t cand_key[kCand];
   int cand_id[kCand];
   uint32_t sel_key[MOE_MAX_K];
@@ -86,6 +86,11 @@ __device__ __forceinline__ void topk_select_rounds(uint32_t (&key)[VPL], int (&e
   }
 }
 
+// Number of set bits of m in the lanes below this one.
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+}
+
 template <int VPL>
 __device__ __forceinline__ void topk_wave(const float *__restrict__ l, int E, int k, int add_shared,
                                           int32_t *__restrict__ ids, float *__restrict__ w, int32_t *ids_copy,
@@ -93,10 +98,14 @@ __device__ __forceinline__ void topk_wave(const float *__restrict__ l, int E, in
   const int lane = threadIdx.x & 63;
   uint32_t key[VPL];
   int eid[VPL];
+  float lv[VPL];
+  // every lane loads (clamped index), so the loads are issued back to back
+#pragma unroll
+  for (int i = 0; i < VPL; i++) lv[i] = l[min(i * 64 + lane, E - 1)];
 #pragma unroll
   for (int i = 0; i < VPL; i++) {
     const int e = i * 64 + lane;
-    key[i] = e < E ? orderable(l[e]) : 0u;
+    key[i] = e < E ? orderable(lv[i]) : 0u;
     eid[i] = e;
   }
 #pragma unroll
@@ -111,62 +120,52 @@ __device__ __forceinline__ void topk_wave(const float *__restrict__ l, int E, in
       key[j] = tk;
       eid[j] = te;
     }
-  // tau: the lane maximum with exactly k-1 larger ones (ties by lane index)
-  S.lane_max[lane] = key[0];
-  __builtin_amdgcn_wave_barrier();
-  const uint32_t mine = key[0];
-  int above = 0;
-#pragma unroll 16
-  for (int j = 0; j < 64; j++) {
-    const uint32_t o = S.lane_max[j];
-    above += (o > mine || (o == mine && j < lane)) ? 1 : 0;
+  // tau: the largest t with at least k lane maxima >= t (the set of such t is closed
+  // downwards, so it is found bit by bit from the top).  At least k lanes hold a key.
+  uint32_t tau = 0u;
+  for (int b = 31; b >= 0; b--) {
+    const uint32_t c = tau | (1u << b);
+    if (__popcll(__ballot(key[0] >= c)) >= k) tau = c;
   }
-  const uint64_t at_k = __ballot(above == k - 1);
-  const uint32_t tau = (uint32_t)__builtin_amdgcn_readlane((int)mine, __ffsll((unsigned long long)at_k) - 1);
-  // candidates: keys >= tau (each lane's come first in its sorted list)
-  int c = 0;
+  // candidates: keys >= tau (each lane's come first in its sorted list); invalid keys
+  // are 0 < tau.  Position = candidates of lower lanes + index in the lane.
+  int base = 0, total = 0;
 #pragma unroll
-  for (int i = 0; i < VPL; i++) c += key[i] >= tau && key[i] != 0u ? 1 : 0;
-  int incl = c;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int n = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += n;
+  for (int i = 0; i < VPL; i++) {
+    const uint64_t m = __ballot(key[i] >= tau);
+    base += lanes_below(m);
+    total += __popcll(m);
   }
-  const int total = __builtin_amdgcn_readlane(incl, 63);
-  __builtin_amdgcn_wave_barrier();
   if (total <= kCand) {
-    const int base = incl - c;
 #pragma unroll
     for (int i = 0; i < VPL; i++)
-      if (i < c) {
+      if (key[i] >= tau) {
         S.cand_key[base + i] = key[i];
         S.cand_id[base + i] = eid[i];
       }
     __builtin_amdgcn_wave_barrier();
-    for (int ci = lane; ci < total; ci += 64) {
-      const uint32_t ck = S.cand_key[ci];
-      const int cid = S.cand_id[ci];
-      int rank = 0;
-      for (int j = 0; j < total; j++) {
-        const uint32_t ok = S.cand_key[j];
-        rank += (ok > ck || (ok == ck && S.cand_id[j] < cid)) ? 1 : 0;
-      }
-      if (rank < k) {
-        S.sel_key[rank] = ck;
-        S.sel_id[rank] = cid;
-      }
+    const uint32_t ck = lane < total ? S.cand_key[lane] : 0u;
+    const int cid = lane < total ? S.cand_id[lane] : 0x7FFFFFFF;
+    int rank = 0;
+    for (int j = 0; j < total; j++) {
+      const uint32_t ok = (uint32_t)__builtin_amdgcn_readlane((int)ck, j);
+      const int oid = __builtin_amdgcn_readlane(cid, j);
+      rank += (ok > ck || (ok == ck && oid < cid)) ? 1 : 0;
+    }
+    if (lane < total && rank < k) {
+      S.sel_key[rank] = ck;
+      S.sel_id[rank] = cid;
     }
   } else {
     topk_select_rounds<VPL>(key, eid, k, S);
   }
   __builtin_amdgcn_wave_barrier();
   // weights: lane j exponentiates selection j; the sum runs over j in order
-  const float top = from_orderable(S.sel_key[0]);
-  float ex = 0.0f;
+  float ex = 0.0f, top = 0.0f;
   int myid = 0;
   if (lane < k) {
     myid = S.sel_id[lane];
+    top = from_orderable(S.sel_key[0]);
     ex = expf(__fsub_rn(from_orderable(S.sel_key[lane]), top));
   }
   float sum = 0.0f;
@@ -320,50 +319,47 @@ __global__ void __launch_bounds__(1024) k_group(const int32_t *__restrict__ ids,
 }
 
 // Grouping of at most 64 slots (decode): the same outputs as group_block, computed
-// directly.  Wave 0 ranks every slot among the others (stable: by id, then slot index);
-// each thread e then counts the slots below and at its id, and the first slot of each
-// active expert and its rank among the distinct ids come from the same counts.
+// from lane reads of the slot ids, with no LDS traffic and no barrier.  Wave 0 ranks
+// every slot among the others (stable: by id, then slot index) and writes the work
+// records; every thread e counts the slots below and at its id.
 constexpr int kTinySlots = 64;
 
 __device__ void group_tiny(const int32_t *ids_l, int n, int n_ids, int32_t *__restrict__ counts,
                            int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_slot,
-                           int32_t *__restrict__ slot_pos, WorkRec *__restrict__ work, int *first_l) {
-  const int tid = threadIdx.x;
-  if (tid < 64) {
-    const int my = tid < n ? ids_l[tid] : 0x7FFFFFFF;
-    int rank = 0, first = 1;
+                           int32_t *__restrict__ slot_pos, WorkRec *__restrict__ work) {
+  const int lane = threadIdx.x & 63;
+  const int my = lane < n ? ids_l[lane] : 0x7FFFFFFF;
+  if (threadIdx.x < 64) {
+    int rank = 0, same = 0, first = 1;
     for (int j = 0; j < n; j++) {
-      const int o = ids_l[j];
-      rank += (o < my || (o == my && j < tid)) ? 1 : 0;
-      first &= (o == my && j < tid) ? 0 : 1;
+      const int o = __builtin_amdgcn_readlane(my, j);
+      rank += (o < my || (o == my && j < lane)) ? 1 : 0;
+      same += o == my ? 1 : 0;
+      first &= (o == my && j < lane) ? 0 : 1;
     }
-    if (tid < n) {
-      sorted_slot[rank] = tid;
-      slot_pos[tid] = rank;
-      first_l[tid] = first;
+    const uint64_t firsts = __ballot(lane < n && first);
+    int distinct_below = 0;
+    for (int j = 0; j < n; j++)
+      distinct_below += ((firsts >> j) & 1u) && __builtin_amdgcn_readlane(my, j) < my ? 1 : 0;
+    if (lane < n) {
+      sorted_slot[rank] = lane;
+      slot_pos[lane] = rank;
+      if (first) work[1 + distinct_below] = WorkRec{my, rank, rank + same, lane};
+    }
+    if (lane == 0) {
+      offsets[n_ids] = n;
+      work[0] = WorkRec{(int)__popcll(firsts), n, 0, 0};
     }
   }
-  __syncthreads();
-  for (int e = tid; e < n_ids; e += blockDim.x) {
-    int below = 0, at = 0, distinct_below = 0, slot0 = -1;
+  for (int e = threadIdx.x; e < n_ids; e += blockDim.x) {
+    int below = 0, at = 0;
     for (int j = 0; j < n; j++) {
-      const int o = ids_l[j];
+      const int o = __builtin_amdgcn_readlane(my, j);
       below += o < e ? 1 : 0;
-      distinct_below += (o < e && first_l[j]) ? 1 : 0;
-      if (o == e) {
-        if (at == 0) slot0 = j;
-        at++;
-      }
+      at += o == e ? 1 : 0;
     }
     counts[e] = at;
     offsets[e] = below;
-    if (at > 0) work[1 + distinct_below] = WorkRec{e, below, below + at, slot0};
-  }
-  if (tid == 0) {
-    int distinct = 0;
-    for (int j = 0; j < n; j++) distinct += first_l[j];
-    offsets[n_ids] = n;
-    work[0] = WorkRec{distinct, n, 0, 0};
   }
 }
 
@@ -381,7 +377,6 @@ __global__ void __launch_bounds__(1024) k_route_group_small(const float *__restr
   __shared__ GroupLds S;
   __shared__ TopkLds TS[kGroupWaves];
   __shared__ int32_t ids_l[kSmallMaxSlots];
-  __shared__ int first_l[kTinySlots];
   const int kprime = k + add_shared;
   const int wave = threadIdx.x >> 6;
   for (int t = wave; t < T; t += kGroupWaves)
@@ -389,7 +384,7 @@ __global__ void __launch_bounds__(1024) k_route_group_small(const float *__restr
                    ids_l + t * kprime, TS[wave]);
   __syncthreads();
   if (T * kprime <= kTinySlots)
-    group_tiny(ids_l, T * kprime, E + add_shared, counts, offsets, sorted_slot, slot_pos, work, first_l);
+    group_tiny(ids_l, T * kprime, E + add_shared, counts, offsets, sorted_slot, slot_pos, work);
   else
     group_block(ids_l, T * kprime, E + add_shared, counts, offsets, sorted_slot, slot_pos, work, S);
 }
@@ -407,9 +402,21 @@ hipError_t launch_route_group(const float *logits, int T, int E, int k, int add_
                               int32_t *counts, int32_t *offsets, int32_t *sorted_slot, int32_t *slot_pos,
                               WorkRec *work, hipStream_t s) {
   const int kprime = k + add_shared;
-  if (T * kprime <= kSmallMaxSlots && T <= 4 * kGroupWaves) {
-    MOE_VPL_DISPATCH(E, k_route_group_small, dim3(1), dim3(1024), 0, s, logits, T, E, k, add_shared, ids, w, counts,
-                     offsets, sorted_slot, slot_pos, work);
+  // one launch for small batches; above 512 experts the 16 keys per lane do not fit
+  // the register budget of a 1024-thread workgroup, so those go through two launches
+  if (T * kprime <= kSmallMaxSlots && T <= 4 * kGroupWaves && E <= 512) {
+    if (E <= 64)
+      hipLaunchKernelGGL(k_route_group_small<1>, dim3(1), dim3(1024), 0, s, logits, T, E, k, add_shared, ids, w,
+                         counts, offsets, sorted_slot, slot_pos, work);
+    else if (E <= 128)
+      hipLaunchKernelGGL(k_route_group_small<2>, dim3(1), dim3(1024), 0, s, logits, T, E, k, add_shared, ids, w,
+                         counts, offsets, sorted_slot, slot_pos, work);
+    else if (E <= 256)
+      hipLaunchKernelGGL(k_route_group_small<4>, dim3(1), dim3(1024), 0, s, logits, T, E, k, add_shared, ids, w,
+                         counts, offsets, sorted_slot, slot_pos, work);
+    else
+      hipLaunchKernelGGL(k_route_group_small<8>, dim3(1), dim3(1024), 0, s, logits, T, E, k, add_shared, ids, w,
+                         counts, offsets, sorted_slot, slot_pos, work);
   } else {
     MOE_VPL_DISPATCH(E, k_topk, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, kprime, add_shared, ids, w);
     hipError_t err = hipGetLastError();
