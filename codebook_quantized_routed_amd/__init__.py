@@ -19,6 +19,7 @@ IQ1M_LIKE = 2
 MAX_BANKS = 4
 MAX_K = 16
 MAX_IDS = 1024
+MATVEC_MAX_TOKENS = 2  # experts with more tokens run on the matrix cores (MOE_MATVEC_MAX_TOKENS)
 
 STATUS = {0: "MOE_OK", -1: "MOE_E_NULL", -2: "MOE_E_SHAPE", -3: "MOE_E_QTYPE", -4: "MOE_E_ALIGN",
           -5: "MOE_E_WORKSPACE", -6: "MOE_E_HIP"}

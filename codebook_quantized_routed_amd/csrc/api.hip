@@ -138,6 +138,22 @@ moe_status check_ffn_common(const moe_layer *layer, LayerArgs *L, int32_t T, int
   return MOE_OK;
 }
 
+// Both kernels of a projection: the mat-vec kernel takes the experts of the first work
+// list, the matrix-core kernel those of the second.
+hipError_t launch_gateup(const LayerArgs &L, const float *x, int T, int kprime, const int32_t *sorted_slot,
+                         const WorkRec *work, int n_ids, float *h, hipStream_t s) {
+  hipError_t err = launch_gateup_gemv(L, x, T, kprime, sorted_slot, work, n_ids, MOE_MATVEC_MAX_TOKENS, h, s);
+  if (err != hipSuccess) return err;
+  return launch_gateup_mfma(L, x, T, kprime, sorted_slot, work, n_ids, h, s);
+}
+
+hipError_t launch_down(const LayerArgs &L, const float *h, int T, int kprime, const WorkRec *work, int n_ids, float *y,
+                       hipStream_t s) {
+  hipError_t err = launch_down_gemv(L, h, T, kprime, work, n_ids, MOE_MATVEC_MAX_TOKENS, y, s);
+  if (err != hipSuccess) return err;
+  return launch_down_mfma(L, h, T, kprime, work, n_ids, y, s);
+}
+
 }  // namespace
 
 moe_status moe_expert_gateup_q(const moe_layer *layer, const float *d_x, int32_t T, int32_t kprime,
@@ -147,8 +163,7 @@ moe_status moe_expert_gateup_q(const moe_layer *layer, const float *d_x, int32_t
   if (st != MOE_OK) return st;
   const int n_ids = layer->n_experts + layer->has_shared;
   clear_pending();
-  return from_hip(launch_gateup_gemv(L, d_x, T, kprime, d_sorted_slot, (const WorkRec *)d_work, n_ids, 1 << 30, d_h,
-                                     stream));
+  return from_hip(launch_gateup(L, d_x, T, kprime, d_sorted_slot, (const WorkRec *)d_work, n_ids, d_h, stream));
 }
 
 moe_status moe_expert_down_q(const moe_layer *layer, const float *d_h, int32_t T, int32_t kprime,
@@ -158,7 +173,7 @@ moe_status moe_expert_down_q(const moe_layer *layer, const float *d_h, int32_t T
   if (st != MOE_OK) return st;
   const int n_ids = layer->n_experts + layer->has_shared;
   clear_pending();
-  return from_hip(launch_down_gemv(L, d_h, T, kprime, (const WorkRec *)d_work, n_ids, 1 << 30, d_y, stream));
+  return from_hip(launch_down(L, d_h, T, kprime, (const WorkRec *)d_work, n_ids, d_y, stream));
 }
 
 moe_status moe_expert_down_accumulate_q(const moe_layer *layer, const float *d_h, int32_t T, int32_t kprime,
@@ -182,9 +197,9 @@ moe_status moe_expert_ffn_q(const moe_layer *layer, const float *d_x, int32_t T,
   const WorkRec *work = (const WorkRec *)d_work;
   float *h = (float *)d_ws;
   clear_pending();
-  hipError_t err = launch_gateup_gemv(L, d_x, T, kprime, d_sorted_slot, work, n_ids, 1 << 30, h, stream);
+  hipError_t err = launch_gateup(L, d_x, T, kprime, d_sorted_slot, work, n_ids, h, stream);
   if (err != hipSuccess) return from_hip(err);
-  return from_hip(launch_down_gemv(L, h, T, kprime, work, n_ids, 1 << 30, d_y, stream));
+  return from_hip(launch_down(L, h, T, kprime, work, n_ids, d_y, stream));
 }
 
 moe_status moe_accumulate(const float *d_y, const float *d_w, const int32_t *d_ids, const int32_t *d_slot_pos,

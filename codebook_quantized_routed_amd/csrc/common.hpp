@@ -143,6 +143,10 @@ hipError_t launch_gateup_gemv(const LayerArgs &L, const float *x, int T, int kpr
                               const WorkRec *work, int n_ids, int max_tokens, float *h, hipStream_t s);
 hipError_t launch_down_gemv(const LayerArgs &L, const float *h, int T, int kprime, const WorkRec *work, int n_ids,
                             int max_tokens, float *y, hipStream_t s);
+hipError_t launch_gateup_mfma(const LayerArgs &L, const float *x, int T, int kprime, const int32_t *sorted_slot,
+                              const WorkRec *work, int n_ids, float *h, hipStream_t s);
+hipError_t launch_down_mfma(const LayerArgs &L, const float *h, int T, int kprime, const WorkRec *work, int n_ids,
+                            float *y, hipStream_t s);
 hipError_t launch_down_accumulate(const LayerArgs &L, const float *h, int T, int kprime, const int32_t *ids,
                                   const float *w, const int32_t *slot_pos, float *acc, hipStream_t s);
 hipError_t launch_accumulate(const float *y, const float *w, const int32_t *ids, const int32_t *slot_pos, int T,

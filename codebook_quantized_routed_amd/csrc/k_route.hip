@@ -261,22 +261,26 @@ __device__ void group_block(const int32_t *ids, int n, int n_ids, int32_t *__res
   }
   const int excl = block_exclusive_scan(c, S);
   const int n_total = S.total;
-  const int aex = block_exclusive_scan(c > 0 ? 1 : 0, S);
-  const int n_active = S.total;
+  const bool wide = c > MOE_MATVEC_MAX_TOKENS;
+  const int nex = block_exclusive_scan(c > 0 && !wide ? 1 : 0, S);
+  const int n_narrow = S.total;
+  const int wex = block_exclusive_scan(wide ? 1 : 0, S);
+  const int n_wide = S.total;
   if (e < n_ids) {
     counts[e] = c;
     offsets[e] = excl;
     S.offs[e] = excl;
-    S.arank[e] = aex;
+    S.arank[e] = wide ? n_ids - wex : 1 + nex;  // the expert's record
     if (c > 0) {
-      work[1 + aex].e = e;
-      work[1 + aex].p0 = excl;
-      work[1 + aex].p1 = excl + c;
+      WorkRec &r = work[S.arank[e]];
+      r.e = e;
+      r.p0 = excl;
+      r.p1 = excl + c;
     }
   }
   if (e == 0) {
     offsets[n_ids] = n_total;
-    work[0] = WorkRec{n_active, n_total, 0, 0};
+    work[0] = WorkRec{n_narrow, n_total, n_wide, 0};
   }
   __syncthreads();
   if (e < n_ids)
@@ -302,7 +306,7 @@ __device__ void group_block(const int32_t *ids, int n, int n_ids, int32_t *__res
       int pos = S.hist[wave][my] + rank;
       sorted_slot[pos] = s;
       slot_pos[s] = pos;
-      if (pos == S.offs[my]) work[1 + S.arank[my]].slot0 = s;
+      if (pos == S.offs[my]) work[S.arank[my]].slot0 = s;
     }
     __builtin_amdgcn_wave_barrier();
     if (my >= 0 && rank == 0) S.hist[wave][my] += tot;
@@ -337,18 +341,24 @@ __device__ void group_tiny(const int32_t *ids_l, int n, int n_ids, int32_t *__re
       same += o == my ? 1 : 0;
       first &= (o == my && j < lane) ? 0 : 1;
     }
+    const bool wide = same > MOE_MATVEC_MAX_TOKENS;
     const uint64_t firsts = __ballot(lane < n && first);
-    int distinct_below = 0;
+    const uint64_t wides = __ballot(lane < n && first && wide);
+    int below = 0;  // distinct experts of the same list with a lower id
     for (int j = 0; j < n; j++)
-      distinct_below += ((firsts >> j) & 1u) && __builtin_amdgcn_readlane(my, j) < my ? 1 : 0;
+      below += ((firsts >> j) & 1u) && ((wides >> j) & 1u) == (uint64_t)wide &&
+                       __builtin_amdgcn_readlane(my, j) < my
+                   ? 1
+                   : 0;
     if (lane < n) {
       sorted_slot[rank] = lane;
       slot_pos[lane] = rank;
-      if (first) work[1 + distinct_below] = WorkRec{my, rank, rank + same, lane};
+      if (first) work[wide ? n_ids - below : 1 + below] = WorkRec{my, rank, rank + same, lane};
     }
     if (lane == 0) {
       offsets[n_ids] = n;
-      work[0] = WorkRec{(int)__popcll(firsts), n, 0, 0};
+      const int n_wide = (int)__popcll(wides);
+      work[0] = WorkRec{(int)__popcll(firsts) - n_wide, n, n_wide, 0};
     }
   }
   for (int e = threadIdx.x; e < n_ids; e += blockDim.x) {

@@ -1,0 +1,132 @@
+// Device helpers shared by the mat-vec and MFMA kernels: streaming loads, the LDS
+// grid tables every workgroup builds from the compact rows, SiLU, and the work list.
+#pragma once
+#include "decode.hpp"
+
+namespace moe {
+
+// ----------------------------------------------------------------------------- loads
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Streaming loads of the code streams (each byte is read once per launch).
+__device__ __forceinline__ uint4 load_stream16(const uint8_t *p) {
+  const u32x4 v = __builtin_nontemporal_load((const u32x4 *)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 load_stream8(const uint8_t *p) {
+  const u32x2 v = __builtin_nontemporal_load((const u32x2 *)p);
+  return make_uint2(v.x, v.y);
+}
+
+// ----------------------------------------------------------------------------- LDS tables
+// fp16 grid rows (8 values, 16 bytes per row) and the IQ2 sign-mask rows: entry s (the
+// 7 explicit sign bits) holds, per pair of weights, 0x8000 in each half whose weight is
+// negative, the 8th sign being the parity of the 7.
+struct TableLayout {
+  int iq2h, iq2m, iq1h, bytes;  // byte offsets in dynamic LDS
+};
+
+__host__ __device__ inline TableLayout table_layout(int formats) {
+  TableLayout t{0, 0, 0, 0};
+  if (formats & MOE_Q_IQ2XS_LIKE) {
+    t.iq2h = t.bytes;
+    t.bytes += kIq2Rows * 16;
+    t.iq2m = t.bytes;
+    t.bytes += 128 * 16;
+  }
+  if (formats & MOE_Q_IQ1M_LIKE) {
+    t.iq1h = t.bytes;
+    t.bytes += kIq1Rows * 16;
+  }
+  return t;
+}
+
+__device__ __forceinline__ uint32_t f16_bits(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
+
+__device__ __forceinline__ uint4 expand_row_f16(uint32_t c, uint32_t h0, uint32_t h1, uint32_t h2) {
+  uint32_t h[8];
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    const uint32_t s = (c >> (2 * j)) & 3u;
+    h[j] = s == 0 ? h0 : (s == 1 ? h1 : h2);
+  }
+  return make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+}
+
+// Builds the tables of the formats present from the compact rows (1 KB / 4 KB reads),
+// in two steps: tables_load issues the global loads (call it before the loads that wait
+// on HBM, so the table build does not queue behind them), tables_store expands into LDS
+// and synchronizes the workgroup.  Thread t expands rows t, t + blockDim, ...
+constexpr int kTableRowsPerThread = kIq1Rows / 256;  // for workgroups of >= 256 threads
+
+struct TableRegs {
+  uint32_t c2[kIq2Rows / 256];
+  uint32_t c1[kTableRowsPerThread];
+};
+
+__device__ __forceinline__ TableRegs tables_load(const uint8_t *grids, int formats) {
+  TableRegs tr;
+  const uint16_t *c2 = (const uint16_t *)(grids + kGridIq2CompactOff);
+  const uint16_t *c1 = (const uint16_t *)(grids + kGridIq1CompactOff);
+#pragma unroll
+  for (int i = 0; i < kIq2Rows / 256; i++) {
+    const int r = threadIdx.x + i * blockDim.x;
+    tr.c2[i] = (formats & MOE_Q_IQ2XS_LIKE) && r < kIq2Rows ? c2[r] : 0u;
+  }
+#pragma unroll
+  for (int i = 0; i < kTableRowsPerThread; i++) {
+    const int r = threadIdx.x + i * blockDim.x;
+    tr.c1[i] = (formats & MOE_Q_IQ1M_LIKE) && r < kIq1Rows ? c1[r] : 0u;
+  }
+  return tr;
+}
+
+__device__ __forceinline__ void tables_store(const TableRegs &tr, int formats, const TableLayout &TL, uint8_t *lds) {
+  if (formats & MOE_Q_IQ2XS_LIKE) {
+    const uint32_t h0 = f16_bits((float)kIq2SymVal[0]), h1 = f16_bits((float)kIq2SymVal[1]),
+                   h2 = f16_bits((float)kIq2SymVal[2]);
+    uint4 *rows = (uint4 *)(lds + TL.iq2h);
+#pragma unroll
+    for (int i = 0; i < kIq2Rows / 256; i++) {
+      const int r = threadIdx.x + i * blockDim.x;
+      if (r < kIq2Rows) rows[r] = expand_row_f16(tr.c2[i], h0, h1, h2);
+    }
+    uint4 *masks = (uint4 *)(lds + TL.iq2m);
+    for (int s = threadIdx.x; s < 128; s += blockDim.x) {
+      const uint32_t S = (uint32_t)s | ((__builtin_popcount(s) & 1u) << 7);
+      uint32_t m[4];
+#pragma unroll
+      for (int p = 0; p < 4; p++) m[p] = (((S >> (2 * p)) & 1u) << 15) | (((S >> (2 * p + 1)) & 1u) << 31);
+      masks[s] = make_uint4(m[0], m[1], m[2], m[3]);
+    }
+  }
+  if (formats & MOE_Q_IQ1M_LIKE) {
+    const uint32_t h0 = f16_bits((float)kIq1SymVal[0]), h1 = f16_bits((float)kIq1SymVal[1]),
+                   h2 = f16_bits((float)kIq1SymVal[2]);
+    uint4 *rows = (uint4 *)(lds + TL.iq1h);
+#pragma unroll
+    for (int i = 0; i < kTableRowsPerThread; i++) {
+      const int r = threadIdx.x + i * blockDim.x;
+      if (r < kIq1Rows) rows[r] = expand_row_f16(tr.c1[i], h0, h1, h2);
+    }
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ void build_tables(const uint8_t *grids, int formats, const TableLayout &TL, uint8_t *lds) {
+  const TableRegs tr = tables_load(grids, formats);
+  tables_store(tr, formats, TL, lds);
+}
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+
+__host__ __device__ inline int layer_formats(const LayerArgs &L) { return L.formats; }
+
+// i must be wave-uniform.
+__device__ __forceinline__ WorkRec load_work(const WorkRec *w, int i) {
+  return sload(w + i);
+}
+
+}  // namespace moe

@@ -58,10 +58,15 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 #define MOE_MAX_BANKS 4
 #define MOE_MAX_K 16        /* routed experts per token */
 #define MOE_MAX_IDS 1024    /* E + has_shared */
+/* Experts with at most this many tokens in a call run on the mat-vec kernels (each
+ * weight decoded once per token); experts with more run on the matrix-core grouped
+ * GEMM (each weight decoded once per block of up to 32 tokens).  The work list written
+ * by moe_route_group keeps the two sets apart. */
+#define MOE_MATVEC_MAX_TOKENS 2
 
 typedef enum {
   MOE_OK = 0,
@@ -137,10 +142,12 @@ size_t moe_workspace_bytes(int32_t T, int32_t kprime, int32_t hidden, int32_t in
  * Outputs (device): d_ids, d_w [T][kprime]; d_counts [E + add_shared]; d_offsets
  * [E + add_shared + 1] (exclusive scan of counts); d_sorted_slot [T*kprime]: slots
  * s = t*kprime + j ordered by (expert id, s); d_slot_pos: its inverse; d_work
- * [4 * (E + add_shared + 1)]: the work list of the FFN calls, 4 ints per record:
- * record 0 = (number of experts with a nonzero count, T*kprime, 0, 0); record 1+a for
- * the a-th such expert in ascending id = (expert id, offsets[e], offsets[e+1],
- * d_sorted_slot[offsets[e]]).
+ * [4 * (E + add_shared + 1)]: the work list of the FFN calls, 4 ints per record.
+ * An expert's record is (expert id, offsets[e], offsets[e+1], d_sorted_slot[offsets[e]]).
+ * With n1 = the number of experts with 1..MOE_MATVEC_MAX_TOKENS slots and n2 = the
+ * number with more: record 0 = (n1, T*kprime, n2, 0); records 1..n1 hold the first
+ * set in ascending id; records E+add_shared-j, j = 0..n2-1, hold the second set in
+ * ascending id (record E+add_shared has the lowest id).
  * Limits: 1 <= T <= 65536, 1 <= k <= min(E, MOE_MAX_K), E + add_shared <= MOE_MAX_IDS. */
 moe_status moe_route_group(const float *d_logits, int32_t T, int32_t E, int32_t k, int32_t add_shared,
                            int32_t *d_ids, float *d_w, int32_t *d_counts, int32_t *d_offsets,
@@ -162,13 +169,16 @@ moe_status moe_expert_ffn_q(const moe_layer *layer, const float *d_x, int32_t T,
 
 /* Gate and up with the SiLU epilogue ("Red Metal dev8", step 4, first half): for every
  * sorted position p as above, d_h[p] = SiLU(Wg_e x_t) * (Wu_e x_t), fp32
- * [T*kprime][inter].  One kernel: each weight row is decoded in registers and applied
- * to every token of its expert. */
+ * [T*kprime][inter].  Weights are decoded in registers: experts with at most
+ * MOE_MATVEC_MAX_TOKENS tokens on the mat-vec kernel, the others on the matrix cores
+ * (fp16 weights, exact, times activations split into two fp16 halves, fp32 sums;
+ * activations must lie within the fp16 range, |x| < 65504). */
 moe_status moe_expert_gateup_q(const moe_layer *layer, const float *d_x, int32_t T, int32_t kprime,
                                const int32_t *d_sorted_slot, const int32_t *d_work, float *d_h, hipStream_t stream);
 
 /* Down projection ("Red Metal dev8", step 4, second half): d_y[p] = Wd_e d_h[p], fp32
- * [T*kprime][hidden] in sorted order. */
+ * [T*kprime][hidden] in sorted order; experts split between the mat-vec kernel and the
+ * matrix cores as in moe_expert_gateup_q (|h| < 65504 for the latter). */
 moe_status moe_expert_down_q(const moe_layer *layer, const float *d_h, int32_t T, int32_t kprime,
                              const int32_t *d_work, float *d_y, hipStream_t stream);
 

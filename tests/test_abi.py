@@ -34,8 +34,18 @@ def test_exports_every_declared_function():
     assert set(moe.EXPORTS) == names
 
 
+def test_binding_constants_match_header():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    defs = dict(re.findall(r"#define (MOE_[A-Z_]+) (\d+)", src))
+    assert int(defs["MOE_ABI_VERSION"]) == moe.abi_version()
+    assert int(defs["MOE_MAX_BANKS"]) == moe.MAX_BANKS
+    assert int(defs["MOE_MAX_K"]) == moe.MAX_K
+    assert int(defs["MOE_MAX_IDS"]) == moe.MAX_IDS
+    assert int(defs["MOE_MATVEC_MAX_TOKENS"]) == moe.MATVEC_MAX_TOKENS
+
+
 def test_version_strings_sizes():
-    assert moe.abi_version() == 1
+    assert moe.abi_version() == 2
     for st in moe.STATUS:
         assert lib.moe_status_string(st)
     assert moe.grids_bytes() >= 512 * 8 + 2048 * 8

@@ -116,12 +116,21 @@ def test_route_group_bit_exact(T, E, k, shared, zipf):
 
 
 def check_work(work, counts, offsets, ss):
-    """Work records: (n_active, n, 0, 0), then (e, offsets[e], offsets[e+1], first slot)."""
+    """Work list: record 0 = (n1, slots, n2, 0); experts with 1..MATVEC_MAX_TOKENS slots
+    in records 1..n1, the others from the last record backwards, each list in ascending
+    id; a record is (e, offsets[e], offsets[e+1], first slot)."""
+    n_ids = len(counts)
     act = np.flatnonzero(counts)
+    narrow = act[counts[act] <= moe.MATVEC_MAX_TOKENS]
+    wide = act[counts[act] > moe.MATVEC_MAX_TOKENS]
     rec = work.reshape(-1, 4)
-    np.testing.assert_array_equal(rec[0], [len(act), offsets[-1], 0, 0])
-    want = np.stack([act, offsets[act], offsets[act + 1], ss[offsets[act]]], axis=1)
-    np.testing.assert_array_equal(rec[1:1 + len(act)], want)
+    assert len(rec) == n_ids + 1
+    np.testing.assert_array_equal(rec[0], [len(narrow), offsets[-1], len(wide), 0])
+
+    def want(a):
+        return np.stack([a, offsets[a], offsets[a + 1], ss[offsets[a]]], axis=1).reshape(-1, 4)
+    np.testing.assert_array_equal(rec[1:1 + len(narrow)], want(narrow))
+    np.testing.assert_array_equal(rec[n_ids - np.arange(len(wide))], want(wide))
 
 
 def test_route_ties_and_explicit_mode():
@@ -156,6 +165,11 @@ LAYER_CASES = {
     "small_mixed_ragged": ([(IQ2, 12), (IQ1, 20)], 512, 256, 32, 1, 19, 6, 0.0),
     "small_mixed_many_tokens": ([(IQ1, 8), (IQ2, 8)], 256, 512, 16, 0, 96, 5, 0.0),
     "mixed_h2048_t24_zipf": ([(IQ2, 24), (IQ1, 40)], 2048, 512, 64, 1, 24, 8, 1.0),
+    # many tokens per expert: the matrix-core path, one and two passes of 32 columns
+    "dense_iq2_t64": ([(IQ2, 16)], 2048, 512, 16, 0, 64, 4, 0.0),
+    "dense_iq1_t40_shared": ([(IQ1, 8)], 2048, 512, 8, 1, 40, 3, 0.0),
+    "mixed_t128_zipf": ([(IQ2, 32), (IQ1, 32)], 2048, 512, 64, 0, 128, 10, 1.1),
+    "mixed_h512_i1024_t48": ([(IQ1, 6), (IQ2, 6)], 512, 1024, 12, 1, 48, 2, 0.0),
 }
 
 
@@ -191,9 +205,10 @@ def test_layer_matches_oracle(layers, ogrids, name):
 
 
 @pytest.mark.parametrize("name", list(LAYER_CASES))
-def test_decode_path_matches_split_path(layers, name):
-    """gate/up + fused down-accumulate == ffn_q + accumulate, bit for bit; and
-    ffn_q == gate/up followed by down."""
+def test_decode_path_matches_split_path(layers, ogrids, name):
+    """gate/up + fused down-accumulate against the oracle; bit for bit equal to ffn_q +
+    accumulate when every expert takes the mat-vec path (the fused down is a mat-vec);
+    and ffn_q == gate/up followed by down."""
     banks, H, I, E, shared, T, k, zipf = LAYER_CASES[name]
     log(f"decode path {name}: T={T}")
     sl, tab, dl = layers(name)
@@ -202,7 +217,11 @@ def test_decode_path_matches_split_path(layers, name):
     acc0 = synth.activations(T, H, tag=f"D/{name}/acc")
     a = run_layer(dl, x, k, shared, logits=lg, acc=acc0)
     b = run_layer(dl, x, k, shared, logits=lg, acc=acc0, decode=True)
-    assert np.array_equal(a["acc"].view(np.uint32), b["acc"].view(np.uint32))
+    if a["counts"].max() <= moe.MATVEC_MAX_TOKENS:
+        assert np.array_equal(a["acc"].view(np.uint32), b["acc"].view(np.uint32))
+    else:
+        ref = O.moe_layer(tab, ogrids, x, k, shared, logits=lg, acc=acc0)
+        assert_rows_close(b["acc"] - acc0, ref["acc"] - acc0, f"{name} fused acc - acc0", rel=3e-5)
     r = Run(T, E, k, shared, H, I)
     r.route(dev(lg))
     h = torch.zeros((T * r.kp, I), dtype=torch.float32, device="cuda")
@@ -212,6 +231,33 @@ def test_decode_path_matches_split_path(layers, name):
     r.ffn(dl, dev(x))
     torch.cuda.synchronize()
     assert torch.equal(r.y, y2)
+
+
+@pytest.mark.parametrize("zipf", [0.0, 1.1])
+def test_prefill_field_shape_sampled(grids, ogrids, zipf):
+    """The batched field-shape layer at full size: 256 tokens, experts 0-255 IQ2_XS-like
+    and 256-511 IQ1_M-like, top-10 (uniform and Zipf(1.1) logits).  Routing of every
+    token is checked bit for bit; outputs of sampled tokens against the oracle."""
+    T, E, k, H, I = 256, 512, 10, 2048, 512
+    log(f"prefill field shape T={T} zipf={zipf}")
+    sl = synth.make_layer([(IQ2, 256), (IQ1, 256)], hidden=H, inter=I, n_experts=E, has_shared=0, tag="L/prefill")
+    dl = device_layer(sl, grids)
+    tab = O.ExpertTable(sl)
+    x = synth.activations(T, H, tag=f"P/{zipf}/x")
+    lg = synth.logits(T, E, tag=f"P/{zipf}/l", zipf_alpha=zipf)
+    g = run_layer(dl, x, k, False, logits=lg)
+    ids, _ = O.route(lg, k, False)
+    np.testing.assert_array_equal(g["ids"], ids)
+    counts = g["counts"]
+    log(f"  experts on matrix cores: {(counts > moe.MATVEC_MAX_TOKENS).sum()}, mat-vec: "
+        f"{((counts > 0) & (counts <= moe.MATVEC_MAX_TOKENS)).sum()}, max tokens {counts.max()}")
+    # sample: the tokens of the busiest expert's first and last pass, plus spread tokens
+    busiest = int(np.argmax(counts))
+    on_busiest = np.flatnonzero((ids == busiest).any(axis=1))
+    sample = sorted(set([int(on_busiest[0]), int(on_busiest[-1]), 0, 97, 200, T - 1]))
+    for t in sample:
+        ref = O.moe_layer(tab, ogrids, x[t:t + 1], k, False, logits=lg[t:t + 1])
+        assert_rows_close(g["acc"][t], ref["acc"][0], f"prefill token {t}")
 
 
 def test_permutation_invariance_and_determinism(layers):
