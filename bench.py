@@ -8,7 +8,11 @@ and the weighted accumulation.  Default workload: the field-shape decode layer
 1 token, top-10).  Inputs are resident in HBM before timing starts.  To keep the
 256 MB last-level cache from serving the weights, each step reads a different copy of
 the layer (--rotate copies, distinct device buffers with identical bytes) and a fresh
-token (distinct seeded activations and logits per step).
+batch (distinct seeded activations and logits per step).
+
+Decode workloads run route -> gate/up -> down fused with the accumulation; batched
+workloads run route -> gate/up -> down -> accumulate, the experts with many tokens on
+the matrix cores.
 
 Prints one JSON line.  Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -24,25 +28,27 @@ import time
 import numpy as np
 
 WORKLOADS = {
-    # name: (bank list, T, k, shared, zipf, description)
-    "decode_iq2": ([(1, 512)], 1, 10, 1, 0.0,
+    # name: (bank list, T, k, shared, zipf, path, description)
+    "decode_iq2": ([(1, 512)], 1, 10, 1, 0.0, "decode",
                    "decode layer, IQ2_XS-like experts, hidden 2048, 512 experts + 1 shared, inter 512, 1 token, top-10"),
-    "decode_iq1_t8": ([(2, 512)], 8, 10, 1, 0.0,
+    "decode_iq1_t8": ([(2, 512)], 8, 10, 1, 0.0, "decode",
                       "decode layer, IQ1_M-like experts, hidden 2048, 512 experts + 1 shared, inter 512, 8 tokens, top-10"),
-    "prefill_mixed_t256": ([(1, 256), (2, 256)], 256, 10, 0, 0.0,
+    "prefill_mixed_t256": ([(1, 256), (2, 256)], 256, 10, 0, 0.0, "prefill",
                            "prefill layer, experts 0-255 IQ2_XS-like and 256-511 IQ1_M-like, hidden 2048, inter 512, "
                            "256 tokens, top-10"),
-    "prefill_mixed_t256_zipf": ([(1, 256), (2, 256)], 256, 10, 0, 1.1,
+    "prefill_mixed_t256_zipf": ([(1, 256), (2, 256)], 256, 10, 0, 1.1, "prefill",
                                 "as prefill_mixed_t256 with Zipf(1.1)-skewed router logits"),
 }
 METRIC = "tokens/sec per routed MoE layer + achieved HBM GB/s (% of peak) at top-10/512"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0  # dense fp16
+H, I, E = 2048, 512, 512
 ROOT = os.path.dirname(os.path.abspath(__file__))
 # Sources that define the mat-vec kernels; the counter summary below records their digest.
 KERNEL_SOURCES = ("codebook_quantized_routed_amd/csrc/common.hpp", "codebook_quantized_routed_amd/csrc/decode.hpp",
+                  "codebook_quantized_routed_amd/csrc/matvec_common.hpp",
                   "codebook_quantized_routed_amd/csrc/k_gemv.hip")
 TRAFFIC_FILES = {"decode_iq2": "profiles/hbm_traffic_decode_iq2_t1.txt"}
-HBM_PEAK_GBS = 8000.0
-H, I, E = 2048, 512, 512
 
 
 def log(msg):
@@ -100,7 +106,7 @@ def main():
     import codebook_quantized_routed_amd as moe
     import synth
 
-    banks, T, k, shared, zipf, desc = WORKLOADS[args.workload]
+    banks, T, k, shared, zipf, path, desc = WORKLOADS[args.workload]
     kp = k + shared
     n_ids = E + shared
     dev = torch.device("cuda:0")
@@ -128,84 +134,81 @@ def main():
     log(f"inputs ready in {time.time() - t0:.1f}s: {args.rotate} x {layers[0].bytes / 1e6:.1f} MB layers")
 
     i32 = dict(dtype=torch.int32, device=dev)
-    ids = torch.zeros((T, kp), **i32)
-    w = torch.zeros((T, kp), dtype=torch.float32, device=dev)
-    counts = torch.zeros(n_ids, **i32)
-    offsets = torch.zeros(n_ids + 1, **i32)
-    sorted_slot = torch.zeros(T * kp, **i32)
-    slot_pos = torch.zeros(T * kp, **i32)
-    work = torch.zeros(moe.work_ints(n_ids), **i32)
-    y = torch.zeros((T * kp, H), dtype=torch.float32, device=dev)
-    ws = torch.zeros(moe.workspace_bytes(T, kp, H, I) // 4, dtype=torch.float32, device=dev)
+
+    def buffers():
+        return dict(ids=torch.zeros((T, kp), **i32), w=torch.zeros((T, kp), dtype=torch.float32, device=dev),
+                    counts=torch.zeros(n_ids, **i32), offsets=torch.zeros(n_ids + 1, **i32),
+                    ss=torch.zeros(T * kp, **i32), sp=torch.zeros(T * kp, **i32),
+                    work=torch.zeros(moe.work_ints(T, kp, n_ids), **i32),
+                    h=torch.zeros((T * kp, I), dtype=torch.float32, device=dev),
+                    y=torch.zeros((T * kp, H), dtype=torch.float32, device=dev) if path == "prefill" else None)
+
     acc = torch.zeros((n_in, T, H), dtype=torch.float32, device=dev)
 
-    h = torch.zeros((T * kp, I), dtype=torch.float32, device=dev)
+    # the steps of the path, each a function of (step index, buffers)
+    def k_route(i, b):
+        moe.route_group(lgs[i], T, E, k, shared, b["ids"], b["w"], b["counts"], b["offsets"], b["ss"], b["sp"],
+                        b["work"])
 
-    def step(i, ev=None):
-        """route + group, gate/up + SiLU, down + weighted accumulation."""
-        L = layers[i % len(layers)]
-        moe.route_group(lgs[i], T, E, k, shared, ids, w, counts, offsets, sorted_slot, slot_pos, work)
-        if ev is not None:
-            ev[0].record()
-        moe.expert_gateup_q(L.desc, xs[i], T, kp, sorted_slot, work, h)
-        if ev is not None:
-            ev[1].record()
-        moe.expert_down_accumulate_q(L.desc, h, T, kp, ids, w, slot_pos, acc[i])
-        if ev is not None:
-            ev[2].record()
+    def k_gateup(i, b):
+        moe.expert_gateup_q(layers[i % len(layers)].desc, xs[i], T, kp, b["ss"], b["work"], b["h"])
+
+    def k_down_acc(i, b):
+        moe.expert_down_accumulate_q(layers[i % len(layers)].desc, b["h"], T, kp, b["ids"], b["w"], b["sp"], acc[i])
+
+    def k_down(i, b):
+        moe.expert_down_q(layers[i % len(layers)].desc, b["h"], T, kp, b["work"], b["y"])
+
+    def k_accumulate(i, b):
+        moe.accumulate(b["y"], b["w"], b["ids"], b["sp"], T, kp, H, acc[i])
+
+    if path == "decode":
+        kernels = [("route_group", k_route), ("gateup", k_gateup), ("down_accumulate", k_down_acc)]
+    else:
+        kernels = [("route_group", k_route), ("gateup", k_gateup), ("down", k_down), ("accumulate", k_accumulate)]
+
+    shared_buf = buffers()
+
+    def step(i):
+        for _, fn in kernels:
+            fn(i, shared_buf)
 
     # ---- parity of the first step against the oracle (sampled tokens)
     step(0)
     torch.cuda.synchronize()
     parity = check_parity(layer, c2, c1, xs[0].cpu().numpy(), lgs[0].cpu().numpy(), k, shared,
-                          acc[0].cpu().numpy(), ids.cpu().numpy())
+                          acc[0].cpu().numpy(), shared_buf["ids"].cpu().numpy())
     log(f"parity: {parity}")
 
-    # ---- algorithmic bytes per step: quantized bytes of the distinct experts a step touches
-    # distinct experts per step from a CPU routing of the same logits (integer-exact)
+    # ---- algorithmic bytes and useful flops per step (from a CPU routing of the same
+    # logits, integer-exact): quantized bytes of the distinct experts a step touches
     import oracle as O
     lg_host = lgs.cpu().numpy()
-    bytes_per_step, gu_bytes, dn_bytes = [], [], []
+    gu_bytes, dn_bytes, step_bytes = [], [], []
     for i in range(args.warmup, n_in):
         sel, _ = O.route(lg_host[i], k, shared)
         distinct = [int(e) for e in np.unique(sel)]
         gu = sum(2 * synth.matrix_bytes(layer.bank_of(e)[0].qtype, I, H) for e in distinct)
-        # the fused down kernel reads each selected expert's down matrix once per token
-        dn = sum(synth.matrix_bytes(layer.bank_of(int(e))[0].qtype, H, I) for e in sel.ravel())
+        dn_distinct = sum(synth.matrix_bytes(layer.bank_of(e)[0].qtype, H, I) for e in distinct)
+        # the fused decode kernel reads each selected expert's down matrix once per token
+        dn = (sum(synth.matrix_bytes(layer.bank_of(int(e))[0].qtype, H, I) for e in sel.ravel())
+              if path == "decode" else dn_distinct)
         gu_bytes.append(gu)
         dn_bytes.append(dn)
-        bytes_per_step.append(gu + dn)
-    bytes_step = float(np.mean(bytes_per_step))
+        step_bytes.append(gu + dn_distinct)
+    flops_step = 2.0 * T * kp * 3 * H * I  # useful multiply-adds of the three projections, x2
 
     # ---- per-kernel timing.  Every timed step is routed first into buffers of its own;
     # then each kernel runs once per step, back to back, queued behind a GPU sleep so the
     # host never starves the queue, between two events on the launch stream.  The same
     # launches appear in a kernel trace of this command.
     K = args.steps
-    per = []
+    per = [buffers() for _ in range(K)]
     for j in range(K):
-        b = dict(ids=torch.zeros((T, kp), **i32), w=torch.zeros((T, kp), dtype=torch.float32, device=dev),
-                 counts=torch.zeros(n_ids, **i32), offsets=torch.zeros(n_ids + 1, **i32),
-                 ss=torch.zeros(T * kp, **i32), sp=torch.zeros(T * kp, **i32),
-                 work=torch.zeros(moe.work_ints(n_ids), **i32),
-                 h=torch.zeros((T * kp, I), dtype=torch.float32, device=dev))
-        per.append(b)
-    acc_k = torch.zeros((K, T, H), dtype=torch.float32, device=dev)
-
-    def rg_k(j):
-        b = per[j]
-        moe.route_group(lgs[args.warmup + j], T, E, k, shared, b["ids"], b["w"], b["counts"], b["offsets"], b["ss"],
-                        b["sp"], b["work"])
-
-    def gu_k(j):
-        b = per[j]
-        moe.expert_gateup_q(layers[(args.warmup + j) % len(layers)].desc, xs[args.warmup + j], T, kp, b["ss"],
-                            b["work"], b["h"])
-
-    def dn_k(j):
-        b = per[j]
-        moe.expert_down_accumulate_q(layers[(args.warmup + j) % len(layers)].desc, b["h"], T, kp, b["ids"], b["w"],
-                                     b["sp"], acc_k[j])
+        k_route(args.warmup + j, per[j])
+        if path == "prefill":
+            k_gateup(args.warmup + j, per[j])
+            k_down(args.warmup + j, per[j])
 
     def back_to_back(fn):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -213,17 +216,13 @@ def main():
         torch.cuda._sleep(50_000_000)
         e0.record()
         for j in range(K):
-            fn(j)
+            fn(args.warmup + j, per[j])
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / K
 
-    for j in range(K):
-        rg_k(j)
-    back_to_back(gu_k)  # warm: code objects and first touches
-    rg_ms = back_to_back(rg_k)
-    gu_ms = back_to_back(gu_k)
-    dn_ms = back_to_back(dn_k)
+    back_to_back(k_gateup)  # warm: code objects and first touches
+    kms = {name: back_to_back(fn) for name, fn in kernels}
 
     # ---- whole-step timing
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -260,8 +259,10 @@ def main():
     ms = start.elapsed_time(end) / args.steps
     tok_s = T / (ms * 1e-3)
 
-    gu_b, dn_b = float(np.mean(gu_bytes)), float(np.mean(dn_bytes))
+    gu_b, dn_b, st_b = float(np.mean(gu_bytes)), float(np.mean(dn_bytes)), float(np.mean(step_bytes))
+    gu_ms = kms["gateup"]
     achieved = gu_b / (gu_ms * 1e-3) / 1e9
+    dn_name = "down_accumulate" if path == "decode" else "down"
     out = {
         "metric": METRIC,
         "value": round(tok_s, 1),
@@ -277,19 +278,25 @@ def main():
         "data": "synthetic",
         "config": {"workload": desc, "tokens_per_step": T, "experts": E, "shared_experts": shared, "top_k": k,
                    "hidden": H, "inter": I, "rotation_copies": args.rotate, "timing": mode},
-        "step_hbm_gbs": round(bytes_step / (ms * 1e-3) / 1e9, 1),
-        "step_hbm_frac": round(bytes_step / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "algorithmic_bytes_per_step": int(bytes_step),
-        "roofline": {"bound": "hbm", "kernel": "k_gateup (dequant gate/up mat-vec + SiLU*up)",
+        "step_hbm_gbs": round(st_b / (ms * 1e-3) / 1e9, 1),
+        "step_hbm_frac": round(st_b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "algorithmic_bytes_per_step": int(st_b),
+        "roofline": {"bound": "hbm", "kernel": "gate/up (dequant mat-vec / MFMA + SiLU*up)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(args.workload, "k_gateup_wide"),
                      "bytes_per_launch": int(gu_b), "launch_us": round(gu_ms * 1e3, 3)},
-        "down_accumulate": {"achieved_gbs": round(dn_b / (dn_ms * 1e-3) / 1e9, 1), "bytes_per_launch": int(dn_b),
-                            "launch_us": round(dn_ms * 1e3, 3)},
-        "route_group": {"launch_us": round(rg_ms * 1e3, 3)},
+        dn_name: {"achieved_gbs": round(dn_b / (kms[dn_name] * 1e-3) / 1e9, 1), "bytes_per_launch": int(dn_b),
+                  "launch_us": round(kms[dn_name] * 1e3, 3)},
+        "route_group": {"launch_us": round(kms["route_group"] * 1e3, 3)},
         "parity": parity,
     }
+    if path == "prefill":
+        ffn_ms = kms["gateup"] + kms["down"]
+        tf = flops_step / (ffn_ms * 1e-3) / 1e12
+        out["accumulate"] = {"launch_us": round(kms["accumulate"] * 1e3, 3)}
+        out["mfma"] = {"useful_tflops": round(tf, 2), "peak": MFMA_PEAK_TFLOPS, "frac": round(tf / MFMA_PEAK_TFLOPS, 4),
+                       "flops_per_step": flops_step, "over": "gate/up + down launches"}
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(layer, c2, c1, xs.cpu().numpy(), lgs.cpu().numpy(), k, shared, T,
                                            args.cpu_seconds)
@@ -323,7 +330,7 @@ def cpu_baseline(layer, c2, c1, xs, lgs, k, shared, T, budget_s):
     tab = O.ExpertTable(layer)
     t0 = time.time()
     n = 0
-    while n < 2 or time.time() - t0 < budget_s:  # cycles over the steps' inputs
+    while n < 1 or time.time() - t0 < budget_s:  # cycles over the steps' inputs
         O.moe_layer(tab, g, xs[n % len(xs)], k, shared, logits=lgs[n % len(lgs)], n_threads=cores)
         n += 1
     dt = time.time() - t0

@@ -19,12 +19,13 @@ IQ1M_LIKE = 2
 MAX_BANKS = 4
 MAX_K = 16
 MAX_IDS = 1024
-MATVEC_MAX_TOKENS = 2  # experts with more tokens run on the matrix cores (MOE_MATVEC_MAX_TOKENS)
+MATVEC_MAX_TOKENS = 1  # experts with more tokens run on the matrix cores (MOE_MATVEC_MAX_TOKENS)
+MFMA_TILE_TOKENS = 16  # tokens per matrix-core tile (MOE_MFMA_TILE_TOKENS)
 
 STATUS = {0: "MOE_OK", -1: "MOE_E_NULL", -2: "MOE_E_SHAPE", -3: "MOE_E_QTYPE", -4: "MOE_E_ALIGN",
           -5: "MOE_E_WORKSPACE", -6: "MOE_E_HIP"}
 
-EXPORTS = ["moe_abi_version", "moe_status_string", "moe_last_hip_error", "moe_last_hip_error_string", "moe_grids_bytes", "moe_grids_expand", "moe_workspace_bytes",
+EXPORTS = ["moe_abi_version", "moe_status_string", "moe_last_hip_error", "moe_last_hip_error_string", "moe_grids_bytes", "moe_grids_expand", "moe_work_ints", "moe_workspace_bytes",
            "moe_route_group", "moe_expert_ffn_q", "moe_expert_gateup_q", "moe_expert_down_q",
            "moe_expert_down_accumulate_q", "moe_accumulate", "moe_dequant_f32", "moe_rmsnorm"]
 
@@ -62,6 +63,7 @@ def _load():
         "moe_last_hip_error_string": (C.c_char_p, []),
         "moe_grids_bytes": (sz, []),
         "moe_grids_expand": (C.c_int, [P, P, P, P]),
+        "moe_work_ints": (i32, [i32, i32, i32]),
         "moe_workspace_bytes": (sz, [i32, i32, i32, i32]),
         "moe_route_group": (C.c_int, [P, i32, i32, i32, i32, P, P, P, P, P, P, P, P]),
         "moe_expert_ffn_q": (C.c_int, [P, P, i32, i32, P, P, P, P, sz, P]),
@@ -117,9 +119,9 @@ def grids_expand(compact_iq2, compact_iq1, grids, stream=None):
                                                     _stream(stream)))
 
 
-def work_ints(n_ids: int) -> int:
-    """Length (int32 elements) of the work list written by route_group."""
-    return 4 * (n_ids + 1)
+def work_ints(T: int, kprime: int, n_ids: int) -> int:
+    """Length (int32 elements) of the work list route_group writes."""
+    return lib.moe_work_ints(T, kprime, n_ids)
 
 
 def route_group(logits, T, E, k, add_shared, ids, w, counts, offsets, sorted_slot, slot_pos, work, stream=None):

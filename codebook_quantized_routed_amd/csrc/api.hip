@@ -100,6 +100,11 @@ moe_status moe_grids_expand(const uint16_t *d_compact_iq2, const uint16_t *d_com
   return from_hip(launch_grids_expand(d_compact_iq2, d_compact_iq1, (uint8_t *)d_grids, stream));
 }
 
+int32_t moe_work_ints(int32_t T, int32_t kprime, int32_t n_ids) {
+  if (T < 1 || kprime < 1 || n_ids < 1) return 0;
+  return 4 * (n_ids + 1 + max_mfma_tiles(T, kprime, n_ids));
+}
+
 size_t moe_workspace_bytes(int32_t T, int32_t kprime, int32_t hidden, int32_t inter) {
   if (T < 1 || kprime < 1 || !width_ok(hidden) || !width_ok(inter)) return 0;
   return round_up((size_t)T * kprime * inter * sizeof(float), 256);

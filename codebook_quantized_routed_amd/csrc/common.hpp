@@ -32,6 +32,18 @@ struct WorkRec {
   int e, p0, p1, slot0;
 };
 
+// Upper bounds on the experts with more than MOE_MATVEC_MAX_TOKENS slots (each has at
+// most one slot per token) and on their tiles of MOE_MFMA_TILE_TOKENS.
+__host__ __device__ inline int max_wide_experts(int T, int kprime, int n_ids) {
+  if (T <= MOE_MATVEC_MAX_TOKENS) return 0;
+  const long by_slots = (long)T * kprime / (MOE_MATVEC_MAX_TOKENS + 1);
+  return (int)(by_slots < n_ids ? by_slots : n_ids);
+}
+__host__ __device__ inline int max_mfma_tiles(int T, int kprime, int n_ids) {
+  const int w = max_wide_experts(T, kprime, n_ids);
+  return w == 0 ? 0 : w + (int)(((long)T * kprime + MOE_MFMA_TILE_TOKENS - 1) / MOE_MFMA_TILE_TOKENS);
+}
+
 // Byte sizes of the three streams of one rows x cols matrix.
 __host__ __device__ inline size_t stream0_bytes(int qt, int rows, int cols) {
   return qt == MOE_Q_IQ2XS_LIKE ? (size_t)rows * (cols / 8) * 2 : (size_t)rows * (cols / 8);

@@ -220,6 +220,7 @@ __global__ void __launch_bounds__(256) k_gateup(LayerArgs L, const float *__rest
   const int a0 = min(pass / ppe, n_ids - 1);
   const WorkRec rec0 = load_work(work, 1 + a0);
   const int total = sload(&work[0].e) * ppe;
+  if ((int)blockIdx.x * 4 >= total) return;  // no pass for this workgroup (uniform)
   GatePass P;
   bool have = pass < total;
   if (have) {
@@ -405,6 +406,7 @@ __global__ void __launch_bounds__(256) k_gateup_wide(LayerArgs L, const float *_
   const int a0 = min(item / ipe, n_ids - 1);  // within the n_ids + 1 records before the count is known
   const WorkRec rec0 = load_work(work, 1 + a0);
   const int total = sload(&work[0].e) * ipe;
+  if ((int)blockIdx.x * 4 >= total) return;  // no item for this workgroup (uniform)
   WideItem It;
   X32 X;
   int cur_tok = -1;
@@ -462,6 +464,7 @@ __global__ void __launch_bounds__(256) k_down(LayerArgs L, const float *__restri
   const TableLayout TL = table_layout(formats);
   const int ppe = L.hidden / RPP;
   const int total = sload(&work[0].e) * ppe;
+  if ((int)blockIdx.x * 4 >= total) return;  // no pass for this workgroup (uniform)
   build_tables(L.grids, formats, TL, lds);
   for (int pass = blockIdx.x * 4 + wave; pass < total; pass += gridDim.x * 4) {
     const int a = pass / ppe, rp = pass - a * ppe;

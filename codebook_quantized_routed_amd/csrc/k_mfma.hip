@@ -28,45 +28,52 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-constexpr int kMfPass = 32;              // token columns per pass (two 16-column tiles)
+constexpr int kMfPass = 16;              // token columns per pass (one 16-column tile)
+static_assert(kMfPass == MOE_MFMA_TILE_TOKENS, "a tile of the work list is one pass");
 constexpr int kMfTiles = 4;              // 16-row tiles per wave
 constexpr int kXRow = 256 + 8;           // halves per staged column (16 bytes of padding)
-constexpr int kXHalves = kMfPass * kXRow;  // one of hi / lo
+constexpr int kXHalves = kMfPass * kXRow;  // one of hi / lo, one buffer
 
+// LDS: grid tables, then two buffers of staged activations (hi, lo), then the pass's
+// source rows.
 __host__ __device__ inline size_t mfma_lds_bytes(int formats) {
-  return table_layout(formats).bytes + 2 * kXHalves * sizeof(_Float16) + kMfPass * sizeof(int);
+  return table_layout(formats).bytes + 4 * kXHalves * sizeof(_Float16) + kMfPass * sizeof(int);
 }
 
 // The lane's codes of one tile row for one super-block.  IQ2: c = 8 codes (u16), s = the
-// scale word.  IQ1: c.xy = 8 index bytes, c.z = 8 nibbles, (s:c.w) = the sd word.
+// scale word, d = the binary16 d.  IQ1: c.xy = 8 index bytes, c.z = 8 nibbles, (s:c.w)
+// = the sd word (d in its low half).  Offsets are 32-bit from the matrix bases, so the
+// loads take a scalar base and a vector offset.
 struct TileCodes {
   uint4 c;
-  uint32_t s;
+  uint32_t s, d;
 };
 
 template <int QT>
 __device__ __forceinline__ TileCodes load_tile_codes(const QMat &m, int cols, int row, int sb, int qd) {
-  const int ng = cols >> 3, nb = cols >> 8, g0 = sb * 32 + 8 * qd;
+  const uint32_t ng = cols >> 3, nb = cols >> 8, g0 = sb * 32 + 8 * qd, blk = row * nb + sb;
   TileCodes t;
   if constexpr (QT == MOE_Q_IQ2XS_LIKE) {
-    t.c = load_stream16(m.s0 + ((size_t)row * ng + g0) * 2);
-    t.s = ((const uint32_t *)m.s1)[(size_t)row * nb + sb];
+    t.c = load_stream16(m.s0 + (uint32_t)((row * ng + g0) * 2));
+    t.s = *(const uint32_t *)(m.s1 + (uint32_t)(blk * 4));
+    t.d = *(const uint16_t *)(m.s2 + (uint32_t)(blk * 2));
   } else {
-    const uint2 ql = load_stream8(m.s0 + (size_t)row * ng + g0);
-    const uint32_t qh = __builtin_nontemporal_load((const uint32_t *)(m.s1 + (size_t)row * (ng / 2) + g0 / 2));
-    const uint2 sd = *(const uint2 *)(m.s2 + ((size_t)row * nb + sb) * 8);
+    const uint2 ql = load_stream8(m.s0 + (uint32_t)(row * ng + g0));
+    const uint32_t qh = __builtin_nontemporal_load((const uint32_t *)(m.s1 + (uint32_t)(row * (ng / 2) + g0 / 2)));
+    const uint2 sd = *(const uint2 *)(m.s2 + (uint32_t)(blk * 8));
     t.c = make_uint4(ql.x, ql.y, qh, sd.x);
     t.s = sd.y;
+    t.d = sd.x & 0xFFFFu;
   }
   return t;
 }
 
-// d / 8 of row `row` in super-block sb (the fp16 d is the low half of the IQ1 sd word).
-template <int QT>
-__device__ __forceinline__ float load_dfac(const QMat &m, int cols, int row, int sb) {
-  const int nb = cols >> 8;
-  const size_t stride = QT == MOE_Q_IQ2XS_LIKE ? 2 : 8;
-  return half_bits_to_float(*(const uint16_t *)(m.s2 + ((size_t)row * nb + sb) * stride)) * 0.125f;
+// d / 8 of the lane's four C rows 4 qd + i of a tile, taken from the lanes that hold
+// those rows' codes (lane j holds row j % 16).
+__device__ __forceinline__ void c_row_factors(const TileCodes &t, int qd, float (&df)[4]) {
+  const float mine = half_bits_to_float(t.d) * 0.125f;
+#pragma unroll
+  for (int i = 0; i < 4; i++) df[i] = __shfl(mine, 4 * qd + i, 64);
 }
 
 __device__ __forceinline__ uint32_t f16_pair(uint32_t v) {
@@ -109,114 +116,107 @@ __device__ __forceinline__ h8 decode_a(const TileCodes &t, int ks, int qd, const
   return __builtin_bit_cast(h8, v);
 }
 
-// Stages 256 columns of up to kMfPass activation rows into LDS as hi / lo fp16
-// halves: thread t takes row t / 8, floats 32 (t % 8) .. + 31.  src_row[c] < 0: zeros.
-__device__ __forceinline__ void stage_x(const float *base, int row_stride, const int *src_row, int col0,
-                                        _Float16 *xhi, _Float16 *xlo) {
-  const int c = threadIdx.x >> 3, part = threadIdx.x & 7;
+// Staging of 256 columns of the pass's kMfPass activation rows: thread t takes row
+// t / 16, floats 16 (t % 16) .. + 15.  stage_load issues the global loads (src_row[c]
+// < 0: zeros), stage_store splits each value into fp16 hi / lo halves in LDS.
+struct XRegs {
+  u32x4 v[4];
+};
+
+__device__ __forceinline__ XRegs stage_load(const float *base, int row_stride, const int *src_row, int col0) {
+  const int c = threadIdx.x >> 4, part = threadIdx.x & 15;
   const int r = src_row[c];
-  u32x4 v[8];
-  if (r >= 0) {
-    const u32x4 *p = (const u32x4 *)(base + (size_t)r * row_stride + col0 + 32 * part);
+  XRegs x;
+  const u32x4 *p = (const u32x4 *)(base + (size_t)(r < 0 ? 0 : r) * row_stride + col0 + 16 * part);
 #pragma unroll
-    for (int i = 0; i < 8; i++) v[i] = p[i];
-  } else {
+  for (int i = 0; i < 4; i++) x.v[i] = r < 0 ? u32x4{0u, 0u, 0u, 0u} : p[i];
+  return x;
+}
+
+__device__ __forceinline__ void stage_store(const XRegs &x, _Float16 *xhi, _Float16 *xlo) {
+  const int c = threadIdx.x >> 4, part = threadIdx.x & 15;
+  uint32_t hi[8], lo[8];
 #pragma unroll
-    for (int i = 0; i < 8; i++) v[i] = u32x4{0u, 0u, 0u, 0u};
-  }
-  uint32_t hi[16], lo[16];
-#pragma unroll
-  for (int i = 0; i < 16; i++) {
-    const float a = __uint_as_float(v[i >> 1][2 * (i & 1)]), b = __uint_as_float(v[i >> 1][2 * (i & 1) + 1]);
+  for (int i = 0; i < 8; i++) {
+    const float a = __uint_as_float(x.v[i >> 1][2 * (i & 1)]), b = __uint_as_float(x.v[i >> 1][2 * (i & 1) + 1]);
     const _Float16 ah = (_Float16)a, bh = (_Float16)b;
     const _Float16 al = (_Float16)(a - (float)ah), bl = (_Float16)(b - (float)bh);
     hi[i] = (uint32_t)__builtin_bit_cast(uint16_t, ah) | ((uint32_t)__builtin_bit_cast(uint16_t, bh) << 16);
     lo[i] = (uint32_t)__builtin_bit_cast(uint16_t, al) | ((uint32_t)__builtin_bit_cast(uint16_t, bl) << 16);
   }
-  u32x4 *dh = (u32x4 *)(xhi + c * kXRow + 32 * part), *dl = (u32x4 *)(xlo + c * kXRow + 32 * part);
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    dh[i] = u32x4{hi[4 * i], hi[4 * i + 1], hi[4 * i + 2], hi[4 * i + 3]};
-    dl[i] = u32x4{lo[4 * i], lo[4 * i + 1], lo[4 * i + 2], lo[4 * i + 3]};
-  }
+  u32x4 *dh = (u32x4 *)(xhi + c * kXRow + 16 * part), *dl = (u32x4 *)(xlo + c * kXRow + 16 * part);
+  dh[0] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+  dh[1] = u32x4{hi[4], hi[5], hi[6], hi[7]};
+  dl[0] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+  dl[1] = u32x4{lo[4], lo[5], lo[6], lo[7]};
 }
 
-// One pass: the wave's kMfTiles row tiles times up to kMfPass staged columns, over the
-// K range [0, cols) in super-blocks.  Ct[t][n]: the fp32 result of tile t, column tile
-// n.  The caller has built the grid tables.
+// One pass: the wave's kMfTiles row tiles times the pass's (up to) 16 staged columns,
+// over the K range [0, cols) in super-blocks.  Super-block sb + 1's activations, codes
+// and scales are loaded while sb is computed; the staged activations alternate
+// between two LDS buffers, with one workgroup barrier per super-block.  Ct[t]: the
+// fp32 result of tile t.  The caller has built the grid tables and set src_row.
 template <int QT>
 __device__ __forceinline__ void mfma_pass(const QMat (&mats)[kMfTiles], const int (&trow)[kMfTiles], int cols,
-                                          const float *xbase, int x_stride, const int *src_row, int n_cols,
-                                          uint8_t *lds, const TableLayout &TL, _Float16 *xhi, _Float16 *xlo,
-                                          f4 (&Ct)[kMfTiles][2]) {
+                                          const float *xbase, int x_stride, const int *src_row, const uint8_t *lds,
+                                          const TableLayout &TL, _Float16 *xbuf, f4 (&Ct)[kMfTiles]) {
   const int lane = threadIdx.x & 63, qd = lane >> 4, lr = lane & 15;
   const int nsb = cols >> 8;
-  const bool two = n_cols > 16;
 #pragma unroll
-  for (int t = 0; t < kMfTiles; t++) Ct[t][0] = Ct[t][1] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int t = 0; t < kMfTiles; t++) Ct[t] = f4{0.0f, 0.0f, 0.0f, 0.0f};
   TileCodes tc[kMfTiles];
 #pragma unroll
   for (int t = 0; t < kMfTiles; t++) tc[t] = load_tile_codes<QT>(mats[t], cols, trow[t] + lr, 0, qd);
+  stage_store(stage_load(xbase, x_stride, src_row, 0), xbuf, xbuf + kXHalves);
+  __syncthreads();
   for (int sb = 0; sb < nsb; sb++) {
-    float df[kMfTiles][4];
-#pragma unroll
-    for (int t = 0; t < kMfTiles; t++)
-#pragma unroll
-      for (int i = 0; i < 4; i++) df[t][i] = load_dfac<QT>(mats[t], cols, trow[t] + 4 * qd + i, sb);
-    stage_x(xbase, x_stride, src_row, sb * 256, xhi, xlo);
-    __syncthreads();
+    const _Float16 *xhi = xbuf + (sb & 1) * 2 * kXHalves, *xlo = xhi + kXHalves;
+    const bool more = sb + 1 < nsb;
+    XRegs xn;
     TileCodes nx[kMfTiles];
-    if (sb + 1 < nsb) {
+    if (more) {
+      xn = stage_load(xbase, x_stride, src_row, (sb + 1) * 256);
 #pragma unroll
       for (int t = 0; t < kMfTiles; t++) nx[t] = load_tile_codes<QT>(mats[t], cols, trow[t] + lr, sb + 1, qd);
     }
-    f4 Cs[kMfTiles][2];
+    f4 Cs[kMfTiles];
 #pragma unroll
-    for (int t = 0; t < kMfTiles; t++) Cs[t][0] = Cs[t][1] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int t = 0; t < kMfTiles; t++) Cs[t] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int ks = 0; ks < 8; ks++) {
-      h8 A[kMfTiles];
+      const int koff = lr * kXRow + (8 * qd + ks) * 8;
+      const h8 bh = *(const h8 *)(xhi + koff), bl = *(const h8 *)(xlo + koff);
 #pragma unroll
-      for (int t = 0; t < kMfTiles; t++) A[t] = decode_a<QT>(tc[t], ks, qd, lds, TL);
-      const int koff = (8 * qd + ks) * 8;
-      {
-        const h8 bh = *(const h8 *)(xhi + lr * kXRow + koff), bl = *(const h8 *)(xlo + lr * kXRow + koff);
-#pragma unroll
-        for (int t = 0; t < kMfTiles; t++) {
-          Cs[t][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[t], bh, Cs[t][0], 0, 0, 0);
-          Cs[t][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[t], bl, Cs[t][0], 0, 0, 0);
-        }
-      }
-      if (two) {
-        const h8 bh = *(const h8 *)(xhi + (16 + lr) * kXRow + koff), bl = *(const h8 *)(xlo + (16 + lr) * kXRow + koff);
-#pragma unroll
-        for (int t = 0; t < kMfTiles; t++) {
-          Cs[t][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[t], bh, Cs[t][1], 0, 0, 0);
-          Cs[t][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[t], bl, Cs[t][1], 0, 0, 0);
-        }
+      for (int t = 0; t < kMfTiles; t++) {
+        const h8 A = decode_a<QT>(tc[t], ks, qd, lds, TL);
+        Cs[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bh, Cs[t], 0, 0, 0);
+        Cs[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bl, Cs[t], 0, 0, 0);
       }
     }
 #pragma unroll
-    for (int t = 0; t < kMfTiles; t++)
+    for (int t = 0; t < kMfTiles; t++) {
+      float df[4];
+      c_row_factors(tc[t], qd, df);
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        Ct[t][0][i] = fmaf(Cs[t][0][i], df[t][i], Ct[t][0][i]);
-        Ct[t][1][i] = fmaf(Cs[t][1][i], df[t][i], Ct[t][1][i]);
-      }
-    if (sb + 1 < nsb) {
+      for (int i = 0; i < 4; i++) Ct[t][i] = fmaf(Cs[t][i], df[i], Ct[t][i]);
+    }
+    if (more) {
+      _Float16 *nh = xbuf + ((sb + 1) & 1) * 2 * kXHalves;
+      stage_store(xn, nh, nh + kXHalves);
 #pragma unroll
       for (int t = 0; t < kMfTiles; t++) tc[t] = nx[t];
     }
-    __syncthreads();  // the staged columns are overwritten next
+    __syncthreads();
   }
 }
 
-// The i-th MFMA expert's record: they are stored from the end of the work list.
-__device__ __forceinline__ WorkRec mfma_record(const WorkRec *work, int n_ids, int a) {
-  return load_work(work, n_ids - a);
+// Tile i of the matrix-core experts: (expert, p0, p1, 0), stored after the n_ids + 1
+// records of the work list.
+__device__ __forceinline__ WorkRec mfma_tile(const WorkRec *work, int n_ids, int i) {
+  return load_work(work, n_ids + 1 + i);
 }
 
-// gate + up + SiLU * up.  Workgroup = (MFMA expert, block of 128 rows of inter); wave
+// gate + up + SiLU * up.  Workgroup = (tile, block of 128 rows of inter); wave
 // w takes gate and up rows r0 .. r0 + 31, r0 = 128 * block + 32 w.  One instance per
 // format: a workgroup whose expert has the other format returns at once.
 template <int QT>
@@ -227,13 +227,13 @@ __global__ void __launch_bounds__(256) k_gateup_mfma(LayerArgs L, const float *_
   extern __shared__ __align__(16) uint8_t lds[];
   const int H = L.hidden, I = L.inter, RB = I / 128;
   const int a = blockIdx.x / RB, rb = blockIdx.x - a * RB;
-  if (a >= sload(&work[0].p1)) return;  // record 0 = (matvec experts, slots, MFMA experts, 0)
-  const WorkRec W = mfma_record(work, n_ids, a);
+  if (a >= sload(&work[0].slot0)) return;  // record 0 = (matvec experts, slots, MFMA experts, tiles)
+  const WorkRec W = mfma_tile(work, n_ids, a);
   const BankArgs &B = bank_of(L, W.e);
   if (B.qtype != QT) return;
   const TableLayout TL = table_layout(QT);
-  _Float16 *xhi = (_Float16 *)(lds + TL.bytes), *xlo = xhi + kXHalves;
-  int *src_row = (int *)(xlo + kXHalves);
+  _Float16 *xbuf = (_Float16 *)(lds + TL.bytes);
+  int *src_row = (int *)(xbuf + 4 * kXHalves);
   build_tables(L.grids, QT, TL, lds);
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6), qd = lane >> 4, lr = lane & 15;
   const QMat Wg = expert_mat(B, W.e, kGate, I, H), Wu = expert_mat(B, W.e, kUp, I, H);
@@ -244,27 +244,23 @@ __global__ void __launch_bounds__(256) k_gateup_mfma(LayerArgs L, const float *_
     const int n = min(kMfPass, W.p1 - pp);
     if (threadIdx.x < kMfPass) src_row[threadIdx.x] = threadIdx.x < n ? sorted_slot[pp + threadIdx.x] / kprime : -1;
     __syncthreads();
-    f4 Ct[kMfTiles][2];
-    mfma_pass<QT>(mats, trow, H, x, H, src_row, n, lds, TL, xhi, xlo, Ct);
+    f4 Ct[kMfTiles];
+    mfma_pass<QT>(mats, trow, H, x, H, src_row, lds, TL, xbuf, Ct);
+    if (lr < n) {
 #pragma unroll
-    for (int nt = 0; nt < 2; nt++) {
-      const int c = 16 * nt + lr;
-      if (c < n) {
-#pragma unroll
-        for (int j = 0; j < 2; j++) {
-          float4 o;
-          o.x = silu(Ct[j][nt][0]) * Ct[2 + j][nt][0];
-          o.y = silu(Ct[j][nt][1]) * Ct[2 + j][nt][1];
-          o.z = silu(Ct[j][nt][2]) * Ct[2 + j][nt][2];
-          o.w = silu(Ct[j][nt][3]) * Ct[2 + j][nt][3];
-          *(float4 *)(h + (size_t)(pp + c) * I + r0 + 16 * j + 4 * qd) = o;
-        }
+      for (int j = 0; j < 2; j++) {
+        float4 o;
+        o.x = silu(Ct[j][0]) * Ct[2 + j][0];
+        o.y = silu(Ct[j][1]) * Ct[2 + j][1];
+        o.z = silu(Ct[j][2]) * Ct[2 + j][2];
+        o.w = silu(Ct[j][3]) * Ct[2 + j][3];
+        *(float4 *)(h + (size_t)(pp + lr) * I + r0 + 16 * j + 4 * qd) = o;
       }
     }
   }
 }
 
-// down: y[p] = Wd h[p].  Workgroup = (MFMA expert, block of 256 rows of hidden); wave w
+// down: y[p] = Wd h[p].  Workgroup = (tile, block of 256 rows of hidden); wave w
 // takes rows r0 .. r0 + 63, r0 = 256 * block + 64 w.  h rows are contiguous per expert.
 // One instance per format, as above.
 template <int QT>
@@ -274,13 +270,13 @@ __global__ void __launch_bounds__(256) k_down_mfma(LayerArgs L, const float *__r
   extern __shared__ __align__(16) uint8_t lds[];
   const int H = L.hidden, I = L.inter, RB = H / 256;
   const int a = blockIdx.x / RB, rb = blockIdx.x - a * RB;
-  if (a >= sload(&work[0].p1)) return;
-  const WorkRec W = mfma_record(work, n_ids, a);
+  if (a >= sload(&work[0].slot0)) return;
+  const WorkRec W = mfma_tile(work, n_ids, a);
   const BankArgs &B = bank_of(L, W.e);
   if (B.qtype != QT) return;
   const TableLayout TL = table_layout(QT);
-  _Float16 *xhi = (_Float16 *)(lds + TL.bytes), *xlo = xhi + kXHalves;
-  int *src_row = (int *)(xlo + kXHalves);
+  _Float16 *xbuf = (_Float16 *)(lds + TL.bytes);
+  int *src_row = (int *)(xbuf + 4 * kXHalves);
   build_tables(L.grids, QT, TL, lds);
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6), qd = lane >> 4, lr = lane & 15;
   const QMat Wd = expert_mat(B, W.e, kDown, H, I);
@@ -291,32 +287,19 @@ __global__ void __launch_bounds__(256) k_down_mfma(LayerArgs L, const float *__r
     const int n = min(kMfPass, W.p1 - pp);
     if (threadIdx.x < kMfPass) src_row[threadIdx.x] = threadIdx.x < n ? pp + (int)threadIdx.x : -1;
     __syncthreads();
-    f4 Ct[kMfTiles][2];
-    mfma_pass<QT>(mats, trow, I, h, I, src_row, n, lds, TL, xhi, xlo, Ct);
+    f4 Ct[kMfTiles];
+    mfma_pass<QT>(mats, trow, I, h, I, src_row, lds, TL, xbuf, Ct);
+    if (lr < n) {
 #pragma unroll
-    for (int nt = 0; nt < 2; nt++) {
-      const int c = 16 * nt + lr;
-      if (c < n) {
-#pragma unroll
-        for (int t = 0; t < kMfTiles; t++)
-          *(float4 *)(y + (size_t)(pp + c) * H + trow[t] + 4 * qd) =
-              make_float4(Ct[t][nt][0], Ct[t][nt][1], Ct[t][nt][2], Ct[t][nt][3]);
-      }
+      for (int t = 0; t < kMfTiles; t++)
+        *(float4 *)(y + (size_t)(pp + lr) * H + trow[t] + 4 * qd) = make_float4(Ct[t][0], Ct[t][1], Ct[t][2], Ct[t][3]);
     }
   }
 }
 
-// Upper bound on the MFMA experts of a call: each has more than MOE_MATVEC_MAX_TOKENS
-// of the T * kprime slots, and at most T (one slot per token).
-static long max_mfma_experts(int T, int kprime, int n_ids) {
-  if (T <= MOE_MATVEC_MAX_TOKENS) return 0;
-  const long by_slots = (long)T * kprime / (MOE_MATVEC_MAX_TOKENS + 1);
-  return by_slots < n_ids ? by_slots : n_ids;
-}
-
 hipError_t launch_gateup_mfma(const LayerArgs &L, const float *x, int T, int kprime, const int32_t *sorted_slot,
                               const WorkRec *work, int n_ids, float *h, hipStream_t s) {
-  const long n = max_mfma_experts(T, kprime, n_ids);
+  const long n = max_mfma_tiles(T, kprime, n_ids);
   if (n == 0) return hipSuccess;
   const dim3 grid((unsigned)(n * (L.inter / 128)));
   if (L.formats & MOE_Q_IQ2XS_LIKE) {
@@ -333,7 +316,7 @@ hipError_t launch_gateup_mfma(const LayerArgs &L, const float *x, int T, int kpr
 
 hipError_t launch_down_mfma(const LayerArgs &L, const float *h, int T, int kprime, const WorkRec *work, int n_ids,
                             float *y, hipStream_t s) {
-  const long n = max_mfma_experts(T, kprime, n_ids);
+  const long n = max_mfma_tiles(T, kprime, n_ids);
   if (n == 0) return hipSuccess;
   const dim3 grid((unsigned)(n * (L.hidden / 256)));
   if (L.formats & MOE_Q_IQ2XS_LIKE) {

@@ -262,25 +262,31 @@ __device__ void group_block(const int32_t *ids, int n, int n_ids, int32_t *__res
   const int excl = block_exclusive_scan(c, S);
   const int n_total = S.total;
   const bool wide = c > MOE_MATVEC_MAX_TOKENS;
+  const int tiles = wide ? (c + MOE_MFMA_TILE_TOKENS - 1) / MOE_MFMA_TILE_TOKENS : 0;
   const int nex = block_exclusive_scan(c > 0 && !wide ? 1 : 0, S);
   const int n_narrow = S.total;
-  const int wex = block_exclusive_scan(wide ? 1 : 0, S);
+  block_exclusive_scan(wide ? 1 : 0, S);
   const int n_wide = S.total;
+  const int tex = block_exclusive_scan(tiles, S);
+  const int n_tiles = S.total;
   if (e < n_ids) {
     counts[e] = c;
     offsets[e] = excl;
     S.offs[e] = excl;
-    S.arank[e] = wide ? n_ids - wex : 1 + nex;  // the expert's record
-    if (c > 0) {
-      WorkRec &r = work[S.arank[e]];
+    S.arank[e] = c > 0 && !wide ? 1 + nex : -1;  // the expert's record in the first set
+    if (c > 0 && !wide) {
+      WorkRec &r = work[1 + nex];
       r.e = e;
       r.p0 = excl;
       r.p1 = excl + c;
     }
+    for (int i = 0; i < tiles; i++)
+      work[n_ids + 1 + tex + i] =
+          WorkRec{e, excl + i * MOE_MFMA_TILE_TOKENS, excl + min(c, (i + 1) * MOE_MFMA_TILE_TOKENS), 0};
   }
   if (e == 0) {
     offsets[n_ids] = n_total;
-    work[0] = WorkRec{n_narrow, n_total, n_wide, 0};
+    work[0] = WorkRec{n_narrow, n_total, n_wide, n_tiles};
   }
   __syncthreads();
   if (e < n_ids)
@@ -306,7 +312,7 @@ __device__ void group_block(const int32_t *ids, int n, int n_ids, int32_t *__res
       int pos = S.hist[wave][my] + rank;
       sorted_slot[pos] = s;
       slot_pos[s] = pos;
-      if (pos == S.offs[my]) work[S.arank[my]].slot0 = s;
+      if (pos == S.offs[my] && S.arank[my] > 0) work[S.arank[my]].slot0 = s;
     }
     __builtin_amdgcn_wave_barrier();
     if (my >= 0 && rank == 0) S.hist[wave][my] += tot;
@@ -344,21 +350,33 @@ __device__ void group_tiny(const int32_t *ids_l, int n, int n_ids, int32_t *__re
     const bool wide = same > MOE_MATVEC_MAX_TOKENS;
     const uint64_t firsts = __ballot(lane < n && first);
     const uint64_t wides = __ballot(lane < n && first && wide);
-    int below = 0;  // distinct experts of the same list with a lower id
-    for (int j = 0; j < n; j++)
-      below += ((firsts >> j) & 1u) && ((wides >> j) & 1u) == (uint64_t)wide &&
-                       __builtin_amdgcn_readlane(my, j) < my
-                   ? 1
-                   : 0;
+    // first set: distinct experts below mine; tiles: the tiles of wide experts below mine
+    int below = 0, tiles_below = 0, n_tiles = 0;
+    for (int j = 0; j < n; j++) {
+      const int oj = __builtin_amdgcn_readlane(my, j), sj = __builtin_amdgcn_readlane(same, j);
+      const bool fj = (firsts >> j) & 1u, wj = (wides >> j) & 1u;
+      const int tj = (sj + MOE_MFMA_TILE_TOKENS - 1) / MOE_MFMA_TILE_TOKENS;
+      if (fj && oj < my) {
+        if (wj)
+          tiles_below += tj;
+        else
+          below++;
+      }
+      n_tiles += wj ? tj : 0;
+    }
     if (lane < n) {
       sorted_slot[rank] = lane;
       slot_pos[lane] = rank;
-      if (first) work[wide ? n_ids - below : 1 + below] = WorkRec{my, rank, rank + same, lane};
+      if (first && !wide) work[1 + below] = WorkRec{my, rank, rank + same, lane};
+      if (first && wide)
+        for (int p = 0; p < same; p += MOE_MFMA_TILE_TOKENS)
+          work[n_ids + 1 + tiles_below + p / MOE_MFMA_TILE_TOKENS] =
+              WorkRec{my, rank + p, rank + min(same, p + MOE_MFMA_TILE_TOKENS), 0};
     }
     if (lane == 0) {
       offsets[n_ids] = n;
       const int n_wide = (int)__popcll(wides);
-      work[0] = WorkRec{(int)__popcll(firsts) - n_wide, n, n_wide, 0};
+      work[0] = WorkRec{(int)__popcll(firsts) - n_wide, n, n_wide, n_tiles};
     }
   }
   for (int e = threadIdx.x; e < n_ids; e += blockDim.x) {

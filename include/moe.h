@@ -58,15 +58,16 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 #define MOE_MAX_BANKS 4
 #define MOE_MAX_K 16        /* routed experts per token */
 #define MOE_MAX_IDS 1024    /* E + has_shared */
 /* Experts with at most this many tokens in a call run on the mat-vec kernels (each
  * weight decoded once per token); experts with more run on the matrix-core grouped
- * GEMM (each weight decoded once per block of up to 32 tokens).  The work list written
- * by moe_route_group keeps the two sets apart. */
-#define MOE_MATVEC_MAX_TOKENS 2
+ * GEMM in tiles of up to MOE_MFMA_TILE_TOKENS tokens (each weight decoded once per
+ * tile).  The work list written by moe_route_group keeps the two sets apart. */
+#define MOE_MATVEC_MAX_TOKENS 1
+#define MOE_MFMA_TILE_TOKENS 16
 
 typedef enum {
   MOE_OK = 0,
@@ -128,6 +129,10 @@ size_t moe_grids_bytes(void);
 moe_status moe_grids_expand(const uint16_t *d_compact_iq2, const uint16_t *d_compact_iq1, void *d_grids,
                             hipStream_t stream);
 
+/* Ints of the work list moe_route_group writes for T tokens, kprime slots per token
+ * and n_ids = E + add_shared expert ids. */
+int32_t moe_work_ints(int32_t T, int32_t kprime, int32_t n_ids);
+
 /* Workspace needed by moe_expert_ffn_q for T tokens with kprime slots each. */
 size_t moe_workspace_bytes(int32_t T, int32_t kprime, int32_t hidden, int32_t inter);
 
@@ -142,12 +147,15 @@ size_t moe_workspace_bytes(int32_t T, int32_t kprime, int32_t hidden, int32_t in
  * Outputs (device): d_ids, d_w [T][kprime]; d_counts [E + add_shared]; d_offsets
  * [E + add_shared + 1] (exclusive scan of counts); d_sorted_slot [T*kprime]: slots
  * s = t*kprime + j ordered by (expert id, s); d_slot_pos: its inverse; d_work
- * [4 * (E + add_shared + 1)]: the work list of the FFN calls, 4 ints per record.
- * An expert's record is (expert id, offsets[e], offsets[e+1], d_sorted_slot[offsets[e]]).
- * With n1 = the number of experts with 1..MOE_MATVEC_MAX_TOKENS slots and n2 = the
- * number with more: record 0 = (n1, T*kprime, n2, 0); records 1..n1 hold the first
- * set in ascending id; records E+add_shared-j, j = 0..n2-1, hold the second set in
- * ascending id (record E+add_shared has the lowest id).
+ * [moe_work_ints(T, kprime, E + add_shared)]: the work list of the FFN calls, records
+ * of 4 ints.  With n_ids = E + add_shared:
+ *   record 0 = (n1, T*kprime, n2, nt): n1 experts with 1..MOE_MATVEC_MAX_TOKENS slots,
+ *     n2 experts with more, nt tiles;
+ *   records 1..n1: (expert id, offsets[e], offsets[e+1], d_sorted_slot[offsets[e]]) of
+ *     the first set, ascending id;
+ *   records n_ids+1 .. n_ids+nt: the tiles of the second set, (expert id, p0, p1, 0)
+ *     covering sorted positions [p0, p1) of the expert, MOE_MFMA_TILE_TOKENS at a time,
+ *     ascending (id, p0).
  * Limits: 1 <= T <= 65536, 1 <= k <= min(E, MOE_MAX_K), E + add_shared <= MOE_MAX_IDS. */
 moe_status moe_route_group(const float *d_logits, int32_t T, int32_t E, int32_t k, int32_t add_shared,
                            int32_t *d_ids, float *d_w, int32_t *d_counts, int32_t *d_offsets,

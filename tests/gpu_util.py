@@ -49,7 +49,7 @@ class Run:
         self.offsets = torch.zeros(n_ids + 1, **i32)
         self.sorted_slot = torch.zeros(T * kp, **i32)
         self.slot_pos = torch.zeros(T * kp, **i32)
-        self.work = torch.zeros(moe.work_ints(n_ids), **i32)
+        self.work = torch.zeros(moe.work_ints(T, kp, n_ids), **i32)
         self.y = torch.zeros((T * kp, H), dtype=torch.float32, device="cuda")
         nws = moe.workspace_bytes(T, kp, H, I)
         self.ws = torch.zeros(max(nws // 4, 4), dtype=torch.float32, device="cuda")

@@ -42,14 +42,20 @@ def test_binding_constants_match_header():
     assert int(defs["MOE_MAX_K"]) == moe.MAX_K
     assert int(defs["MOE_MAX_IDS"]) == moe.MAX_IDS
     assert int(defs["MOE_MATVEC_MAX_TOKENS"]) == moe.MATVEC_MAX_TOKENS
+    assert int(defs["MOE_MFMA_TILE_TOKENS"]) == moe.MFMA_TILE_TOKENS
 
 
 def test_version_strings_sizes():
-    assert moe.abi_version() == 2
+    assert moe.abi_version() == 3
     for st in moe.STATUS:
         assert lib.moe_status_string(st)
     assert moe.grids_bytes() >= 512 * 8 + 2048 * 8
     assert moe.workspace_bytes(1, 11, 2048, 512) == 11 * 512 * 4
+    # the work list: n_ids + 1 records, then room for the matrix-core tiles
+    assert moe.work_ints(1, 11, 513) == 4 * 514                       # one token: no expert above 1 slot
+    n_wide = min(513, 256 * 10 // (moe.MATVEC_MAX_TOKENS + 1))
+    assert moe.work_ints(256, 10, 512) == 4 * (513 + min(512, n_wide) + (2560 + 15) // 16)
+    assert moe.work_ints(0, 11, 513) == 0
     assert moe.workspace_bytes(0, 11, 2048, 512) == 0
     assert moe.workspace_bytes(1, 11, 2048, 300) == 0
 

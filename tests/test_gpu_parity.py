@@ -116,21 +116,22 @@ def test_route_group_bit_exact(T, E, k, shared, zipf):
 
 
 def check_work(work, counts, offsets, ss):
-    """Work list: record 0 = (n1, slots, n2, 0); experts with 1..MATVEC_MAX_TOKENS slots
-    in records 1..n1, the others from the last record backwards, each list in ascending
-    id; a record is (e, offsets[e], offsets[e+1], first slot)."""
+    """Work list: record 0 = (n1, slots, n2, tiles); the experts with 1..MATVEC_MAX_TOKENS
+    slots in records 1..n1, ascending id, as (e, offsets[e], offsets[e+1], first slot);
+    after the n_ids + 1 records, the other experts' tiles of MFMA_TILE_TOKENS positions,
+    ascending (id, start)."""
     n_ids = len(counts)
     act = np.flatnonzero(counts)
     narrow = act[counts[act] <= moe.MATVEC_MAX_TOKENS]
     wide = act[counts[act] > moe.MATVEC_MAX_TOKENS]
+    tiles = [(e, p, min(p + moe.MFMA_TILE_TOKENS, offsets[e + 1]), 0)
+             for e in wide for p in range(offsets[e], offsets[e + 1], moe.MFMA_TILE_TOKENS)]
     rec = work.reshape(-1, 4)
-    assert len(rec) == n_ids + 1
-    np.testing.assert_array_equal(rec[0], [len(narrow), offsets[-1], len(wide), 0])
-
-    def want(a):
-        return np.stack([a, offsets[a], offsets[a + 1], ss[offsets[a]]], axis=1).reshape(-1, 4)
-    np.testing.assert_array_equal(rec[1:1 + len(narrow)], want(narrow))
-    np.testing.assert_array_equal(rec[n_ids - np.arange(len(wide))], want(wide))
+    assert len(rec) >= n_ids + 1 + len(tiles)
+    np.testing.assert_array_equal(rec[0], [len(narrow), offsets[-1], len(wide), len(tiles)])
+    want = np.stack([narrow, offsets[narrow], offsets[narrow + 1], ss[offsets[narrow]]], axis=1).reshape(-1, 4)
+    np.testing.assert_array_equal(rec[1:1 + len(narrow)], want)
+    np.testing.assert_array_equal(rec[n_ids + 1:n_ids + 1 + len(tiles)], np.array(tiles, dtype=np.int64).reshape(-1, 4))
 
 
 def test_route_ties_and_explicit_mode():
