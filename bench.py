@@ -10,9 +10,10 @@ and the weighted accumulation.  Default workload: the field-shape decode layer
 the layer (--rotate copies, distinct device buffers with identical bytes) and a fresh
 batch (distinct seeded activations and logits per step).
 
-Decode workloads run route -> gate/up -> down fused with the accumulation; batched
-workloads run route -> gate/up -> down -> accumulate, the experts with many tokens on
-the matrix cores.
+One-token decode runs the whole layer in one launch (moe_layer_decode_q); the
+three-call path (route, gate/up, down fused with the accumulation) is timed beside it.
+Multi-token decode runs the three-call path; batched workloads run route -> gate/up ->
+down -> accumulate, the experts with many tokens on the matrix cores.
 
 Prints one JSON line.  Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -47,7 +48,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 # Sources that define the mat-vec kernels; the counter summary below records their digest.
 KERNEL_SOURCES = ("codebook_quantized_routed_amd/csrc/common.hpp", "codebook_quantized_routed_amd/csrc/decode.hpp",
                   "codebook_quantized_routed_amd/csrc/matvec_common.hpp",
-                  "codebook_quantized_routed_amd/csrc/k_gemv.hip")
+                  "codebook_quantized_routed_amd/csrc/gemv_dev.hpp", "codebook_quantized_routed_amd/csrc/route_dev.hpp",
+                  "codebook_quantized_routed_amd/csrc/k_fused.hip")
 TRAFFIC_FILES = {"decode_iq2": "profiles/hbm_traffic_decode_iq2_t1.txt"}
 
 
@@ -162,8 +164,18 @@ def main():
     def k_accumulate(i, b):
         moe.accumulate(b["y"], b["w"], b["ids"], b["sp"], T, kp, H, acc[i])
 
-    if path == "decode":
-        kernels = [("route_group", k_route), ("gateup", k_gateup), ("down_accumulate", k_down_acc)]
+    fused = path == "decode" and T == 1
+    ws = torch.zeros(moe.decode_workspace_bytes(kp, I) // 4, dtype=torch.int32, device=dev) if fused else None
+
+    def k_layer_decode(i, b):
+        moe.layer_decode_q(layers[i % len(layers)].desc, lgs[i], xs[i], k, shared, b["ids"], b["w"], b["counts"],
+                           b["offsets"], b["ss"], b["sp"], b["work"], acc[i], ws)
+
+    split = [("route_group", k_route), ("gateup", k_gateup), ("down_accumulate", k_down_acc)]
+    if fused:
+        kernels = [("layer_decode", k_layer_decode)]
+    elif path == "decode":
+        kernels = split
     else:
         kernels = [("route_group", k_route), ("gateup", k_gateup), ("down", k_down), ("accumulate", k_accumulate)]
 
@@ -221,8 +233,10 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / K
 
-    back_to_back(k_gateup)  # warm: code objects and first touches
+    back_to_back(kernels[-1][1])  # warm: code objects and first touches
     kms = {name: back_to_back(fn) for name, fn in kernels}
+    if fused:  # the three-call path of the same steps, for comparison
+        kms.update({name: back_to_back(fn) for name, fn in split})
 
     # ---- whole-step timing
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -260,8 +274,14 @@ def main():
     tok_s = T / (ms * 1e-3)
 
     gu_b, dn_b, st_b = float(np.mean(gu_bytes)), float(np.mean(dn_bytes)), float(np.mean(step_bytes))
-    gu_ms = kms["gateup"]
-    achieved = gu_b / (gu_ms * 1e-3) / 1e9
+    if fused:  # the dominant (only) kernel: the whole layer in one launch
+        rl_kernel, rl_b, rl_ms = "k_layer_decode (route + gate/up + down + accumulate, one launch)", gu_b + dn_b, \
+            kms["layer_decode"]
+        traffic = measured_traffic(args.workload, "k_layer_decode")
+    else:
+        rl_kernel, rl_b, rl_ms = "gate/up (dequant mat-vec / MFMA + SiLU*up)", gu_b, kms["gateup"]
+        traffic = measured_traffic(args.workload, "k_gateup_wide")
+    achieved = rl_b / (rl_ms * 1e-3) / 1e9
     dn_name = "down_accumulate" if path == "decode" else "down"
     out = {
         "metric": METRIC,
@@ -281,11 +301,12 @@ def main():
         "step_hbm_gbs": round(st_b / (ms * 1e-3) / 1e9, 1),
         "step_hbm_frac": round(st_b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": int(st_b),
-        "roofline": {"bound": "hbm", "kernel": "gate/up (dequant mat-vec / MFMA + SiLU*up)",
+        "roofline": {"bound": "hbm", "kernel": rl_kernel,
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(args.workload, "k_gateup_wide"),
-                     "bytes_per_launch": int(gu_b), "launch_us": round(gu_ms * 1e3, 3)},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "bytes_per_launch": int(rl_b), "launch_us": round(rl_ms * 1e3, 3)},
+        "gateup": {"achieved_gbs": round(gu_b / (kms["gateup"] * 1e-3) / 1e9, 1), "bytes_per_launch": int(gu_b),
+                   "launch_us": round(kms["gateup"] * 1e3, 3)},
         dn_name: {"achieved_gbs": round(dn_b / (kms[dn_name] * 1e-3) / 1e9, 1), "bytes_per_launch": int(dn_b),
                   "launch_us": round(kms[dn_name] * 1e3, 3)},
         "route_group": {"launch_us": round(kms["route_group"] * 1e3, 3)},

@@ -27,7 +27,8 @@ STATUS = {0: "MOE_OK", -1: "MOE_E_NULL", -2: "MOE_E_SHAPE", -3: "MOE_E_QTYPE", -
 
 EXPORTS = ["moe_abi_version", "moe_status_string", "moe_last_hip_error", "moe_last_hip_error_string", "moe_grids_bytes", "moe_grids_expand", "moe_work_ints", "moe_workspace_bytes",
            "moe_route_group", "moe_expert_ffn_q", "moe_expert_gateup_q", "moe_expert_down_q",
-           "moe_expert_down_accumulate_q", "moe_accumulate", "moe_dequant_f32", "moe_rmsnorm"]
+           "moe_expert_down_accumulate_q", "moe_decode_workspace_bytes", "moe_layer_decode_q", "moe_accumulate",
+           "moe_dequant_f32", "moe_rmsnorm"]
 
 
 class MoeError(RuntimeError):
@@ -70,6 +71,8 @@ def _load():
         "moe_expert_gateup_q": (C.c_int, [P, P, i32, i32, P, P, P, P]),
         "moe_expert_down_q": (C.c_int, [P, P, i32, i32, P, P, P]),
         "moe_expert_down_accumulate_q": (C.c_int, [P, P, i32, i32, P, P, P, P, P]),
+        "moe_decode_workspace_bytes": (sz, [i32, i32]),
+        "moe_layer_decode_q": (C.c_int, [P, P, P, i32, i32, P, P, P, P, P, P, P, P, P, sz, P]),
         "moe_accumulate": (C.c_int, [P, P, P, P, i32, i32, i32, P, P]),
         "moe_dequant_f32": (C.c_int, [i32, i32, i32, P, P, P, P, P, P]),
         "moe_rmsnorm": (C.c_int, [P, i32, i32, C.c_float, P, P]),
@@ -150,6 +153,21 @@ def expert_down_accumulate_q(layer: Layer, h, T, kprime, ids, w, slot_pos, acc, 
     _check("moe_expert_down_accumulate_q",
            lib.moe_expert_down_accumulate_q(C.byref(layer), _ptr(h), T, kprime, _ptr(ids), _ptr(w), _ptr(slot_pos),
                                             _ptr(acc), _stream(stream)))
+
+
+def decode_workspace_bytes(kprime: int, inter: int) -> int:
+    return lib.moe_decode_workspace_bytes(kprime, inter)
+
+
+def layer_decode_q(layer: Layer, logits, x, k, add_shared, ids, w, counts, offsets, sorted_slot, slot_pos, work, acc,
+                   ws, stream=None):
+    """One decode step (one token) of the layer in one launch; ws: decode_workspace_bytes
+    bytes, its first 256 zero before the first call."""
+    nbytes = ws.numel() * ws.element_size()
+    _check("moe_layer_decode_q",
+           lib.moe_layer_decode_q(C.byref(layer), _ptr(logits), _ptr(x), k, add_shared, _ptr(ids), _ptr(w),
+                                  _ptr(counts), _ptr(offsets), _ptr(sorted_slot), _ptr(slot_pos), _ptr(work),
+                                  _ptr(acc), _ptr(ws), nbytes, _stream(stream)))
 
 
 def accumulate(y, w, ids, slot_pos, T, kprime, hidden, acc, stream=None):

@@ -207,6 +207,29 @@ moe_status moe_expert_ffn_q(const moe_layer *layer, const float *d_x, int32_t T,
   return from_hip(launch_down(L, h, T, kprime, work, n_ids, d_y, stream));
 }
 
+size_t moe_decode_workspace_bytes(int32_t kprime, int32_t inter) {
+  if (kprime < 1 || kprime > MOE_MAX_K + 1 || inter < 1) return 0;
+  return fused_sync_bytes() + (size_t)kprime * inter * sizeof(float);
+}
+
+moe_status moe_layer_decode_q(const moe_layer *layer, const float *d_logits, const float *d_x, int32_t k,
+                              int32_t add_shared, int32_t *d_ids, float *d_w, int32_t *d_counts, int32_t *d_offsets,
+                              int32_t *d_sorted_slot, int32_t *d_slot_pos, int32_t *d_work, float *d_acc, void *d_ws,
+                              size_t ws_bytes, hipStream_t stream) {
+  LayerArgs L;
+  moe_status st = check_ffn_common(layer, &L, 1, k + add_shared,
+                                   {d_x, d_ids, d_w, d_counts, d_offsets, d_sorted_slot, d_slot_pos, d_work, d_acc, d_ws});
+  if (st != MOE_OK) return st;
+  if (d_logits && !aligned16(d_logits)) return MOE_E_ALIGN;
+  const int E = layer->n_experts;
+  if (k < 1 || k > MOE_MAX_K || k > E || add_shared != layer->has_shared || E > 512) return MOE_E_SHAPE;
+  if (L.hidden != 2048 || (L.inter != 256 && L.inter != 512)) return MOE_E_SHAPE;
+  if (ws_bytes < moe_decode_workspace_bytes(k + add_shared, L.inter)) return MOE_E_WORKSPACE;
+  clear_pending();
+  return from_hip(launch_layer_decode(L, d_logits, d_x, E, k, add_shared, d_ids, d_w, d_counts, d_offsets,
+                                      d_sorted_slot, d_slot_pos, (WorkRec *)d_work, d_acc, d_ws, stream));
+}
+
 moe_status moe_accumulate(const float *d_y, const float *d_w, const int32_t *d_ids, const int32_t *d_slot_pos,
                           int32_t T, int32_t kprime, int32_t hidden, float *d_acc, hipStream_t stream) {
   if (!d_y || !d_w || !d_ids || !d_slot_pos || !d_acc) return MOE_E_NULL;

@@ -161,6 +161,10 @@ hipError_t launch_down_mfma(const LayerArgs &L, const float *h, int T, int kprim
                             float *y, hipStream_t s);
 hipError_t launch_down_accumulate(const LayerArgs &L, const float *h, int T, int kprime, const int32_t *ids,
                                   const float *w, const int32_t *slot_pos, float *acc, hipStream_t s);
+size_t fused_sync_bytes();
+hipError_t launch_layer_decode(const LayerArgs &L, const float *logits, const float *x, int E, int k, int add_shared,
+                               int32_t *ids, float *w, int32_t *counts, int32_t *offsets, int32_t *sorted_slot,
+                               int32_t *slot_pos, WorkRec *work, float *acc, void *ws, hipStream_t s);
 hipError_t launch_accumulate(const float *y, const float *w, const int32_t *ids, const int32_t *slot_pos, int T,
                              int kprime, int H, float *acc, hipStream_t s);
 hipError_t launch_rmsnorm(const float *h, int T, int H, float eps, float *x, hipStream_t s);

@@ -1,0 +1,324 @@
+// The whole decode step of one layer for one token in a single launch.
+//
+// "Red Metal dev8 — resident routed top-k layer", steps 3-6: the router selects the
+// experts, each selected expert runs gate, up, SiLU(gate) * up and down, and the
+// outputs are accumulated as acc += router_weight * expert_output in one command, with
+// only the final output leaving the layer.  Here that command is one kernel:
+//
+//  1. every workgroup selects the same experts (top-k of the token's logits, or the
+//     caller's explicit list) -- no exchange is needed for routing; the routing
+//     outputs of moe_route_group are written at the end;
+//  2. gate / up items (2 rows of one expert) are dealt to the waves of the whole grid,
+//     h goes to global memory in sorted order;
+//  3. a grid-wide barrier (all workgroups are resident: one per compute unit at most);
+//     h is written and read with agent-scope atomics, so every row is visible to
+//     every workgroup once its writer has arrived; the down rows a wave needs after
+//     the barrier depend on the routing only, so their loads are issued between its
+//     workgroup's arrival and the wait;
+//  4. down + the weighted accumulation in ascending expert id for the workgroup's
+//     block of output rows.
+// The arithmetic of every step is the one of moe_route_group, moe_expert_gateup_q and
+// moe_expert_down_accumulate_q, so the results are the same bits.
+//
+// The barrier waits a bounded time: if a workgroup never arrives (which needs another
+// kernel holding compute units meanwhile), the waiters give up after about a second,
+// set the error word and finish; the results of that call are then undefined.
+#include "gemv_dev.hpp"
+#include "route_dev.hpp"
+
+namespace moe {
+
+constexpr int kFusedWaves = 8;
+constexpr int kDownWaves = kFusedWaves - 1;  // the last wave polls the grid barrier
+constexpr int kFusedMaxSlots = MOE_MAX_K + 1;
+constexpr int kFusedSlotsPerWave = (kFusedMaxSlots + kDownWaves - 1) / kDownWaves;
+constexpr int kSpinLimit = 1 << 20;  // polls of about 1 us: about a second
+
+// Workspace of the fused call: the barrier words, then h [kprime][inter] fp32.  The
+// barrier is two-level: workgroup g counts on the counter of its group g / kBarGroup,
+// the last arrival of a group counts on the top counter.  Counters are monotonic over
+// all calls (a call completes a whole round of each) and sit in separate 128-byte
+// lines; error is set if a wait timed out.
+constexpr int kBarGroup = 16;
+constexpr int kBarGroups = 32;  // up to 512 workgroups
+struct FusedSync {
+  uint64_t top, pad0[15];
+  uint32_t error, pad1[31];
+  struct Line {
+    uint64_t count, pad[15];
+  } group[kBarGroups];
+};
+static_assert(sizeof(FusedSync) == 4352, "h follows the barrier words");
+
+struct FusedLds {
+  TopkLds topk;
+  int32_t ids[kFusedMaxSlots];         // slot j -> expert
+  float w[kFusedMaxSlots];             // slot j -> router weight
+  int32_t slot_at[kFusedMaxSlots];     // sorted position p -> slot
+  int32_t pos_of[kFusedMaxSlots];      // slot j -> sorted position
+  float ydot[kFusedMaxSlots][16];      // down outputs of the block's rows, per slot
+};
+
+__host__ __device__ inline size_t fused_stage_floats(int lpr) {
+  return (size_t)kFusedWaves * kFusedSlotsPerWave * lpr * kChunkPad;
+}
+
+// Grid-wide barrier over n workgroups, in two halves so a workgroup can work between
+// them; called by one thread per workgroup.  Every value exchanged through it (h) is
+// stored and loaded with agent-scope atomics, which reach the coherence point directly,
+// and each wave waits for its stores before the workgroup barrier that precedes the
+// arrival, so the barrier words themselves need no cache maintenance.  Arrival: count
+// on the group's counter; the group's last arrival of this round counts on the top
+// counter.  Wait: poll the top counter (with a pause between polls, a bounded number
+// of times) until it completes the round.
+__device__ inline uint64_t barrier_arrive(FusedSync *s, uint32_t n) {
+  const uint32_t g = blockIdx.x / kBarGroup, n_groups = (n + kBarGroup - 1) / kBarGroup;
+  const uint32_t size = min((uint32_t)kBarGroup, n - g * kBarGroup);
+  const uint64_t prev =
+      __hip_atomic_fetch_add(&s->group[g].count, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t round = prev / size;
+  if ((prev + 1) % size == 0)
+    __hip_atomic_fetch_add(&s->top, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return (round + 1) * n_groups;
+}
+
+__device__ inline void barrier_wait(FusedSync *s, uint64_t target) {
+  for (int spin = 0; __hip_atomic_load(&s->top, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target; spin++) {
+    if (spin == kSpinLimit) {
+      __hip_atomic_store(&s->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(8);
+  }
+}
+
+template <int LPR>
+__global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, const float *__restrict__ logits,
+                                                                    const float *__restrict__ x, int E, int k,
+                                                                    int add_shared, int32_t *__restrict__ ids,
+                                                                    float *__restrict__ w, int32_t *__restrict__ counts,
+                                                                    int32_t *__restrict__ offsets,
+                                                                    int32_t *__restrict__ sorted_slot,
+                                                                    int32_t *__restrict__ slot_pos,
+                                                                    WorkRec *__restrict__ work, float *__restrict__ acc,
+                                                                    FusedSync *__restrict__ sync) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  __shared__ FusedLds S;
+  constexpr int RPP = 64 / LPR, HS = LPR * kChunkPad;
+  const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
+  const int kprime = k + add_shared, n_ids = E + add_shared;
+  const int H = L.hidden, I = L.inter;
+  float *h = (float *)(sync + 1);
+  const int formats = layer_formats(L);
+  const TableLayout TL = table_layout(formats);
+  float *hs = (float *)(lds + TL.bytes) + wave * kFusedSlotsPerWave * HS;
+  // wave 0's logits are the first loads of the kernel; the table rows are loaded by
+  // waves 1.. while wave 0 routes (vector loads complete in order)
+  TopkVals<8> tv;
+  if (wave == 0 && logits) tv = topk_load<8>(logits, E);
+  const TableRegs tr = tables_load(L.grids, formats, threadIdx.x - 64, blockDim.x - 64);
+
+  // ---- 1. routing, in every workgroup
+  if (wave == 0) {
+    if (logits) {
+      topk_select<8>(tv, E, k, add_shared, blockIdx.x == 0 ? ids : nullptr, w, S.ids, S.w, S.topk);
+    } else {
+      if (lane < k) {
+        S.ids[lane] = ids[lane];
+        S.w[lane] = w[lane];
+      }
+      if (add_shared && lane == k) {
+        S.ids[k] = E;
+        S.w[k] = 1.0f;
+        if (blockIdx.x == 0) {
+          ids[k] = E;
+          w[k] = 1.0f;
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    const int my = lane < kprime ? S.ids[lane] : 0x7FFFFFFF;
+    int rank = 0;
+    for (int j = 0; j < kprime; j++) {
+      const int o = __builtin_amdgcn_readlane(my, j);
+      rank += (o < my || (o == my && j < lane)) ? 1 : 0;
+    }
+    if (lane < kprime) {
+      S.pos_of[lane] = rank;
+      S.slot_at[rank] = lane;
+    }
+  }
+  __syncthreads();
+
+  // ---- 2. gate / up items: activations, then the first two items, issued before
+  // anything waits
+  X32 X;
+  load_x32(x + 32 * lane, X);
+  const int q = lane, lq = lane % LPR, sub = lane / LPR;
+  const int ipe = I / kWideRows, n_items = kprime * ipe, nw = gridDim.x * kFusedWaves;
+  int item = blockIdx.x * kFusedWaves + wave;
+  WideItem It, It2;
+  int cur_tok = 0;
+  bool gs_ok = false;
+  const bool have1 = item < n_items, have2 = item + nw < n_items;
+  if (have1) {
+    const int p = item / ipe, slot = uniform(S.slot_at[p]);
+    It.W = WorkRec{uniform(S.ids[slot]), p, p + 1, slot};
+    wide_issue(L, It, item - p * ipe, q);
+  }
+  if (have2) {
+    const int it2 = item + nw, p = it2 / ipe, slot = uniform(S.slot_at[p]);
+    It2.W = WorkRec{uniform(S.ids[slot]), p, p + 1, slot};
+    wide_issue(L, It2, it2 - p * ipe, q);
+  }
+  tables_store(tr, formats, TL, lds, threadIdx.x - 64, blockDim.x - 64);
+  if (have1) {
+    if (It.qt == MOE_Q_IQ2XS_LIKE)
+      wide_run<MOE_Q_IQ2XS_LIKE, true>(L, It, X, cur_tok, gs_ok, q, kprime, x, sorted_slot, lds, TL, h);
+    else
+      wide_run<MOE_Q_IQ1M_LIKE, true>(L, It, X, cur_tok, gs_ok, q, kprime, x, sorted_slot, lds, TL, h);
+  }
+  for (item += nw; item < n_items; item += nw) {
+    if (item != blockIdx.x * kFusedWaves + wave + nw) {  // the second item was issued above
+      const int p = item / ipe, slot = uniform(S.slot_at[p]);
+      It2.W = WorkRec{uniform(S.ids[slot]), p, p + 1, slot};
+      wide_issue(L, It2, item - p * ipe, q);
+    }
+    if (It2.qt == MOE_Q_IQ2XS_LIKE)
+      wide_run<MOE_Q_IQ2XS_LIKE, true>(L, It2, X, cur_tok, gs_ok, q, kprime, x, sorted_slot, lds, TL, h);
+    else
+      wide_run<MOE_Q_IQ1M_LIKE, true>(L, It2, X, cur_tok, gs_ok, q, kprime, x, sorted_slot, lds, TL, h);
+  }
+
+  // ---- 3. every h row written before any is read: each wave's h stores complete, then
+  // the workgroup arrives.  Between arrival and wait, waves 0 .. kDownWaves-1 load the
+  // down rows of the workgroup's first block and its acc values; the last wave polls
+  // (its loads would otherwise queue behind those).
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const bool poller = threadIdx.x == 64 * kDownWaves;
+  uint64_t target = 0;
+  if (poller) target = barrier_arrive(sync, gridDim.x);
+  const int tiles = H / RPP;
+  int tile = blockIdx.x;
+  RowRaw Rd[kFusedSlotsPerWave];
+  int dqt[kFusedSlotsPerWave];
+#pragma unroll
+  for (int i = 0; i < kFusedSlotsPerWave; i++) {
+    const int j = wave + kDownWaves * i;
+    dqt[i] = 0;
+    if (wave < kDownWaves && j < kprime && tile < tiles) {
+      const int e = uniform(S.ids[j]);
+      const BankArgs &B = bank_of(L, e);
+      const QMat Wd = expert_mat(B, e, kDown, H, I);
+      dqt[i] = B.qtype;
+      Rd[i] = B.qtype == MOE_Q_IQ2XS_LIKE ? load_row<MOE_Q_IQ2XS_LIKE>(Wd, I, tile * RPP + sub, lq)
+                                          : load_row<MOE_Q_IQ1M_LIKE>(Wd, I, tile * RPP + sub, lq);
+    }
+  }
+  float acc_in = 0.0f;
+  if (threadIdx.x < RPP && tile < tiles) acc_in = acc[tile * RPP + threadIdx.x];
+  if (poller) barrier_wait(sync, target);
+  __syncthreads();
+
+  // ---- 4. down + accumulation, block by block of RPP output rows
+  for (bool first = true; tile < tiles; tile += gridDim.x, first = false) {
+#pragma unroll
+    for (int i = 0; i < kFusedSlotsPerWave; i++) {
+      const int j = wave + kDownWaves * i;
+      if (wave < kDownWaves && j < kprime) {
+        if (!first) {
+          const int e = uniform(S.ids[j]);
+          const BankArgs &B = bank_of(L, e);
+          const QMat Wd = expert_mat(B, e, kDown, H, I);
+          Rd[i] = dqt[i] == MOE_Q_IQ2XS_LIKE ? load_row<MOE_Q_IQ2XS_LIKE>(Wd, I, tile * RPP + sub, lq)
+                                             : load_row<MOE_Q_IQ1M_LIKE>(Wd, I, tile * RPP + sub, lq);
+        }
+        // the slot's h row into the wave's LDS area (64-float chunks padded to kChunkPad
+        // floats), read with agent-scope loads: other workgroups wrote it
+        const uint32_t *src = (const uint32_t *)(h + (size_t)S.pos_of[j] * I);
+        for (int f = lane; f < LPR * 16; f += 64) {
+          uint4 v;
+          v.x = __hip_atomic_load(src + 4 * f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          v.y = __hip_atomic_load(src + 4 * f + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          v.z = __hip_atomic_load(src + 4 * f + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          v.w = __hip_atomic_load(src + 4 * f + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          *(uint4 *)(hs + i * HS + (f >> 4) * kChunkPad + (f & 15) * 4) = v;
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < kFusedSlotsPerWave; i++) {
+      const int j = wave + kDownWaves * i;
+      if (wave < kDownWaves && j < kprime) {
+        const float *hrow = hs + i * HS + lq * kChunkPad;
+        const float v = dqt[i] == MOE_Q_IQ2XS_LIKE ? down_slot_dot<MOE_Q_IQ2XS_LIKE, LPR>(Rd[i], hrow, lq, lds, TL)
+                                                   : down_slot_dot<MOE_Q_IQ1M_LIKE, LPR>(Rd[i], hrow, lq, lds, TL);
+        if (lq == 0) S.ydot[j][sub] = v;
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x < RPP) {
+      const int r = tile * RPP + threadIdx.x;
+      float a = first ? acc_in : acc[r];
+      for (int p = 0; p < kprime; p++) {
+        const int j = S.slot_at[p];
+        a = __fadd_rn(a, __fmul_rn(S.w[j], S.ydot[j][threadIdx.x]));
+      }
+      acc[r] = a;
+    }
+    __syncthreads();
+  }
+
+  // ---- 5. the grouping outputs of moe_route_group (one token: every count is 0 or 1):
+  // counts and offsets spread over the workgroups, the rest from workgroup 0
+  for (int e = blockIdx.x + gridDim.x * threadIdx.x; e < n_ids; e += gridDim.x * blockDim.x) {
+    int below = 0, at = 0;
+    for (int j = 0; j < kprime; j++) {
+      below += S.ids[j] < e ? 1 : 0;
+      at += S.ids[j] == e ? 1 : 0;
+    }
+    counts[e] = at;
+    offsets[e] = below;
+  }
+  if (blockIdx.x == 0 && threadIdx.x < kprime) {
+    const int p = threadIdx.x, slot = S.slot_at[p];
+    sorted_slot[p] = slot;
+    slot_pos[slot] = p;
+    work[1 + p] = WorkRec{S.ids[slot], p, p + 1, slot};
+    if (p == 0) {
+      offsets[n_ids] = kprime;
+      work[0] = WorkRec{kprime, kprime, 0, 0};
+    }
+  }
+}
+
+size_t fused_sync_bytes() { return sizeof(FusedSync); }
+
+size_t fused_lds_bytes(const LayerArgs &L) {
+  return table_layout(L.formats).bytes + fused_stage_floats(L.inter / 64) * sizeof(float);
+}
+
+hipError_t launch_layer_decode(const LayerArgs &L, const float *logits, const float *x, int E, int k, int add_shared,
+                               int32_t *ids, float *w, int32_t *counts, int32_t *offsets, int32_t *sorted_slot,
+                               int32_t *slot_pos, WorkRec *work, float *acc, void *ws, hipStream_t s) {
+  int dev = 0, cus = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (err != hipSuccess) return err;
+  const int lpr = L.inter / 64, tiles = L.hidden / (64 / lpr);
+  const int g = tiles < cus ? tiles : cus;
+  const dim3 grid((unsigned)(g < kBarGroup * kBarGroups ? g : kBarGroup * kBarGroups)), block(64 * kFusedWaves);
+  FusedSync *sync = (FusedSync *)ws;
+  if (lpr == 8)
+    hipLaunchKernelGGL(k_layer_decode<8>, grid, block, fused_lds_bytes(L), s, L, logits, x, E, k, add_shared, ids, w,
+                       counts, offsets, sorted_slot, slot_pos, work, acc, sync);
+  else
+    hipLaunchKernelGGL(k_layer_decode<4>, grid, block, fused_lds_bytes(L), s, L, logits, x, E, k, add_shared, ids, w,
+                       counts, offsets, sorted_slot, slot_pos, work, acc, sync);
+  return hipGetLastError();
+}
+
+}  // namespace moe

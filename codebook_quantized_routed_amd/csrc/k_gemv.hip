@@ -20,130 +20,9 @@
 //    sums of x formed once per activation row; d * (2s+1) scales each 16-column
 //    sub-block sum.
 // Every dequantized weight is exact; products and sums are rounded in fp32.
-#include "matvec_common.hpp"
+#include "gemv_dev.hpp"
 
 namespace moe {
-
-// A lane's slice of one row.  IQ2: a = 8 codes, b = (sc word, d bits).
-// IQ1: a.xy = 8 ql bytes, a.z = 4 qh bytes, b = the 64-bit sd word.
-struct RowRaw {
-  uint4 a;
-  uint2 b;
-};
-
-// Hides a row's codes from loop-invariant code motion, which would otherwise decode
-// the row once before a token loop and keep every decoded weight live.
-__device__ __forceinline__ void opaque(RowRaw &R) {
-  asm volatile("" : "+v"(R.a.x), "+v"(R.a.y), "+v"(R.a.z), "+v"(R.a.w), "+v"(R.b.x), "+v"(R.b.y));
-}
-
-template <int QT>
-__device__ __forceinline__ RowRaw load_row(const QMat &m, int cols, int r, int q) {
-  const int ng = cols >> 3, nb = cols >> 8, b = q >> 2;
-  RowRaw R;
-  if constexpr (QT == MOE_Q_IQ2XS_LIKE) {
-    R.a = load_stream16(m.s0 + ((size_t)r * ng + 8 * q) * 2);
-    R.b.x = ((const uint32_t *)m.s1)[(size_t)r * nb + b];
-    R.b.y = ((const uint16_t *)m.s2)[(size_t)r * nb + b];
-  } else {
-    const uint2 ql = load_stream8(m.s0 + (size_t)r * ng + 8 * q);
-    const uint32_t qh = __builtin_nontemporal_load((const uint32_t *)(m.s1 + (size_t)r * (ng / 2) + 4 * q));
-    R.a = make_uint4(ql.x, ql.y, qh, 0u);
-    R.b = *(const uint2 *)(m.s2 + ((size_t)r * nb + b) * 8);
-  }
-  return R;
-}
-
-// Activation slice of a lane: 64 floats, plus the 8 group sums times 1/8 (IQ1 only).
-struct XChunk {
-  float v[64];
-  float gs8[8];
-};
-
-template <int QT>
-__device__ __forceinline__ void load_x(const float *p, XChunk &X) {
-  const float4 *p4 = (const float4 *)p;
-#pragma unroll
-  for (int i = 0; i < 16; i++) {
-    const float4 f = p4[i];
-    X.v[4 * i] = f.x;
-    X.v[4 * i + 1] = f.y;
-    X.v[4 * i + 2] = f.z;
-    X.v[4 * i + 3] = f.w;
-  }
-  if constexpr (QT == MOE_Q_IQ1M_LIKE) {
-#pragma unroll
-    for (int g = 0; g < 8; g++) {
-      float s = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 8; j++) s += X.v[8 * g + j];
-      X.gs8[g] = s * 0.125f;
-    }
-  }
-}
-
-// ----------------------------------------------------------------------------- dot
-__device__ __forceinline__ float lo16(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w).x; }
-__device__ __forceinline__ float hi16(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w).y; }
-
-// 8 weights (4 packed fp16 pairs) times 8 activations added into two accumulation
-// chains (even and odd columns); each step is one v_fma_mix_f32.
-__device__ __forceinline__ void dot8(const uint4 &w, const float *x, float &a, float &b) {
-  a = fmaf(lo16(w.x), x[0], a);
-  b = fmaf(hi16(w.x), x[1], b);
-  a = fmaf(lo16(w.y), x[2], a);
-  b = fmaf(hi16(w.y), x[3], b);
-  a = fmaf(lo16(w.z), x[4], a);
-  b = fmaf(hi16(w.z), x[5], b);
-  a = fmaf(lo16(w.w), x[6], a);
-  b = fmaf(hi16(w.w), x[7], b);
-}
-
-// Dot product of a lane's 64-column slice of one row with its activation slice.
-template <int QT>
-__device__ __forceinline__ float dot_chunk(const RowRaw &R, int q, const uint8_t *lds, const TableLayout &TL,
-                                           const XChunk &X) {
-  if constexpr (QT == MOE_Q_IQ2XS_LIKE) {
-    const uint4 *rows = (const uint4 *)(lds + TL.iq2h);
-    const uint4 *masks = (const uint4 *)(lds + TL.iq2m);
-    float a[2] = {0.0f, 0.0f}, b[2] = {0.0f, 0.0f};
-#pragma unroll
-    for (int g = 0; g < 8; g++) {
-      const uint32_t w32 = g < 2 ? R.a.x : (g < 4 ? R.a.y : (g < 6 ? R.a.z : R.a.w));
-      const uint32_t code = (g & 1) ? (w32 >> 16) : (w32 & 0xFFFFu);
-      uint4 v = rows[code & 0x1FFu];
-      const uint4 m = masks[(code >> 9) & 0x7Fu];
-      v.x ^= m.x;
-      v.y ^= m.y;
-      v.z ^= m.z;
-      v.w ^= m.w;
-      dot8(v, X.v + 8 * g, a[g >> 2], b[g >> 2]);
-    }
-    const float acc[2] = {a[0] + b[0], a[1] + b[1]};
-    const int sb = 2 * (q & 3);
-    return fmaf(acc[1], iq2_factor(R.b.x, R.b.y, sb + 1), acc[0] * iq2_factor(R.b.x, R.b.y, sb));
-  } else {
-    const uint4 *rows = (const uint4 *)(lds + TL.iq1h);
-    float a[4] = {0.0f, 0.0f, 0.0f, 0.0f}, b[4] = {0.0f, 0.0f, 0.0f, 0.0f}, ds[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int g = 0; g < 8; g++) {
-      const uint32_t ql8 = ((g < 4 ? R.a.x : R.a.y) >> (8 * (g & 3))) & 0xFFu;
-      const uint32_t nib = (R.a.z >> (4 * g)) & 15u;
-      const uint4 v = rows[ql8 | ((nib & 7u) << 8)];
-      ds[g >> 1] += (nib & 8u) ? -X.gs8[g] : X.gs8[g];
-      dot8(v, X.v + 8 * g, a[g >> 1], b[g >> 1]);
-    }
-    float acc[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) acc[i] = (a[i] + b[i]) + ds[i];
-    const uint64_t sd = ((uint64_t)R.b.y << 32) | R.b.x;
-    const int sb = 4 * (q & 3);
-    float r = acc[0] * iq1_factor(sd, sb);
-    r = fmaf(acc[1], iq1_factor(sd, sb + 1), r);
-    r = fmaf(acc[2], iq1_factor(sd, sb + 2), r);
-    return fmaf(acc[3], iq1_factor(sd, sb + 3), r);
-  }
-}
 
 // ----------------------------------------------------------------------------- gate + up
 // A pass = rows [rp*RPP, rp*RPP + RPP) of one active expert, gate and up together.  A
@@ -245,153 +124,9 @@ __global__ void __launch_bounds__(256) k_gateup(LayerArgs L, const float *__rest
   }
 }
 
-// ----------------------------------------------------------------------------- gate + up, hidden 2048
-// Decode layout for hidden = 2048: a whole wave covers one row (32 columns per lane), so
-// a lane's activation slice is 32 floats with no copy shared between lanes, loaded once
-// per wave while the wave's items keep the same token.  An item is kWideRows rows of one
-// expert, gate and up.  Issue order: compact-table loads, work record (scalar), row and
-// activation loads, then the table build; compute waits only for what it uses.
-constexpr int kWideRows = 2;
-
-struct Row32 {  // IQ2: x = codes 0-1, y = codes 2-3, z = sc word, w = d bits.
-  uint4 v;      // IQ1: x = 4 ql bytes, y = 4 qh nibbles (16 bits), z/w = the sd word.
-};
-
-__device__ __forceinline__ void opaque(Row32 &R) { asm volatile("" : "+v"(R.v.x), "+v"(R.v.y), "+v"(R.v.z), "+v"(R.v.w)); }
-
-template <int QT>
-__device__ __forceinline__ Row32 load_row32(const QMat &m, int cols, int r, int q) {
-  const int ng = cols >> 3, nb = cols >> 8, b = q >> 3;
-  Row32 R;
-  if constexpr (QT == MOE_Q_IQ2XS_LIKE) {
-    const uint2 c = load_stream8(m.s0 + ((size_t)r * ng + 4 * q) * 2);
-    R.v = make_uint4(c.x, c.y, ((const uint32_t *)m.s1)[(size_t)r * nb + b], ((const uint16_t *)m.s2)[(size_t)r * nb + b]);
-  } else {
-    const uint32_t ql = __builtin_nontemporal_load((const uint32_t *)(m.s0 + (size_t)r * ng + 4 * q));
-    const uint32_t qh = __builtin_nontemporal_load((const uint16_t *)(m.s1 + (size_t)r * (ng / 2) + 2 * q));
-    const uint2 sd = *(const uint2 *)(m.s2 + ((size_t)r * nb + b) * 8);
-    R.v = make_uint4(ql, qh, sd.x, sd.y);
-  }
-  return R;
-}
-
-struct X32 {
-  float v[32];
-  float gs8[4];
-};
-
-template <int QT>
-__device__ __forceinline__ float dot32(const Row32 &R, int q, const uint8_t *lds, const TableLayout &TL, const X32 &X) {
-  if constexpr (QT == MOE_Q_IQ2XS_LIKE) {
-    const uint4 *rows = (const uint4 *)(lds + TL.iq2h);
-    const uint4 *masks = (const uint4 *)(lds + TL.iq2m);
-    float a = 0.0f, b = 0.0f;
-#pragma unroll
-    for (int g = 0; g < 4; g++) {
-      const uint32_t w32 = g < 2 ? R.v.x : R.v.y;
-      const uint32_t code = (g & 1) ? (w32 >> 16) : (w32 & 0xFFFFu);
-      uint4 v = rows[code & 0x1FFu];
-      const uint4 m = masks[(code >> 9) & 0x7Fu];
-      v.x ^= m.x;
-      v.y ^= m.y;
-      v.z ^= m.z;
-      v.w ^= m.w;
-      dot8(v, X.v + 8 * g, a, b);
-    }
-    return (a + b) * iq2_factor(R.v.z, R.v.w, q & 7);
-  } else {
-    const uint4 *rows = (const uint4 *)(lds + TL.iq1h);
-    float a[2] = {0.0f, 0.0f}, b[2] = {0.0f, 0.0f}, ds[2] = {0.0f, 0.0f};
-#pragma unroll
-    for (int g = 0; g < 4; g++) {
-      const uint32_t ql8 = (R.v.x >> (8 * g)) & 0xFFu;
-      const uint32_t nib = (R.v.y >> (4 * g)) & 15u;
-      const uint4 v = rows[ql8 | ((nib & 7u) << 8)];
-      ds[g >> 1] += (nib & 8u) ? -X.gs8[g] : X.gs8[g];
-      dot8(v, X.v + 8 * g, a[g >> 1], b[g >> 1]);
-    }
-    const uint64_t sd = ((uint64_t)R.v.w << 32) | R.v.z;
-    const int sb = 2 * (q & 7);
-    return fmaf((a[1] + b[1]) + ds[1], iq1_factor(sd, sb + 1), ((a[0] + b[0]) + ds[0]) * iq1_factor(sd, sb));
-  }
-}
-
-__device__ __forceinline__ void load_x32(const float *p, X32 &X) {
-  const float4 *p4 = (const float4 *)p;
-#pragma unroll
-  for (int i = 0; i < 8; i++) {
-    const float4 f = p4[i];
-    X.v[4 * i] = f.x;
-    X.v[4 * i + 1] = f.y;
-    X.v[4 * i + 2] = f.z;
-    X.v[4 * i + 3] = f.w;
-  }
-}
-
-__device__ __forceinline__ void group_sums32(X32 &X) {
-#pragma unroll
-  for (int g = 0; g < 4; g++) {
-    float s = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; j++) s += X.v[8 * g + j];
-    X.gs8[g] = s * 0.125f;
-  }
-}
-
-struct WideItem {
-  WorkRec W;
-  Row32 g[kWideRows], u[kWideRows];
-  int r0, qt;
-};
-
-__device__ __forceinline__ void wide_issue(const LayerArgs &L, WideItem &It, int rb, int q) {
-  const int H = L.hidden, I = L.inter;
-  const BankArgs &B = bank_of(L, It.W.e);
-  It.qt = B.qtype;
-  It.r0 = rb * kWideRows;
-  const QMat Wg = expert_mat(B, It.W.e, kGate, I, H), Wu = expert_mat(B, It.W.e, kUp, I, H);
-#pragma unroll
-  for (int i = 0; i < kWideRows; i++) {
-    if (It.qt == MOE_Q_IQ2XS_LIKE) {
-      It.g[i] = load_row32<MOE_Q_IQ2XS_LIKE>(Wg, H, It.r0 + i, q);
-      It.u[i] = load_row32<MOE_Q_IQ2XS_LIKE>(Wu, H, It.r0 + i, q);
-    } else {
-      It.g[i] = load_row32<MOE_Q_IQ1M_LIKE>(Wg, H, It.r0 + i, q);
-      It.u[i] = load_row32<MOE_Q_IQ1M_LIKE>(Wu, H, It.r0 + i, q);
-    }
-  }
-}
-
-template <int QT>
-__device__ __forceinline__ void wide_run(const LayerArgs &L, WideItem &It, X32 &X, int &cur_tok, bool &gs_ok, int q,
-                                         int kprime, const float *x, const int32_t *sorted_slot, const uint8_t *lds,
-                                         const TableLayout &TL, float *h) {
-  const int H = L.hidden, I = L.inter;
-  for (int p = It.W.p0; p < It.W.p1; p++) {
-    const int tok = (p == It.W.p0 ? It.W.slot0 : sload(sorted_slot + p)) / kprime;
-    if (tok != cur_tok) {
-      load_x32(x + (size_t)tok * H + 32 * q, X);
-      cur_tok = tok;
-      gs_ok = false;
-    }
-    if constexpr (QT == MOE_Q_IQ1M_LIKE) {  // group sums of the current activations, once
-      if (!gs_ok) group_sums32(X);
-      gs_ok = true;
-    }
-#pragma unroll
-    for (int i = 0; i < kWideRows; i++) {
-      Row32 g = It.g[i], u = It.u[i];
-      opaque(g);
-      opaque(u);
-      float vg = dot32<QT>(g, q, lds, TL, X);
-      float vu = dot32<QT>(u, q, lds, TL, X);
-      vg = group_sum_first<64>(vg);
-      vu = group_sum_first<64>(vu);
-      if (q == 0) h[(size_t)p * I + It.r0 + i] = silu(vg) * vu;
-    }
-  }
-}
-
+// gate + up for hidden 2048 (one row per wave, 32 columns per lane; see the item
+// layout in gemv_dev.hpp): one item per wave and grid step, the first item's loads
+// issued before the table build.
 __global__ void __launch_bounds__(256) k_gateup_wide(LayerArgs L, const float *__restrict__ x, int kprime,
                                                      const int32_t *__restrict__ sorted_slot,
                                                      const WorkRec *__restrict__ work, int max_tokens, int n_ids,
@@ -490,20 +225,6 @@ __global__ void __launch_bounds__(256) k_down(LayerArgs L, const float *__restri
 // 64-float chunk padded to 68 floats so the lanes of different chunks hit different
 // banks), the slots' weight rows, acc and w.  The slot scalars come through the scalar
 // cache, so issuing the weight loads never waits on a vector load.
-constexpr int kDaWaves = 4;
-constexpr int kDaSlots = (MOE_MAX_K + 1 + kDaWaves - 1) / kDaWaves;  // slots per wave, at most
-constexpr int kChunkPad = 68;
-
-__host__ __device__ inline size_t down_acc_stage_bytes(int lpr) { return (size_t)kDaWaves * kDaSlots * lpr * kChunkPad * 4; }
-
-template <int QT, int LPR>
-__device__ __forceinline__ float down_slot_dot(const RowRaw &R, const float *hrow, int q, const uint8_t *lds,
-                                               const TableLayout &TL) {
-  XChunk X;
-  load_x<QT>(hrow, X);
-  return group_sum_first<LPR>(dot_chunk<QT>(R, q, lds, TL, X));
-}
-
 template <int LPR, bool STAGE>
 __global__ void __launch_bounds__(256) k_down_acc(LayerArgs L, const float *__restrict__ h, int kprime,
                                                   const int32_t *__restrict__ ids, const float *__restrict__ w,

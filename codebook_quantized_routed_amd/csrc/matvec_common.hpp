@@ -58,40 +58,43 @@ __device__ __forceinline__ uint4 expand_row_f16(uint32_t c, uint32_t h0, uint32_
 // Builds the tables of the formats present from the compact rows (1 KB / 4 KB reads),
 // in two steps: tables_load issues the global loads (call it before the loads that wait
 // on HBM, so the table build does not queue behind them), tables_store expands into LDS
-// and synchronizes the workgroup.  Thread t expands rows t, t + blockDim, ...
-constexpr int kTableRowsPerThread = kIq1Rows / 256;  // for workgroups of >= 256 threads
+// and synchronizes the workgroup.  Loader t of n (by default every thread) expands
+// rows t, t + n, ...; t < 0 loads nothing.
+constexpr int kTableRowsPerThread = kIq1Rows / 256;  // for n >= 256 loaders
 
 struct TableRegs {
   uint32_t c2[kIq2Rows / 256];
   uint32_t c1[kTableRowsPerThread];
 };
 
-__device__ __forceinline__ TableRegs tables_load(const uint8_t *grids, int formats) {
+__device__ __forceinline__ TableRegs tables_load(const uint8_t *grids, int formats, int t = threadIdx.x,
+                                                 int n = blockDim.x) {
   TableRegs tr;
   const uint16_t *c2 = (const uint16_t *)(grids + kGridIq2CompactOff);
   const uint16_t *c1 = (const uint16_t *)(grids + kGridIq1CompactOff);
 #pragma unroll
   for (int i = 0; i < kIq2Rows / 256; i++) {
-    const int r = threadIdx.x + i * blockDim.x;
-    tr.c2[i] = (formats & MOE_Q_IQ2XS_LIKE) && r < kIq2Rows ? c2[r] : 0u;
+    const int r = t + i * n;
+    tr.c2[i] = (formats & MOE_Q_IQ2XS_LIKE) && t >= 0 && r < kIq2Rows ? c2[r] : 0u;
   }
 #pragma unroll
   for (int i = 0; i < kTableRowsPerThread; i++) {
-    const int r = threadIdx.x + i * blockDim.x;
-    tr.c1[i] = (formats & MOE_Q_IQ1M_LIKE) && r < kIq1Rows ? c1[r] : 0u;
+    const int r = t + i * n;
+    tr.c1[i] = (formats & MOE_Q_IQ1M_LIKE) && t >= 0 && r < kIq1Rows ? c1[r] : 0u;
   }
   return tr;
 }
 
-__device__ __forceinline__ void tables_store(const TableRegs &tr, int formats, const TableLayout &TL, uint8_t *lds) {
+__device__ __forceinline__ void tables_store(const TableRegs &tr, int formats, const TableLayout &TL, uint8_t *lds,
+                                             int t = threadIdx.x, int n = blockDim.x) {
   if (formats & MOE_Q_IQ2XS_LIKE) {
     const uint32_t h0 = f16_bits((float)kIq2SymVal[0]), h1 = f16_bits((float)kIq2SymVal[1]),
                    h2 = f16_bits((float)kIq2SymVal[2]);
     uint4 *rows = (uint4 *)(lds + TL.iq2h);
 #pragma unroll
     for (int i = 0; i < kIq2Rows / 256; i++) {
-      const int r = threadIdx.x + i * blockDim.x;
-      if (r < kIq2Rows) rows[r] = expand_row_f16(tr.c2[i], h0, h1, h2);
+      const int r = t + i * n;
+      if (t >= 0 && r < kIq2Rows) rows[r] = expand_row_f16(tr.c2[i], h0, h1, h2);
     }
     uint4 *masks = (uint4 *)(lds + TL.iq2m);
     for (int s = threadIdx.x; s < 128; s += blockDim.x) {
@@ -108,8 +111,8 @@ __device__ __forceinline__ void tables_store(const TableRegs &tr, int formats, c
     uint4 *rows = (uint4 *)(lds + TL.iq1h);
 #pragma unroll
     for (int i = 0; i < kTableRowsPerThread; i++) {
-      const int r = threadIdx.x + i * blockDim.x;
-      if (r < kIq1Rows) rows[r] = expand_row_f16(tr.c1[i], h0, h1, h2);
+      const int r = t + i * n;
+      if (t >= 0 && r < kIq1Rows) rows[r] = expand_row_f16(tr.c1[i], h0, h1, h2);
     }
   }
   __syncthreads();

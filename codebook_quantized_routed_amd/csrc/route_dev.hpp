@@ -1,0 +1,272 @@
+// Device functions of the router top-k and of the grouping of a few slots, shared by
+// the routing kernels and the fused decode-layer kernel.
+#pragma once
+#include "common.hpp"
+
+namespace moe {
+
+// Float -> u32 with the same order; every finite value maps above 0x007FFFFF, so 0 can
+// stand for "taken / no value".
+__device__ __forceinline__ uint32_t orderable(float f) {
+  uint32_t b = __float_as_uint(f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float from_orderable(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Wave-wide max / min of a u32 through DPP row shifts and row broadcasts (lane 63 ends
+// with the result), then read lane 63.  Lanes outside a shift's row take the identity.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false));  // row_shr:1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false));  // row_shr:2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false));  // row_shr:4
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false));  // row_shr:8
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  const int I = -1;  // 0xFFFFFFFF, identity of min
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(I, (int)v, 0x111, 0xf, 0xf, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(I, (int)v, 0x112, 0xf, 0xf, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(I, (int)v, 0x114, 0xf, 0xf, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(I, (int)v, 0x118, 0xf, 0xf, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(I, (int)v, 0x142, 0xa, 0xf, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(I, (int)v, 0x143, 0xc, 0xf, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Top-k of one token by one wave.  Lane l holds the logits of experts e = l + 64 i as
+// orderable keys, sorted in the lane (descending key, ascending id on ties).
+//
+// Fast path: tau = the k-th largest of the 64 lane maxima is a lower bound on the k-th
+// largest key (those k maxima are k keys >= tau), so every selected key is >= tau.
+// tau comes from a bitwise search over ballots; the few keys >= tau (about k to 2k for
+// N(0,1) logits) are packed into LDS, one per lane, and each is ranked against the
+// others by (key descending, id ascending) through lane reads; rank < k is selected.
+// If more than 64 keys reach tau (heavy ties), the selection falls back to k rounds of
+// a wave-wide arg-max over the lanes' sorted lists.  Both give the same result.
+// Outputs: ids / w (global, skipped when ids is null) and the optional copies.
+constexpr int kCand = 64;
+
+struct TopkLds {
+  uint32_t cand_key[kCand];
+  int cand_id[kCand];
+  uint32_t sel_key[MOE_MAX_K];
+  int sel_id[MOE_MAX_K];
+};
+
+template <int VPL>
+__device__ __forceinline__ void topk_select_rounds(uint32_t (&key)[VPL], int (&eid)[VPL], int k, TopkLds &S) {
+  const int lane = threadIdx.x & 63;
+  for (int j = 0; j < k; j++) {
+    const uint32_t m = wave_max_u32(key[0]);
+    const uint64_t hit = __ballot(key[0] == m);
+    int id;
+    if (__popcll(hit) == 1)
+      id = __builtin_amdgcn_readlane(eid[0], __ffsll((unsigned long long)hit) - 1);
+    else
+      id = (int)wave_min_u32(key[0] == m ? (uint32_t)eid[0] : 0xFFFFFFFFu);
+    if (key[0] == m && eid[0] == id) {
+#pragma unroll
+      for (int i = 0; i + 1 < VPL; i++) {
+        key[i] = key[i + 1];
+        eid[i] = eid[i + 1];
+      }
+      key[VPL - 1] = 0u;
+    }
+    if (lane == 0) {
+      S.sel_key[j] = m;
+      S.sel_id[j] = id;
+    }
+  }
+}
+
+// Number of set bits of m in the lanes below this one.
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+}
+
+// The token's logits as lane l holds them (experts l + 64 i); every lane loads (clamped
+// index), so the loads are issued back to back.
+template <int VPL>
+struct TopkVals {
+  float v[VPL];
+};
+
+template <int VPL>
+__device__ __forceinline__ TopkVals<VPL> topk_load(const float *__restrict__ l, int E) {
+  const int lane = threadIdx.x & 63;
+  TopkVals<VPL> t;
+#pragma unroll
+  for (int i = 0; i < VPL; i++) t.v[i] = l[min(i * 64 + lane, E - 1)];
+  return t;
+}
+
+template <int VPL>
+__device__ __forceinline__ void topk_select(const TopkVals<VPL> &tv, int E, int k, int add_shared,
+                                            int32_t *__restrict__ ids, float *__restrict__ w, int32_t *ids_copy,
+                                            float *w_copy, TopkLds &S) {
+  const int lane = threadIdx.x & 63;
+  uint32_t key[VPL];
+  int eid[VPL];
+  const float *lv = tv.v;
+#pragma unroll
+  for (int i = 0; i < VPL; i++) {
+    const int e = i * 64 + lane;
+    key[i] = e < E ? orderable(lv[i]) : 0u;
+    eid[i] = e;
+  }
+#pragma unroll
+  for (int i = 1; i < VPL; i++)
+#pragma unroll
+    for (int j = i; j > 0; j--) {
+      const bool swap = key[j] > key[j - 1];  // equal keys keep the lower id first
+      const uint32_t tk = swap ? key[j - 1] : key[j];
+      const int te = swap ? eid[j - 1] : eid[j];
+      key[j - 1] = swap ? key[j] : key[j - 1];
+      eid[j - 1] = swap ? eid[j] : eid[j - 1];
+      key[j] = tk;
+      eid[j] = te;
+    }
+  // tau: the largest t with at least k lane maxima >= t (the set of such t is closed
+  // downwards, so it is found bit by bit from the top).  At least k lanes hold a key.
+  uint32_t tau = 0u;
+  for (int b = 31; b >= 0; b--) {
+    const uint32_t c = tau | (1u << b);
+    if (__popcll(__ballot(key[0] >= c)) >= k) tau = c;
+  }
+  // candidates: keys >= tau (each lane's come first in its sorted list); invalid keys
+  // are 0 < tau.  Position = candidates of lower lanes + index in the lane.
+  int base = 0, total = 0;
+#pragma unroll
+  for (int i = 0; i < VPL; i++) {
+    const uint64_t m = __ballot(key[i] >= tau);
+    base += lanes_below(m);
+    total += __popcll(m);
+  }
+  if (total <= kCand) {
+#pragma unroll
+    for (int i = 0; i < VPL; i++)
+      if (key[i] >= tau) {
+        S.cand_key[base + i] = key[i];
+        S.cand_id[base + i] = eid[i];
+      }
+    __builtin_amdgcn_wave_barrier();
+    const uint32_t ck = lane < total ? S.cand_key[lane] : 0u;
+    const int cid = lane < total ? S.cand_id[lane] : 0x7FFFFFFF;
+    int rank = 0;
+    for (int j = 0; j < total; j++) {
+      const uint32_t ok = (uint32_t)__builtin_amdgcn_readlane((int)ck, j);
+      const int oid = __builtin_amdgcn_readlane(cid, j);
+      rank += (ok > ck || (ok == ck && oid < cid)) ? 1 : 0;
+    }
+    if (lane < total && rank < k) {
+      S.sel_key[rank] = ck;
+      S.sel_id[rank] = cid;
+    }
+  } else {
+    topk_select_rounds<VPL>(key, eid, k, S);
+  }
+  __builtin_amdgcn_wave_barrier();
+  // weights: lane j exponentiates selection j; the sum runs over j in order
+  float ex = 0.0f, top = 0.0f;
+  int myid = 0;
+  if (lane < k) {
+    myid = S.sel_id[lane];
+    top = from_orderable(S.sel_key[0]);
+    ex = expf(__fsub_rn(from_orderable(S.sel_key[lane]), top));
+  }
+  float sum = 0.0f;
+  for (int j = 0; j < k; j++) sum = __fadd_rn(sum, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j)));
+  if (lane < k) {
+    const float wl = __fdiv_rn(ex, sum);
+    if (ids) {
+      ids[lane] = myid;
+      w[lane] = wl;
+    }
+    if (ids_copy) ids_copy[lane] = myid;
+    if (w_copy) w_copy[lane] = wl;
+  }
+  if (add_shared && lane == k) {
+    if (ids) {
+      ids[k] = E;
+      w[k] = 1.0f;
+    }
+    if (ids_copy) ids_copy[k] = E;
+    if (w_copy) w_copy[k] = 1.0f;
+  }
+}
+
+template <int VPL>
+__device__ __forceinline__ void topk_wave(const float *__restrict__ l, int E, int k, int add_shared,
+                                          int32_t *__restrict__ ids, float *__restrict__ w, int32_t *ids_copy,
+                                          float *w_copy, TopkLds &S) {
+  topk_select<VPL>(topk_load<VPL>(l, E), E, k, add_shared, ids, w, ids_copy, w_copy, S);
+}
+
+// Grouping of at most 64 slots (decode): the same outputs as group_block, computed
+// from lane reads of the slot ids, with no LDS traffic and no barrier.  Wave 0 ranks
+// every slot among the others (stable: by id, then slot index) and writes the work
+// records; every thread e counts the slots below and at its id.
+constexpr int kTinySlots = 64;
+
+__device__ inline void group_tiny(const int32_t *ids_l, int n, int n_ids, int32_t *__restrict__ counts,
+                           int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_slot,
+                           int32_t *__restrict__ slot_pos, WorkRec *__restrict__ work) {
+  const int lane = threadIdx.x & 63;
+  const int my = lane < n ? ids_l[lane] : 0x7FFFFFFF;
+  if (threadIdx.x < 64) {
+    int rank = 0, same = 0, first = 1;
+    for (int j = 0; j < n; j++) {
+      const int o = __builtin_amdgcn_readlane(my, j);
+      rank += (o < my || (o == my && j < lane)) ? 1 : 0;
+      same += o == my ? 1 : 0;
+      first &= (o == my && j < lane) ? 0 : 1;
+    }
+    const bool wide = same > MOE_MATVEC_MAX_TOKENS;
+    const uint64_t firsts = __ballot(lane < n && first);
+    const uint64_t wides = __ballot(lane < n && first && wide);
+    // first set: distinct experts below mine; tiles: the tiles of wide experts below mine
+    int below = 0, tiles_below = 0, n_tiles = 0;
+    for (int j = 0; j < n; j++) {
+      const int oj = __builtin_amdgcn_readlane(my, j), sj = __builtin_amdgcn_readlane(same, j);
+      const bool fj = (firsts >> j) & 1u, wj = (wides >> j) & 1u;
+      const int tj = (sj + MOE_MFMA_TILE_TOKENS - 1) / MOE_MFMA_TILE_TOKENS;
+      if (fj && oj < my) {
+        if (wj)
+          tiles_below += tj;
+        else
+          below++;
+      }
+      n_tiles += wj ? tj : 0;
+    }
+    if (lane < n) {
+      sorted_slot[rank] = lane;
+      slot_pos[lane] = rank;
+      if (first && !wide) work[1 + below] = WorkRec{my, rank, rank + same, lane};
+      if (first && wide)
+        for (int p = 0; p < same; p += MOE_MFMA_TILE_TOKENS)
+          work[n_ids + 1 + tiles_below + p / MOE_MFMA_TILE_TOKENS] =
+              WorkRec{my, rank + p, rank + min(same, p + MOE_MFMA_TILE_TOKENS), 0};
+    }
+    if (lane == 0) {
+      offsets[n_ids] = n;
+      const int n_wide = (int)__popcll(wides);
+      work[0] = WorkRec{(int)__popcll(firsts) - n_wide, n, n_wide, n_tiles};
+    }
+  }
+  for (int e = threadIdx.x; e < n_ids; e += blockDim.x) {
+    int below = 0, at = 0;
+    for (int j = 0; j < n; j++) {
+      const int o = __builtin_amdgcn_readlane(my, j);
+      below += o < e ? 1 : 0;
+      at += o == e ? 1 : 0;
+    }
+    counts[e] = at;
+    offsets[e] = below;
+  }
+}
+
+}  // namespace moe

@@ -200,6 +200,30 @@ moe_status moe_expert_down_accumulate_q(const moe_layer *layer, const float *d_h
                                         const int32_t *d_ids, const float *d_w, const int32_t *d_slot_pos,
                                         float *d_acc, hipStream_t stream);
 
+/* Workspace of moe_layer_decode_q: MOE_DECODE_SYNC_BYTES of synchronisation words, then h. */
+#define MOE_DECODE_SYNC_BYTES 4352
+size_t moe_decode_workspace_bytes(int32_t kprime, int32_t inter);
+
+/* One decode step of a layer for one token, in one launch ("Red Metal dev8", steps 3-6:
+ * route, run every selected expert, accumulate; only the layer output leaves the
+ * call).  Computes exactly what moe_route_group (T = 1), moe_expert_gateup_q and
+ * moe_expert_down_accumulate_q compute, bit for bit, and writes the same outputs:
+ * d_ids, d_w [kprime]; d_counts, d_offsets, d_sorted_slot, d_slot_pos, d_work as
+ * moe_route_group; d_acc [hidden] (in/out).  d_logits [E] or NULL (explicit d_ids /
+ * d_w inputs, as in moe_route_group); d_x [hidden].  kprime = k + add_shared;
+ * add_shared must equal the layer's has_shared.
+ * d_ws: moe_decode_workspace_bytes(kprime, inter) bytes; its first MOE_DECODE_SYNC_BYTES
+ * must be zero before the first call, and each call leaves them ready for the next
+ * (calls that share a workspace must not overlap).  The uint32 at byte 128 becomes
+ * nonzero if the kernel's grid barrier ever timed out, which can only happen when other
+ * kernels hold compute units while this one runs; the results of that call are then
+ * undefined.
+ * Limits: hidden == 2048, inter == 256 or 512, E <= 512. */
+moe_status moe_layer_decode_q(const moe_layer *layer, const float *d_logits, const float *d_x, int32_t k,
+                              int32_t add_shared, int32_t *d_ids, float *d_w, int32_t *d_counts, int32_t *d_offsets,
+                              int32_t *d_sorted_slot, int32_t *d_slot_pos, int32_t *d_work, float *d_acc, void *d_ws,
+                              size_t ws_bytes, hipStream_t stream);
+
 /* Weighted accumulation ("Red Metal dev8", step 5: accumulator += router_weight *
  * expert_output after each expert).  d_acc[t][c] (in/out) gets w * y added for each
  * slot of token t, taken in ascending expert id (the shared expert, id E, last), as

@@ -43,6 +43,7 @@ def test_binding_constants_match_header():
     assert int(defs["MOE_MAX_IDS"]) == moe.MAX_IDS
     assert int(defs["MOE_MATVEC_MAX_TOKENS"]) == moe.MATVEC_MAX_TOKENS
     assert int(defs["MOE_MFMA_TILE_TOKENS"]) == moe.MFMA_TILE_TOKENS
+    assert moe.decode_workspace_bytes(11, 512) - 11 * 512 * 4 == int(defs["MOE_DECODE_SYNC_BYTES"])
 
 
 def test_version_strings_sizes():
@@ -147,3 +148,24 @@ def test_other_rejects():
     assert lib.moe_rmsnorm(A, 1, 2048, float("nan"), A, None) == -2
     assert lib.moe_grids_expand(A, None, A, None) == -1
     assert lib.moe_grids_expand(A, A, MIS, None) == -4
+
+
+def test_layer_decode_rejects():
+    d = layer()
+    ws_need = moe.decode_workspace_bytes(11, 512)
+    assert ws_need == 4352 + 11 * 512 * 4
+
+    def call(d=d, logits=A, x=A, k=10, add_shared=1, ws=A, ws_bytes=ws_need, acc=A):
+        return lib.moe_layer_decode_q(C.byref(d), logits, x, k, add_shared, A, A, A, A, A, A, A, acc, ws, ws_bytes,
+                                      None)
+    assert lib.moe_layer_decode_q(None, A, A, 10, 1, A, A, A, A, A, A, A, A, A, ws_need, None) == -1
+    assert call(x=None) == -1
+    assert call(ws=None) == -1
+    assert call(logits=MIS) == -4
+    assert call(acc=MIS) == -4
+    assert call(k=0) == -2
+    assert call(k=17) == -2
+    assert call(add_shared=0) == -2                     # must match the layer's shared expert
+    assert call(d=layer(hidden=1024, n_experts=512)) == -2
+    assert call(d=layer(inter=1024)) == -2
+    assert call(ws_bytes=ws_need - 4) == -5

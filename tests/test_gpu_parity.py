@@ -171,6 +171,7 @@ LAYER_CASES = {
     "dense_iq1_t40_shared": ([(IQ1, 8)], 2048, 512, 8, 1, 40, 3, 0.0),
     "mixed_t128_zipf": ([(IQ2, 32), (IQ1, 32)], 2048, 512, 64, 0, 128, 10, 1.1),
     "mixed_h512_i1024_t48": ([(IQ1, 6), (IQ2, 6)], 512, 1024, 12, 1, 48, 2, 0.0),
+    "decode_mixed_i256_shared": ([(IQ2, 20), (IQ1, 12)], 2048, 256, 32, 1, 1, 6, 0.0),
 }
 
 
@@ -259,6 +260,52 @@ def test_prefill_field_shape_sampled(grids, ogrids, zipf):
     for t in sample:
         ref = O.moe_layer(tab, ogrids, x[t:t + 1], k, False, logits=lg[t:t + 1])
         assert_rows_close(g["acc"][t], ref["acc"][0], f"prefill token {t}")
+
+
+FUSED_CASES = ["decode_iq2_top10_shared", "tiny16_top4_iq2", "mixed_h2048_t24_zipf", "decode_mixed_i256_shared"]
+
+
+@pytest.mark.parametrize("name", FUSED_CASES)
+def test_fused_decode_matches_three_calls(layers, name):
+    """moe_layer_decode_q (one launch) writes the same bits as moe_route_group +
+    moe_expert_gateup_q + moe_expert_down_accumulate_q, on consecutive calls that share
+    one workspace, with router logits and with an explicit selection."""
+    banks, H, I, E, shared, T, k, zipf = LAYER_CASES[name]
+    sl, tab, dl = layers(name)
+    kp = k + shared
+    ws = torch.zeros(moe.decode_workspace_bytes(kp, I) // 4, dtype=torch.int32, device="cuda")
+    for call in range(3):
+        log(f"fused decode {name} call {call}")
+        x = synth.activations(1, H, tag=f"F/{name}/{call}/x")
+        acc0 = synth.activations(1, H, tag=f"F/{name}/{call}/acc")
+        if call < 2:
+            lg = synth.logits(1, E, tag=f"F/{name}/{call}/l", zipf_alpha=zipf)
+            ref = run_layer(dl, x, k, shared, logits=lg, acc=acc0, decode=True)
+            sel = None
+        else:  # explicit experts and weights
+            lg = None
+            ids = np.argsort(synth.u64(3, f"F/{name}/ids", E), kind="stable")[:k].astype(np.int32)[None, :]
+            wts = synth.uniform(3, f"F/{name}/w", k).astype(np.float32)[None, :]
+            ref = run_layer(dl, x, k, shared, ids=ids, w=wts, acc=acc0, decode=True)
+            sel = (ids, wts)
+        r = Run(1, E, k, shared, H, I)
+        if sel is not None:
+            r.ids[:, :k] = dev(sel[0])
+            r.w[:, :k] = dev(sel[1])
+        acc_d = dev(acc0.astype(np.float32))
+        moe.layer_decode_q(dl.desc, None if lg is None else dev(lg), dev(x), k, shared, r.ids, r.w, r.counts,
+                           r.offsets, r.sorted_slot, r.slot_pos, r.work, acc_d, ws)
+        got = r.host()
+        for key in ("ids", "w", "counts", "offsets", "sorted_slot", "slot_pos", "work"):
+            np.testing.assert_array_equal(got[key], ref[key], err_msg=key)
+        assert np.array_equal(acc_d.cpu().numpy().view(np.uint32), ref["acc"].view(np.uint32))
+        sync = ws[:64].cpu().numpy().view(np.uint32)
+        rounds = int(sync[0]) | (int(sync[1]) << 32)     # top counter: one round of groups per call
+        if call == 0:
+            groups = rounds
+            assert groups > 0
+        assert rounds == (call + 1) * groups
+        assert sync[32] == 0                             # no barrier time-out
 
 
 def test_permutation_invariance_and_determinism(layers):
