@@ -166,7 +166,7 @@ LAYER_CASES = {
     "small_mixed_ragged": ([(IQ2, 12), (IQ1, 20)], 512, 256, 32, 1, 19, 6, 0.0),
     "small_mixed_many_tokens": ([(IQ1, 8), (IQ2, 8)], 256, 512, 16, 0, 96, 5, 0.0),
     "mixed_h2048_t24_zipf": ([(IQ2, 24), (IQ1, 40)], 2048, 512, 64, 1, 24, 8, 1.0),
-    # many tokens per expert: the matrix-core path, one and two passes of 32 columns
+    # many tokens per expert: the matrix-core path, one to three 16-token tiles per expert
     "dense_iq2_t64": ([(IQ2, 16)], 2048, 512, 16, 0, 64, 4, 0.0),
     "dense_iq1_t40_shared": ([(IQ1, 8)], 2048, 512, 8, 1, 40, 3, 0.0),
     "mixed_t128_zipf": ([(IQ2, 32), (IQ1, 32)], 2048, 512, 64, 0, 128, 10, 1.1),
