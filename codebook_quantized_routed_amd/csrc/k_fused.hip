@@ -28,7 +28,7 @@
 
 namespace moe {
 
-constexpr int kFusedWaves = 8;
+constexpr int kFusedWaves = 12;
 constexpr int kDownWaves = kFusedWaves - 1;  // the last wave polls the grid barrier
 constexpr int kFusedMaxSlots = MOE_MAX_K + 1;
 constexpr int kFusedSlotsPerWave = (kFusedMaxSlots + kDownWaves - 1) / kDownWaves;
@@ -60,7 +60,7 @@ struct FusedLds {
 };
 
 __host__ __device__ inline size_t fused_stage_floats(int lpr) {
-  return (size_t)kFusedWaves * kFusedSlotsPerWave * lpr * kChunkPad;
+  return (size_t)kFusedWaves * lpr * kChunkPad;
 }
 
 // Grid-wide barrier over n workgroups, in two halves so a workgroup can work between
@@ -111,7 +111,7 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
   float *h = (float *)(sync + 1);
   const int formats = layer_formats(L);
   const TableLayout TL = table_layout(formats);
-  float *hs = (float *)(lds + TL.bytes) + wave * kFusedSlotsPerWave * HS;
+  float *hs = (float *)(lds + TL.bytes) + wave * HS;
   // wave 0's logits are the first loads of the kernel; the table rows are loaded by
   // waves 1.. while wave 0 routes (vector loads complete in order)
   TopkVals<8> tv;
@@ -150,44 +150,30 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
   }
   __syncthreads();
 
-  // ---- 2. gate / up items: activations, then the first two items, issued before
-  // anything waits
+  // ---- 2. gate / up items dealt over the grid's waves (at most one per wave when the
+  // grid has as many waves as items): the activations and the wave's first item are
+  // issued before anything waits; later items are issued one at a time
   X32 X;
   load_x32(x + 32 * lane, X);
   const int q = lane, lq = lane % LPR, sub = lane / LPR;
   const int ipe = I / kWideRows, n_items = kprime * ipe, nw = gridDim.x * kFusedWaves;
-  int item = blockIdx.x * kFusedWaves + wave;
-  WideItem It, It2;
+  const int item0 = blockIdx.x * kFusedWaves + wave;
+  WideItem It;
   int cur_tok = 0;
   bool gs_ok = false;
-  const bool have1 = item < n_items, have2 = item + nw < n_items;
-  if (have1) {
+  auto issue = [&](int item) {
     const int p = item / ipe, slot = uniform(S.slot_at[p]);
     It.W = WorkRec{uniform(S.ids[slot]), p, p + 1, slot};
     wide_issue(L, It, item - p * ipe, q);
-  }
-  if (have2) {
-    const int it2 = item + nw, p = it2 / ipe, slot = uniform(S.slot_at[p]);
-    It2.W = WorkRec{uniform(S.ids[slot]), p, p + 1, slot};
-    wide_issue(L, It2, it2 - p * ipe, q);
-  }
+  };
+  if (item0 < n_items) issue(item0);
   tables_store(tr, formats, TL, lds, threadIdx.x - 64, blockDim.x - 64);
-  if (have1) {
+  for (int item = item0; item < n_items; item += nw) {
+    if (item != item0) issue(item);
     if (It.qt == MOE_Q_IQ2XS_LIKE)
       wide_run<MOE_Q_IQ2XS_LIKE, true>(L, It, X, cur_tok, gs_ok, q, kprime, x, sorted_slot, lds, TL, h);
     else
       wide_run<MOE_Q_IQ1M_LIKE, true>(L, It, X, cur_tok, gs_ok, q, kprime, x, sorted_slot, lds, TL, h);
-  }
-  for (item += nw; item < n_items; item += nw) {
-    if (item != blockIdx.x * kFusedWaves + wave + nw) {  // the second item was issued above
-      const int p = item / ipe, slot = uniform(S.slot_at[p]);
-      It2.W = WorkRec{uniform(S.ids[slot]), p, p + 1, slot};
-      wide_issue(L, It2, item - p * ipe, q);
-    }
-    if (It2.qt == MOE_Q_IQ2XS_LIKE)
-      wide_run<MOE_Q_IQ2XS_LIKE, true>(L, It2, X, cur_tok, gs_ok, q, kprime, x, sorted_slot, lds, TL, h);
-    else
-      wide_run<MOE_Q_IQ1M_LIKE, true>(L, It2, X, cur_tok, gs_ok, q, kprime, x, sorted_slot, lds, TL, h);
   }
 
   // ---- 3. every h row written before any is read: each wave's h stores complete, then
@@ -201,62 +187,59 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
   if (poller) target = barrier_arrive(sync, gridDim.x);
   const int tiles = H / RPP;
   int tile = blockIdx.x;
-  RowRaw Rd[kFusedSlotsPerWave];
-  int dqt[kFusedSlotsPerWave];
-#pragma unroll
-  for (int i = 0; i < kFusedSlotsPerWave; i++) {
-    const int j = wave + kDownWaves * i;
-    dqt[i] = 0;
-    if (wave < kDownWaves && j < kprime && tile < tiles) {
-      const int e = uniform(S.ids[j]);
-      const BankArgs &B = bank_of(L, e);
-      const QMat Wd = expert_mat(B, e, kDown, H, I);
-      dqt[i] = B.qtype;
-      Rd[i] = B.qtype == MOE_Q_IQ2XS_LIKE ? load_row<MOE_Q_IQ2XS_LIKE>(Wd, I, tile * RPP + sub, lq)
-                                          : load_row<MOE_Q_IQ1M_LIKE>(Wd, I, tile * RPP + sub, lq);
-    }
+  const bool down_wave = wave < kDownWaves;
+  RowRaw Rd0;  // the wave's first slot (slot = wave) of the first block, loaded early
+  int dqt0 = 0;
+  if (down_wave && wave < kprime && tile < tiles) {
+    const int e = uniform(S.ids[wave]);
+    const BankArgs &B = bank_of(L, e);
+    const QMat Wd = expert_mat(B, e, kDown, H, I);
+    dqt0 = B.qtype;
+    Rd0 = B.qtype == MOE_Q_IQ2XS_LIKE ? load_row<MOE_Q_IQ2XS_LIKE>(Wd, I, tile * RPP + sub, lq)
+                                      : load_row<MOE_Q_IQ1M_LIKE>(Wd, I, tile * RPP + sub, lq);
   }
   float acc_in = 0.0f;
   if (threadIdx.x < RPP && tile < tiles) acc_in = acc[tile * RPP + threadIdx.x];
   if (poller) barrier_wait(sync, target);
   __syncthreads();
 
-  // ---- 4. down + accumulation, block by block of RPP output rows
+  // ---- 4. down + accumulation, block by block of RPP output rows; a wave takes slots
+  // wave, wave + kDownWaves, ... one after the other
   for (bool first = true; tile < tiles; tile += gridDim.x, first = false) {
-#pragma unroll
+#pragma unroll 1
     for (int i = 0; i < kFusedSlotsPerWave; i++) {
       const int j = wave + kDownWaves * i;
-      if (wave < kDownWaves && j < kprime) {
-        if (!first) {
-          const int e = uniform(S.ids[j]);
-          const BankArgs &B = bank_of(L, e);
-          const QMat Wd = expert_mat(B, e, kDown, H, I);
-          Rd[i] = dqt[i] == MOE_Q_IQ2XS_LIKE ? load_row<MOE_Q_IQ2XS_LIKE>(Wd, I, tile * RPP + sub, lq)
-                                             : load_row<MOE_Q_IQ1M_LIKE>(Wd, I, tile * RPP + sub, lq);
-        }
-        // the slot's h row into the wave's LDS area (64-float chunks padded to kChunkPad
-        // floats), read with agent-scope loads: other workgroups wrote it
-        const uint32_t *src = (const uint32_t *)(h + (size_t)S.pos_of[j] * I);
-        for (int f = lane; f < LPR * 16; f += 64) {
-          uint4 v;
-          v.x = __hip_atomic_load(src + 4 * f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          v.y = __hip_atomic_load(src + 4 * f + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          v.z = __hip_atomic_load(src + 4 * f + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          v.w = __hip_atomic_load(src + 4 * f + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          *(uint4 *)(hs + i * HS + (f >> 4) * kChunkPad + (f & 15) * 4) = v;
-        }
+      if (!down_wave || j >= kprime) break;
+      RowRaw R;
+      int qt;
+      if (first && i == 0) {
+        R = Rd0;
+        qt = dqt0;
+      } else {
+        const int e = uniform(S.ids[j]);
+        const BankArgs &B = bank_of(L, e);
+        const QMat Wd = expert_mat(B, e, kDown, H, I);
+        qt = B.qtype;
+        R = qt == MOE_Q_IQ2XS_LIKE ? load_row<MOE_Q_IQ2XS_LIKE>(Wd, I, tile * RPP + sub, lq)
+                                   : load_row<MOE_Q_IQ1M_LIKE>(Wd, I, tile * RPP + sub, lq);
       }
-    }
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int i = 0; i < kFusedSlotsPerWave; i++) {
-      const int j = wave + kDownWaves * i;
-      if (wave < kDownWaves && j < kprime) {
-        const float *hrow = hs + i * HS + lq * kChunkPad;
-        const float v = dqt[i] == MOE_Q_IQ2XS_LIKE ? down_slot_dot<MOE_Q_IQ2XS_LIKE, LPR>(Rd[i], hrow, lq, lds, TL)
-                                                   : down_slot_dot<MOE_Q_IQ1M_LIKE, LPR>(Rd[i], hrow, lq, lds, TL);
-        if (lq == 0) S.ydot[j][sub] = v;
+      // the slot's h row into the wave's LDS area (64-float chunks padded to kChunkPad
+      // floats), read with agent-scope loads: other workgroups wrote it
+      const uint32_t *src = (const uint32_t *)(h + (size_t)S.pos_of[j] * I);
+      for (int f = lane; f < LPR * 16; f += 64) {
+        uint4 v;
+        v.x = __hip_atomic_load(src + 4 * f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v.y = __hip_atomic_load(src + 4 * f + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v.z = __hip_atomic_load(src + 4 * f + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v.w = __hip_atomic_load(src + 4 * f + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *(uint4 *)(hs + (f >> 4) * kChunkPad + (f & 15) * 4) = v;
       }
+      __builtin_amdgcn_wave_barrier();
+      const float *hrow = hs + lq * kChunkPad;
+      const float v = qt == MOE_Q_IQ2XS_LIKE ? down_slot_dot<MOE_Q_IQ2XS_LIKE, LPR>(R, hrow, lq, lds, TL)
+                                             : down_slot_dot<MOE_Q_IQ1M_LIKE, LPR>(R, hrow, lq, lds, TL);
+      if (lq == 0) S.ydot[j][sub] = v;
+      __builtin_amdgcn_wave_barrier();  // the staging area is reused by the next slot
     }
     __syncthreads();
     if (threadIdx.x < RPP) {

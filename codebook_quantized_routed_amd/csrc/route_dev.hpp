@@ -38,7 +38,7 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
 }
 
 // Top-k of one token by one wave.  Lane l holds the logits of experts e = l + 64 i as
-// orderable keys, sorted in the lane (descending key, ascending id on ties).
+// orderable keys (no order within the lane).
 //
 // Fast path: tau = the k-th largest of the 64 lane maxima is a lower bound on the k-th
 // largest key (those k maxima are k keys >= tau), so every selected key is >= tau.
@@ -46,7 +46,7 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
 // N(0,1) logits) are packed into LDS, one per lane, and each is ranked against the
 // others by (key descending, id ascending) through lane reads; rank < k is selected.
 // If more than 64 keys reach tau (heavy ties), the selection falls back to k rounds of
-// a wave-wide arg-max over the lanes' sorted lists.  Both give the same result.
+// a wave-wide arg-max.  Both give the same result.
 // Outputs: ids / w (global, skipped when ids is null) and the optional copies.
 constexpr int kCand = 64;
 
@@ -57,25 +57,24 @@ struct TopkLds {
   int sel_id[MOE_MAX_K];
 };
 
+// k rounds of: the largest remaining key, ties to the lowest expert id; the winner is
+// removed (key 0 = taken / no value).
 template <int VPL>
-__device__ __forceinline__ void topk_select_rounds(uint32_t (&key)[VPL], int (&eid)[VPL], int k, TopkLds &S) {
+__device__ __forceinline__ void topk_select_rounds(uint32_t (&key)[VPL], int k, TopkLds &S) {
   const int lane = threadIdx.x & 63;
   for (int j = 0; j < k; j++) {
-    const uint32_t m = wave_max_u32(key[0]);
-    const uint64_t hit = __ballot(key[0] == m);
-    int id;
-    if (__popcll(hit) == 1)
-      id = __builtin_amdgcn_readlane(eid[0], __ffsll((unsigned long long)hit) - 1);
-    else
-      id = (int)wave_min_u32(key[0] == m ? (uint32_t)eid[0] : 0xFFFFFFFFu);
-    if (key[0] == m && eid[0] == id) {
+    uint32_t lmax = key[0];
 #pragma unroll
-      for (int i = 0; i + 1 < VPL; i++) {
-        key[i] = key[i + 1];
-        eid[i] = eid[i + 1];
-      }
-      key[VPL - 1] = 0u;
-    }
+    for (int i = 1; i < VPL; i++) lmax = max(lmax, key[i]);
+    const uint32_t m = wave_max_u32(lmax);
+    uint32_t lid = 0xFFFFFFFFu;  // the lane's lowest id holding m
+#pragma unroll
+    for (int i = VPL - 1; i >= 0; i--)
+      if (key[i] == m) lid = (uint32_t)(i * 64 + lane);
+    const int id = (int)wave_min_u32(lid);
+#pragma unroll
+    for (int i = 0; i < VPL; i++)
+      if (i * 64 + lane == id) key[i] = 0u;
     if (lane == 0) {
       S.sel_key[j] = m;
       S.sel_id[j] = id;
@@ -109,49 +108,33 @@ __device__ __forceinline__ void topk_select(const TopkVals<VPL> &tv, int E, int 
                                             int32_t *__restrict__ ids, float *__restrict__ w, int32_t *ids_copy,
                                             float *w_copy, TopkLds &S) {
   const int lane = threadIdx.x & 63;
-  uint32_t key[VPL];
-  int eid[VPL];
-  const float *lv = tv.v;
+  uint32_t key[VPL], lmax = 0u;
 #pragma unroll
   for (int i = 0; i < VPL; i++) {
-    const int e = i * 64 + lane;
-    key[i] = e < E ? orderable(lv[i]) : 0u;
-    eid[i] = e;
+    key[i] = i * 64 + lane < E ? orderable(tv.v[i]) : 0u;
+    lmax = max(lmax, key[i]);
   }
-#pragma unroll
-  for (int i = 1; i < VPL; i++)
-#pragma unroll
-    for (int j = i; j > 0; j--) {
-      const bool swap = key[j] > key[j - 1];  // equal keys keep the lower id first
-      const uint32_t tk = swap ? key[j - 1] : key[j];
-      const int te = swap ? eid[j - 1] : eid[j];
-      key[j - 1] = swap ? key[j] : key[j - 1];
-      eid[j - 1] = swap ? eid[j] : eid[j - 1];
-      key[j] = tk;
-      eid[j] = te;
-    }
   // tau: the largest t with at least k lane maxima >= t (the set of such t is closed
   // downwards, so it is found bit by bit from the top).  At least k lanes hold a key.
   uint32_t tau = 0u;
   for (int b = 31; b >= 0; b--) {
     const uint32_t c = tau | (1u << b);
-    if (__popcll(__ballot(key[0] >= c)) >= k) tau = c;
+    if (__popcll(__ballot(lmax >= c)) >= k) tau = c;
   }
-  // candidates: keys >= tau (each lane's come first in its sorted list); invalid keys
-  // are 0 < tau.  Position = candidates of lower lanes + index in the lane.
-  int base = 0, total = 0;
+  // candidates: keys >= tau (invalid keys are 0 < tau), packed in (i, lane) order
+  int pos[VPL], total = 0;
 #pragma unroll
   for (int i = 0; i < VPL; i++) {
     const uint64_t m = __ballot(key[i] >= tau);
-    base += lanes_below(m);
-    total += __popcll(m);
+    pos[i] = total + lanes_below(m);
+    total += (int)__popcll(m);
   }
   if (total <= kCand) {
 #pragma unroll
     for (int i = 0; i < VPL; i++)
       if (key[i] >= tau) {
-        S.cand_key[base + i] = key[i];
-        S.cand_id[base + i] = eid[i];
+        S.cand_key[pos[i]] = key[i];
+        S.cand_id[pos[i]] = i * 64 + lane;
       }
     __builtin_amdgcn_wave_barrier();
     const uint32_t ck = lane < total ? S.cand_key[lane] : 0u;
@@ -167,7 +150,7 @@ __device__ __forceinline__ void topk_select(const TopkVals<VPL> &tv, int E, int 
       S.sel_id[rank] = cid;
     }
   } else {
-    topk_select_rounds<VPL>(key, eid, k, S);
+    topk_select_rounds<VPL>(key, k, S);
   }
   __builtin_amdgcn_wave_barrier();
   // weights: lane j exponentiates selection j; the sum runs over j in order
