@@ -36,19 +36,24 @@ constexpr int kSpinLimit = 1 << 20;  // polls of about 1 us: about a second
 
 // Workspace of the fused call: the barrier words, then h [kprime][inter] fp32.  The
 // barrier is two-level: workgroup g counts on the counter of its group g / kBarGroup,
-// the last arrival of a group counts on the top counter.  Counters are monotonic over
-// all calls (a call completes a whole round of each) and sit in separate 128-byte
-// lines; error is set if a wait timed out.
+// the last arrival of a group counts on the top counter, and the arrival that completes
+// the top count publishes it in the release word, which the waiters poll (polls on the
+// counters' own lines would slow the atomics that update them).  Counters and release
+// are monotonic over all calls; every call on a device launches the same number of
+// workgroups, so each call completes exactly one round of every counter.  The counters
+// sit in separate 128-byte lines; error is set if a wait timed out.
 constexpr int kBarGroup = 16;
 constexpr int kBarGroups = 32;  // up to 512 workgroups
 struct FusedSync {
   uint64_t top, pad0[15];
-  uint32_t error, pad1[31];
+  uint32_t error, pad1[15];
+  uint64_t release, pad2[7];
   struct Line {
     uint64_t count, pad[15];
   } group[kBarGroups];
 };
 static_assert(sizeof(FusedSync) == 4352, "h follows the barrier words");
+static_assert(offsetof(FusedSync, error) == 128 && offsetof(FusedSync, release) == 192, "documented offsets");
 
 struct FusedLds {
   TopkLds topk;
@@ -69,21 +74,25 @@ __host__ __device__ inline size_t fused_stage_floats(int lpr) {
 // and each wave waits for its stores before the workgroup barrier that precedes the
 // arrival, so the barrier words themselves need no cache maintenance.  Arrival: count
 // on the group's counter; the group's last arrival of this round counts on the top
-// counter.  Wait: poll the top counter (with a pause between polls, a bounded number
-// of times) until it completes the round.
+// counter, and the arrival that completes the round stores the new top value in the
+// release word.  Wait: poll the release word (with a pause between polls, a bounded
+// number of times) until it reaches the round's value.
 __device__ inline uint64_t barrier_arrive(FusedSync *s, uint32_t n) {
   const uint32_t g = blockIdx.x / kBarGroup, n_groups = (n + kBarGroup - 1) / kBarGroup;
   const uint32_t size = min((uint32_t)kBarGroup, n - g * kBarGroup);
   const uint64_t prev =
       __hip_atomic_fetch_add(&s->group[g].count, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const uint64_t round = prev / size;
-  if ((prev + 1) % size == 0)
-    __hip_atomic_fetch_add(&s->top, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return (round + 1) * n_groups;
+  const uint64_t target = (prev / size + 1) * n_groups;
+  if ((prev + 1) % size == 0) {
+    const uint64_t top =
+        __hip_atomic_fetch_add(&s->top, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
+    if (top == target) __hip_atomic_store(&s->release, top, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+  return target;
 }
 
 __device__ inline void barrier_wait(FusedSync *s, uint64_t target) {
-  for (int spin = 0; __hip_atomic_load(&s->top, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target; spin++) {
+  for (int spin = 0; __hip_atomic_load(&s->release, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) < target; spin++) {
     if (spin == kSpinLimit) {
       __hip_atomic_store(&s->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       break;
@@ -200,7 +209,7 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
   }
   float acc_in = 0.0f;
   if (threadIdx.x < RPP && tile < tiles) acc_in = acc[tile * RPP + threadIdx.x];
-  if (poller) barrier_wait(sync, target);
+  if (poller && tile < tiles) barrier_wait(sync, target);  // a workgroup without a block only arrives
   __syncthreads();
 
   // ---- 4. down + accumulation, block by block of RPP output rows; a wave takes slots
@@ -291,9 +300,10 @@ hipError_t launch_layer_decode(const LayerArgs &L, const float *logits, const fl
   if (err != hipSuccess) return err;
   err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (err != hipSuccess) return err;
-  const int lpr = L.inter / 64, tiles = L.hidden / (64 / lpr);
-  const int g = tiles < cus ? tiles : cus;
-  const dim3 grid((unsigned)(g < kBarGroup * kBarGroups ? g : kBarGroup * kBarGroups)), block(64 * kFusedWaves);
+  // one workgroup per compute unit, whatever the layer's shape: the barrier counters of
+  // a workspace advance by the same round on every call
+  const int lpr = L.inter / 64;
+  const dim3 grid((unsigned)(cus < kBarGroup * kBarGroups ? cus : kBarGroup * kBarGroups)), block(64 * kFusedWaves);
   FusedSync *sync = (FusedSync *)ws;
   if (lpr == 8)
     hipLaunchKernelGGL(k_layer_decode<8>, grid, block, fused_lds_bytes(L), s, L, logits, x, E, k, add_shared, ids, w,

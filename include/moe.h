@@ -213,11 +213,12 @@ size_t moe_decode_workspace_bytes(int32_t kprime, int32_t inter);
  * d_w inputs, as in moe_route_group); d_x [hidden].  kprime = k + add_shared;
  * add_shared must equal the layer's has_shared.
  * d_ws: moe_decode_workspace_bytes(kprime, inter) bytes; its first MOE_DECODE_SYNC_BYTES
- * must be zero before the first call, and each call leaves them ready for the next
- * (calls that share a workspace must not overlap).  The uint32 at byte 128 becomes
- * nonzero if the kernel's grid barrier ever timed out, which can only happen when other
- * kernels hold compute units while this one runs; the results of that call are then
- * undefined.
+ * must be zero before the first call, and each call leaves them ready for the next,
+ * whatever the layer (calls that share a workspace must not overlap, and a workspace
+ * serves one device).  The uint32 at byte 128 becomes nonzero if the kernel's grid
+ * barrier ever timed out, which can only happen when other kernels hold compute units
+ * while this one runs; the results of that call are then undefined, and the first
+ * MOE_DECODE_SYNC_BYTES must be zeroed again before the next call.
  * Limits: hidden == 2048, inter == 256 or 512, E <= 512. */
 moe_status moe_layer_decode_q(const moe_layer *layer, const float *d_logits, const float *d_x, int32_t k,
                               int32_t add_shared, int32_t *d_ids, float *d_w, int32_t *d_counts, int32_t *d_offsets,

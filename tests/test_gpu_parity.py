@@ -305,7 +305,40 @@ def test_fused_decode_matches_three_calls(layers, name):
             groups = rounds
             assert groups > 0
         assert rounds == (call + 1) * groups
+        assert int(sync[48]) | (int(sync[49]) << 32) == rounds  # release word
         assert sync[32] == 0                             # no barrier time-out
+
+
+def test_fused_decode_workspace_shared_across_shapes(layers):
+    """One workspace serves layers of different shapes (inter 512 and 256, different
+    slot counts) in any order: every call matches the three calls bit for bit and
+    advances the barrier words by one round."""
+    names = ["decode_iq2_top10_shared", "decode_mixed_i256_shared", "decode_mixed_i256_shared",
+             "decode_iq2_top10_shared", "tiny16_top4_iq2", "decode_mixed_i256_shared"]
+    ws = torch.zeros(moe.decode_workspace_bytes(moe.MAX_K + 1, 512) // 4, dtype=torch.int32, device="cuda")
+    groups = None
+    for call, name in enumerate(names):
+        banks, H, I, E, shared, T, k, zipf = LAYER_CASES[name]
+        log(f"shared workspace call {call}: {name}")
+        sl, tab, dl = layers(name)
+        x = synth.activations(1, H, tag=f"W/{call}/x")
+        acc0 = synth.activations(1, H, tag=f"W/{call}/acc")
+        lg = synth.logits(1, E, tag=f"W/{call}/l", zipf_alpha=zipf)
+        ref = run_layer(dl, x, k, shared, logits=lg, acc=acc0, decode=True)
+        r = Run(1, E, k, shared, H, I)
+        acc_d = dev(acc0.astype(np.float32))
+        moe.layer_decode_q(dl.desc, dev(lg), dev(x), k, shared, r.ids, r.w, r.counts, r.offsets, r.sorted_slot,
+                           r.slot_pos, r.work, acc_d, ws)
+        got = r.host()
+        for key in ("ids", "w", "counts", "offsets", "sorted_slot", "slot_pos", "work"):
+            np.testing.assert_array_equal(got[key], ref[key], err_msg=key)
+        assert np.array_equal(acc_d.cpu().numpy().view(np.uint32), ref["acc"].view(np.uint32)), name
+        sync = ws[:64].cpu().numpy().view(np.uint32)
+        rounds = int(sync[0]) | (int(sync[1]) << 32)
+        groups = rounds if groups is None else groups
+        assert rounds == (call + 1) * groups
+        assert int(sync[48]) | (int(sync[49]) << 32) == rounds
+        assert sync[32] == 0
 
 
 def test_permutation_invariance_and_determinism(layers):
