@@ -127,7 +127,8 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
   if (wave == 0 && logits) tv = topk_load<8>(logits, E);
   const TableRegs tr = tables_load(L.grids, formats, threadIdx.x - 64, blockDim.x - 64);
 
-  // ---- 1. routing, in every workgroup
+  // ---- 1. routing, in every workgroup, by wave 0; the other waves expand the grid
+  // tables into LDS meanwhile
   if (wave == 0) {
     if (logits) {
       topk_select<8>(tv, E, k, add_shared, blockIdx.x == 0 ? ids : nullptr, w, S.ids, S.w, S.topk);
@@ -156,14 +157,15 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
       S.pos_of[lane] = rank;
       S.slot_at[rank] = lane;
     }
+  } else {
+    tables_store(tr, formats, TL, lds, threadIdx.x - 64, blockDim.x - 64, false);
   }
   __syncthreads();
 
   // ---- 2. gate / up items dealt over the grid's waves (at most one per wave when the
-  // grid has as many waves as items): the activations and the wave's first item are
-  // issued before anything waits; later items are issued one at a time
-  X32 X;
-  load_x32(x + 32 * lane, X);
+  // grid has as many waves as items): the wave's first item, then the activations, are
+  // issued before anything waits (nothing younger is in flight when the item's loads
+  // are issued); later items are issued one at a time
   const int q = lane, lq = lane % LPR, sub = lane / LPR;
   const int ipe = I / kWideRows, n_items = kprime * ipe, nw = gridDim.x * kFusedWaves;
   const int item0 = blockIdx.x * kFusedWaves + wave;
@@ -176,7 +178,8 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
     wide_issue(L, It, item - p * ipe, q);
   };
   if (item0 < n_items) issue(item0);
-  tables_store(tr, formats, TL, lds, threadIdx.x - 64, blockDim.x - 64);
+  X32 X;
+  load_x32(x + 32 * lane, X);
   for (int item = item0; item < n_items; item += nw) {
     if (item != item0) issue(item);
     if (It.qt == MOE_Q_IQ2XS_LIKE)

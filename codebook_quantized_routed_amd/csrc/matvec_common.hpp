@@ -58,8 +58,8 @@ __device__ __forceinline__ uint4 expand_row_f16(uint32_t c, uint32_t h0, uint32_
 // Builds the tables of the formats present from the compact rows (1 KB / 4 KB reads),
 // in two steps: tables_load issues the global loads (call it before the loads that wait
 // on HBM, so the table build does not queue behind them), tables_store expands into LDS
-// and synchronizes the workgroup.  Loader t of n (by default every thread) expands
-// rows t, t + n, ...; t < 0 loads nothing.
+// and synchronizes the workgroup (unless told not to).  Loader t of n (by default every
+// thread) expands rows t, t + n, ...; t < 0 loads and stores nothing.
 constexpr int kTableRowsPerThread = kIq1Rows / 256;  // for n >= 256 loaders
 
 struct TableRegs {
@@ -86,7 +86,7 @@ __device__ __forceinline__ TableRegs tables_load(const uint8_t *grids, int forma
 }
 
 __device__ __forceinline__ void tables_store(const TableRegs &tr, int formats, const TableLayout &TL, uint8_t *lds,
-                                             int t = threadIdx.x, int n = blockDim.x) {
+                                             int t = threadIdx.x, int n = blockDim.x, bool sync = true) {
   if (formats & MOE_Q_IQ2XS_LIKE) {
     const uint32_t h0 = f16_bits((float)kIq2SymVal[0]), h1 = f16_bits((float)kIq2SymVal[1]),
                    h2 = f16_bits((float)kIq2SymVal[2]);
@@ -97,7 +97,7 @@ __device__ __forceinline__ void tables_store(const TableRegs &tr, int formats, c
       if (t >= 0 && r < kIq2Rows) rows[r] = expand_row_f16(tr.c2[i], h0, h1, h2);
     }
     uint4 *masks = (uint4 *)(lds + TL.iq2m);
-    for (int s = threadIdx.x; s < 128; s += blockDim.x) {
+    for (int s = t; t >= 0 && s < 128; s += n) {
       const uint32_t S = (uint32_t)s | ((__builtin_popcount(s) & 1u) << 7);
       uint32_t m[4];
 #pragma unroll
@@ -115,7 +115,7 @@ __device__ __forceinline__ void tables_store(const TableRegs &tr, int formats, c
       if (t >= 0 && r < kIq1Rows) rows[r] = expand_row_f16(tr.c1[i], h0, h1, h2);
     }
   }
-  __syncthreads();
+  if (sync) __syncthreads();
 }
 
 __device__ __forceinline__ void build_tables(const uint8_t *grids, int formats, const TableLayout &TL, uint8_t *lds) {
