@@ -21,6 +21,7 @@ MAX_K = 16
 MAX_IDS = 1024
 MATVEC_MAX_TOKENS = 1  # experts with more tokens run on the matrix cores (MOE_MATVEC_MAX_TOKENS)
 MFMA_TILE_TOKENS = 16  # tokens per matrix-core tile (MOE_MFMA_TILE_TOKENS)
+DECODE_SYNC_BYTES = 4352  # synchronisation words at the start of a decode workspace (MOE_DECODE_SYNC_BYTES)
 
 STATUS = {0: "MOE_OK", -1: "MOE_E_NULL", -2: "MOE_E_SHAPE", -3: "MOE_E_QTYPE", -4: "MOE_E_ALIGN",
           -5: "MOE_E_WORKSPACE", -6: "MOE_E_HIP"}

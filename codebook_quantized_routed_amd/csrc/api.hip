@@ -209,7 +209,7 @@ moe_status moe_expert_ffn_q(const moe_layer *layer, const float *d_x, int32_t T,
 
 size_t moe_decode_workspace_bytes(int32_t kprime, int32_t inter) {
   if (kprime < 1 || kprime > MOE_MAX_K + 1 || inter < 1) return 0;
-  return fused_sync_bytes() + (size_t)kprime * inter * sizeof(float);
+  return fused_sync_bytes() + (size_t)kprime * inter * sizeof(uint64_t);
 }
 
 moe_status moe_layer_decode_q(const moe_layer *layer, const float *d_logits, const float *d_x, int32_t k,

@@ -244,12 +244,13 @@ __device__ __forceinline__ void wide_issue(const LayerArgs &L, WideItem &It, int
   }
 }
 
-// COHERENT: h is stored with agent-scope relaxed atomic stores (written through to the
-// coherence point), for readers in other workgroups of the same launch.
+// COHERENT: h holds 64-bit (value bits, tag) pairs, each stored with one agent-scope
+// relaxed atomic store (written through to the coherence point), for readers in other
+// workgroups of the same launch; otherwise h holds floats.
 template <int QT, bool COHERENT = false>
 __device__ __forceinline__ void wide_run(const LayerArgs &L, WideItem &It, X32 &X, int &cur_tok, bool &gs_ok, int q,
                                          int kprime, const float *x, const int32_t *sorted_slot, const uint8_t *lds,
-                                         const TableLayout &TL, float *h) {
+                                         const TableLayout &TL, void *h, uint32_t tag = 0) {
   const int H = L.hidden, I = L.inter;
   for (int p = It.W.p0; p < It.W.p1; p++) {
     const int tok = (p == It.W.p0 ? It.W.slot0 : sload(sorted_slot + p)) / kprime;
@@ -272,12 +273,13 @@ __device__ __forceinline__ void wide_run(const LayerArgs &L, WideItem &It, X32 &
       vg = group_sum_first<64>(vg);
       vu = group_sum_first<64>(vu);
       if (q == 0) {
-        float *dst = h + (size_t)p * I + It.r0 + i;
+        const size_t at = (size_t)p * I + It.r0 + i;
         const float v = silu(vg) * vu;
         if constexpr (COHERENT)
-          __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store((uint64_t *)h + at, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
         else
-          *dst = v;
+          ((float *)h)[at] = v;
       }
     }
   }

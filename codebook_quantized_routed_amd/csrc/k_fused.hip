@@ -8,21 +8,23 @@
 //  1. every workgroup selects the same experts (top-k of the token's logits, or the
 //     caller's explicit list) -- no exchange is needed for routing; the routing
 //     outputs of moe_route_group are written at the end;
-//  2. gate / up items (2 rows of one expert) are dealt to the waves of the whole grid,
-//     h goes to global memory in sorted order;
-//  3. a grid-wide barrier (all workgroups are resident: one per compute unit at most);
-//     h is written and read with agent-scope atomics, so every row is visible to
-//     every workgroup once its writer has arrived; the down rows a wave needs after
-//     the barrier depend on the routing only, so their loads are issued between its
-//     workgroup's arrival and the wait;
-//  4. down + the weighted accumulation in ascending expert id for the workgroup's
-//     block of output rows.
+//  2. gate / up items (2 rows of one expert) are dealt to the waves of the whole grid;
+//     each h value goes to global memory in sorted order, paired with the call's tag
+//     in one 64-bit agent-scope atomic store;
+//  3. down + the weighted accumulation in ascending expert id for the workgroup's
+//     block of output rows: a wave reads the h row of its slot as soon as its own
+//     gate / up work is done, and reads again the values whose tag is not yet the
+//     call's (their writers have not finished), so no grid-wide barrier is needed.
+// The call's tag comes from a per-call count: each workgroup adds one to its group's
+// counter at the start, and every launch on a device has the same number of
+// workgroups, so each call moves every counter by exactly one round.
 // The arithmetic of every step is the one of moe_route_group, moe_expert_gateup_q and
 // moe_expert_down_accumulate_q, so the results are the same bits.
 //
-// The barrier waits a bounded time: if a workgroup never arrives (which needs another
-// kernel holding compute units meanwhile), the waiters give up after about a second,
-// set the error word and finish; the results of that call are then undefined.
+// The wait for h is bounded: if an h value never gets the call's tag (which needs a
+// workgroup that never runs, i.e. another kernel holding compute units meanwhile), the
+// waiting wave gives up after about a second, sets the error word and finishes; the
+// results of that call are then undefined.
 #include "gemv_dev.hpp"
 #include "route_dev.hpp"
 
@@ -32,28 +34,23 @@ constexpr int kFusedWaves = 12;
 constexpr int kDownWaves = kFusedWaves - 1;  // the last wave polls the grid barrier
 constexpr int kFusedMaxSlots = MOE_MAX_K + 1;
 constexpr int kFusedSlotsPerWave = (kFusedMaxSlots + kDownWaves - 1) / kDownWaves;
-constexpr int kSpinLimit = 1 << 20;  // polls of about 1 us: about a second
+constexpr int kSpinLimit = 1 << 20;  // polls of a few hundred ns: a fraction of a second
 
-// Workspace of the fused call: the barrier words, then h [kprime][inter] fp32.  The
-// barrier is two-level: workgroup g counts on the counter of its group g / kBarGroup,
-// the last arrival of a group counts on the top counter, and the arrival that completes
-// the top count publishes it in the release word, which the waiters poll (polls on the
-// counters' own lines would slow the atomics that update them).  Counters and release
-// are monotonic over all calls; every call on a device launches the same number of
-// workgroups, so each call completes exactly one round of every counter.  The counters
-// sit in separate 128-byte lines; error is set if a wait timed out.
+// Workspace of the fused call: the synchronisation words, then h [kprime][inter] as
+// 64-bit (value bits, tag) pairs.  Workgroup g counts calls on the counter of its group
+// g / kBarGroup (counters in separate 128-byte lines, so few workgroups share one);
+// error is set if a wait timed out.
 constexpr int kBarGroup = 16;
 constexpr int kBarGroups = 32;  // up to 512 workgroups
 struct FusedSync {
-  uint64_t top, pad0[15];
-  uint32_t error, pad1[15];
-  uint64_t release, pad2[7];
+  uint64_t reserved[16];
+  uint32_t error, pad1[31];
   struct Line {
     uint64_t count, pad[15];
   } group[kBarGroups];
 };
-static_assert(sizeof(FusedSync) == 4352, "h follows the barrier words");
-static_assert(offsetof(FusedSync, error) == 128 && offsetof(FusedSync, release) == 192, "documented offsets");
+static_assert(sizeof(FusedSync) == 4352, "h follows the synchronisation words");
+static_assert(offsetof(FusedSync, error) == 128 && offsetof(FusedSync, group) == 256, "documented offsets");
 
 struct FusedLds {
   TopkLds topk;
@@ -62,43 +59,49 @@ struct FusedLds {
   int32_t slot_at[kFusedMaxSlots];     // sorted position p -> slot
   int32_t pos_of[kFusedMaxSlots];      // slot j -> sorted position
   float ydot[kFusedMaxSlots][16];      // down outputs of the block's rows, per slot
+  uint32_t tag;                        // the call's tag
 };
 
 __host__ __device__ inline size_t fused_stage_floats(int lpr) {
   return (size_t)kFusedWaves * lpr * kChunkPad;
 }
 
-// Grid-wide barrier over n workgroups, in two halves so a workgroup can work between
-// them; called by one thread per workgroup.  Every value exchanged through it (h) is
-// stored and loaded with agent-scope atomics, which reach the coherence point directly,
-// and each wave waits for its stores before the workgroup barrier that precedes the
-// arrival, so the barrier words themselves need no cache maintenance.  Arrival: count
-// on the group's counter; the group's last arrival of this round counts on the top
-// counter, and the arrival that completes the round stores the new top value in the
-// release word.  Wait: poll the release word (with a pause between polls, a bounded
-// number of times) until it reaches the round's value.
-__device__ inline uint64_t barrier_arrive(FusedSync *s, uint32_t n) {
-  const uint32_t g = blockIdx.x / kBarGroup, n_groups = (n + kBarGroup - 1) / kBarGroup;
+// The call's tag (nonzero): one more than the number of earlier calls, from this
+// workgroup's count on its group's counter.
+__device__ inline uint32_t call_tag(FusedSync *s) {
+  const uint32_t g = blockIdx.x / kBarGroup, n = gridDim.x;
   const uint32_t size = min((uint32_t)kBarGroup, n - g * kBarGroup);
   const uint64_t prev =
       __hip_atomic_fetch_add(&s->group[g].count, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const uint64_t target = (prev / size + 1) * n_groups;
-  if ((prev + 1) % size == 0) {
-    const uint64_t top =
-        __hip_atomic_fetch_add(&s->top, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
-    if (top == target) __hip_atomic_store(&s->release, top, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-  }
-  return target;
+  return (uint32_t)(prev / size) + 1u;
 }
 
-__device__ inline void barrier_wait(FusedSync *s, uint64_t target) {
-  for (int spin = 0; __hip_atomic_load(&s->release, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) < target; spin++) {
+// The h row of one slot (I pairs) into a wave's LDS area as floats (64-value chunks
+// padded to kChunkPad floats): lane l takes pairs l, l + 64, ...; pairs whose tag is
+// not yet the call's are read again after a pause, a bounded number of times.
+template <int LPR>
+__device__ inline void stage_h_row(const uint64_t *src, uint32_t tag, float *hs, FusedSync *s) {
+  const int lane = threadIdx.x & 63;
+  uint64_t v[LPR];
+#pragma unroll
+  for (int i = 0; i < LPR; i++) v[i] = __hip_atomic_load(src + lane + 64 * i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int spin = 0;; spin++) {
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < LPR; i++) ok = ok && (uint32_t)(v[i] >> 32) == tag;
+    if (__ballot(!ok) == 0ull) break;
     if (spin == kSpinLimit) {
-      __hip_atomic_store(&s->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (lane == 0) __hip_atomic_store(&s->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       break;
     }
-    __builtin_amdgcn_s_sleep(8);
+    __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+    for (int i = 0; i < LPR; i++)
+      if ((uint32_t)(v[i] >> 32) != tag)
+        v[i] = __hip_atomic_load(src + lane + 64 * i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+#pragma unroll
+  for (int i = 0; i < LPR; i++) hs[i * kChunkPad + lane] = __uint_as_float((uint32_t)v[i]);
 }
 
 template <int LPR>
@@ -117,7 +120,7 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
   const int kprime = k + add_shared, n_ids = E + add_shared;
   const int H = L.hidden, I = L.inter;
-  float *h = (float *)(sync + 1);
+  uint64_t *h = (uint64_t *)(sync + 1);
   const int formats = layer_formats(L);
   const TableLayout TL = table_layout(formats);
   float *hs = (float *)(lds + TL.bytes) + wave * HS;
@@ -126,6 +129,8 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
   TopkVals<8> tv;
   if (wave == 0 && logits) tv = topk_load<8>(logits, E);
   const TableRegs tr = tables_load(L.grids, formats, threadIdx.x - 64, blockDim.x - 64);
+  uint32_t tag = 0;
+  if (threadIdx.x == 64) tag = call_tag(sync);
 
   // ---- 1. routing, in every workgroup, by wave 0; the other waves expand the grid
   // tables into LDS meanwhile
@@ -159,8 +164,10 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
     }
   } else {
     tables_store(tr, formats, TL, lds, threadIdx.x - 64, blockDim.x - 64, false);
+    if (threadIdx.x == 64) S.tag = tag;
   }
   __syncthreads();
+  tag = S.tag;
 
   // ---- 2. gate / up items dealt over the grid's waves (at most one per wave when the
   // grid has as many waves as items): the wave's first item, then the activations, are
@@ -183,24 +190,17 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
   for (int item = item0; item < n_items; item += nw) {
     if (item != item0) issue(item);
     if (It.qt == MOE_Q_IQ2XS_LIKE)
-      wide_run<MOE_Q_IQ2XS_LIKE, true>(L, It, X, cur_tok, gs_ok, q, kprime, x, sorted_slot, lds, TL, h);
+      wide_run<MOE_Q_IQ2XS_LIKE, true>(L, It, X, cur_tok, gs_ok, q, kprime, x, sorted_slot, lds, TL, h, tag);
     else
-      wide_run<MOE_Q_IQ1M_LIKE, true>(L, It, X, cur_tok, gs_ok, q, kprime, x, sorted_slot, lds, TL, h);
+      wide_run<MOE_Q_IQ1M_LIKE, true>(L, It, X, cur_tok, gs_ok, q, kprime, x, sorted_slot, lds, TL, h, tag);
   }
 
-  // ---- 3. every h row written before any is read: each wave's h stores complete, then
-  // the workgroup arrives.  Between arrival and wait, waves 0 .. kDownWaves-1 load the
-  // down rows of the workgroup's first block and its acc values; the last wave polls
-  // (its loads would otherwise queue behind those).
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  const bool poller = threadIdx.x == 64 * kDownWaves;
-  uint64_t target = 0;
-  if (poller) target = barrier_arrive(sync, gridDim.x);
+  // ---- 3. the down rows of the wave's first slot (slot = wave) in the workgroup's first
+  // block, and its acc values, are loaded as soon as the wave's gate / up work is done
   const int tiles = H / RPP;
   int tile = blockIdx.x;
   const bool down_wave = wave < kDownWaves;
-  RowRaw Rd0;  // the wave's first slot (slot = wave) of the first block, loaded early
+  RowRaw Rd0;
   int dqt0 = 0;
   if (down_wave && wave < kprime && tile < tiles) {
     const int e = uniform(S.ids[wave]);
@@ -212,8 +212,6 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
   }
   float acc_in = 0.0f;
   if (threadIdx.x < RPP && tile < tiles) acc_in = acc[tile * RPP + threadIdx.x];
-  if (poller && tile < tiles) barrier_wait(sync, target);  // a workgroup without a block only arrives
-  __syncthreads();
 
   // ---- 4. down + accumulation, block by block of RPP output rows; a wave takes slots
   // wave, wave + kDownWaves, ... one after the other
@@ -235,17 +233,8 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
         R = qt == MOE_Q_IQ2XS_LIKE ? load_row<MOE_Q_IQ2XS_LIKE>(Wd, I, tile * RPP + sub, lq)
                                    : load_row<MOE_Q_IQ1M_LIKE>(Wd, I, tile * RPP + sub, lq);
       }
-      // the slot's h row into the wave's LDS area (64-float chunks padded to kChunkPad
-      // floats), read with agent-scope loads: other workgroups wrote it
-      const uint32_t *src = (const uint32_t *)(h + (size_t)S.pos_of[j] * I);
-      for (int f = lane; f < LPR * 16; f += 64) {
-        uint4 v;
-        v.x = __hip_atomic_load(src + 4 * f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        v.y = __hip_atomic_load(src + 4 * f + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        v.z = __hip_atomic_load(src + 4 * f + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        v.w = __hip_atomic_load(src + 4 * f + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        *(uint4 *)(hs + (f >> 4) * kChunkPad + (f & 15) * 4) = v;
-      }
+      // the slot's h row (written by other workgroups) into the wave's LDS area
+      stage_h_row<LPR>(h + (size_t)S.pos_of[j] * I, tag, hs, sync);
       __builtin_amdgcn_wave_barrier();
       const float *hrow = hs + lq * kChunkPad;
       const float v = qt == MOE_Q_IQ2XS_LIKE ? down_slot_dot<MOE_Q_IQ2XS_LIKE, LPR>(R, hrow, lq, lds, TL)

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 #define MOE_MAX_BANKS 4
 #define MOE_MAX_K 16        /* routed experts per token */
 #define MOE_MAX_IDS 1024    /* E + has_shared */
@@ -200,7 +200,8 @@ moe_status moe_expert_down_accumulate_q(const moe_layer *layer, const float *d_h
                                         const int32_t *d_ids, const float *d_w, const int32_t *d_slot_pos,
                                         float *d_acc, hipStream_t stream);
 
-/* Workspace of moe_layer_decode_q: MOE_DECODE_SYNC_BYTES of synchronisation words, then h. */
+/* Workspace of moe_layer_decode_q: MOE_DECODE_SYNC_BYTES of synchronisation words, then h
+ * [kprime][inter] as 64-bit (fp32 bits, call tag) pairs. */
 #define MOE_DECODE_SYNC_BYTES 4352
 size_t moe_decode_workspace_bytes(int32_t kprime, int32_t inter);
 
@@ -215,10 +216,10 @@ size_t moe_decode_workspace_bytes(int32_t kprime, int32_t inter);
  * d_ws: moe_decode_workspace_bytes(kprime, inter) bytes; its first MOE_DECODE_SYNC_BYTES
  * must be zero before the first call, and each call leaves them ready for the next,
  * whatever the layer (calls that share a workspace must not overlap, and a workspace
- * serves one device).  The uint32 at byte 128 becomes nonzero if the kernel's grid
- * barrier ever timed out, which can only happen when other kernels hold compute units
- * while this one runs; the results of that call are then undefined, and the first
- * MOE_DECODE_SYNC_BYTES must be zeroed again before the next call.
+ * serves one device).  The uint32 at byte 128 becomes nonzero if a wait of the kernel
+ * for another workgroup's h values ever timed out, which can only happen when other
+ * kernels hold compute units while this one runs; the results of that call are then
+ * undefined, and the whole workspace must be zeroed again before the next call.
  * Limits: hidden == 2048, inter == 256 or 512, E <= 512. */
 moe_status moe_layer_decode_q(const moe_layer *layer, const float *d_logits, const float *d_x, int32_t k,
                               int32_t add_shared, int32_t *d_ids, float *d_w, int32_t *d_counts, int32_t *d_offsets,

@@ -43,11 +43,12 @@ def test_binding_constants_match_header():
     assert int(defs["MOE_MAX_IDS"]) == moe.MAX_IDS
     assert int(defs["MOE_MATVEC_MAX_TOKENS"]) == moe.MATVEC_MAX_TOKENS
     assert int(defs["MOE_MFMA_TILE_TOKENS"]) == moe.MFMA_TILE_TOKENS
-    assert moe.decode_workspace_bytes(11, 512) - 11 * 512 * 4 == int(defs["MOE_DECODE_SYNC_BYTES"])
+    assert int(defs["MOE_DECODE_SYNC_BYTES"]) == moe.DECODE_SYNC_BYTES
+    assert moe.decode_workspace_bytes(11, 512) - 11 * 512 * 8 == moe.DECODE_SYNC_BYTES
 
 
 def test_version_strings_sizes():
-    assert moe.abi_version() == 3
+    assert moe.abi_version() == 4
     for st in moe.STATUS:
         assert lib.moe_status_string(st)
     assert moe.grids_bytes() >= 512 * 8 + 2048 * 8
@@ -153,7 +154,7 @@ def test_other_rejects():
 def test_layer_decode_rejects():
     d = layer()
     ws_need = moe.decode_workspace_bytes(11, 512)
-    assert ws_need == 4352 + 11 * 512 * 4
+    assert ws_need == 4352 + 11 * 512 * 8
 
     def call(d=d, logits=A, x=A, k=10, add_shared=1, ws=A, ws_bytes=ws_need, acc=A):
         return lib.moe_layer_decode_q(C.byref(d), logits, x, k, add_shared, A, A, A, A, A, A, A, acc, ws, ws_bytes,
