@@ -226,12 +226,11 @@ struct WideItem {
   int r0, qt;
 };
 
-__device__ __forceinline__ void wide_issue(const LayerArgs &L, WideItem &It, int rb, int q) {
-  const int H = L.hidden, I = L.inter;
-  const BankArgs &B = bank_of(L, It.W.e);
-  It.qt = B.qtype;
+// The loads of item rb (rows kWideRows * rb ..) of gate Wg and up Wu, format qt.
+__device__ __forceinline__ void wide_issue_mats(WideItem &It, const QMat &Wg, const QMat &Wu, int qt, int H, int rb,
+                                                int q) {
+  It.qt = qt;
   It.r0 = rb * kWideRows;
-  const QMat Wg = expert_mat(B, It.W.e, kGate, I, H), Wu = expert_mat(B, It.W.e, kUp, I, H);
 #pragma unroll
   for (int i = 0; i < kWideRows; i++) {
     if (It.qt == MOE_Q_IQ2XS_LIKE) {
@@ -242,6 +241,12 @@ __device__ __forceinline__ void wide_issue(const LayerArgs &L, WideItem &It, int
       It.u[i] = load_row32<MOE_Q_IQ1M_LIKE>(Wu, H, It.r0 + i, q);
     }
   }
+}
+
+__device__ __forceinline__ void wide_issue(const LayerArgs &L, WideItem &It, int rb, int q) {
+  const int H = L.hidden, I = L.inter;
+  const BankArgs &B = bank_of(L, It.W.e);
+  wide_issue_mats(It, expert_mat(B, It.W.e, kGate, I, H), expert_mat(B, It.W.e, kUp, I, H), B.qtype, H, rb, q);
 }
 
 // COHERENT: h holds 64-bit (value bits, tag) pairs, each stored with one agent-scope

@@ -52,13 +52,34 @@ struct FusedSync {
 static_assert(sizeof(FusedSync) == 4352, "h follows the synchronisation words");
 static_assert(offsetof(FusedSync, error) == 128 && offsetof(FusedSync, group) == 256, "documented offsets");
 
+// Activations staged in LDS: lane l of a wave takes columns 32 l .. 32 l + 31 (hidden
+// 2048), stored at l * kXsRow floats (the padding spreads the lanes over the banks).
+constexpr int kXsRow = 36;
+
+// The layer's banks, copied from the kernel arguments into LDS during routing (static
+// indexing, so the copy reads scalar registers): per matrix and stream the base and the
+// bytes of one expert.
+struct BankLds {
+  const uint8_t *base[3][3];  // [gate, up, down][stream]
+  uint64_t bytes[3][3];
+  int32_t first, qt, pad[2];
+};
+
+// The expert at one sorted position: its id, slot and bank.
+struct PosRec {
+  int32_t e, slot, bank, pad;
+};
+
 struct FusedLds {
+  BankLds banks[MOE_MAX_BANKS];
+  PosRec pos[kFusedMaxSlots];          // sorted position p -> its expert
   TopkLds topk;
   int32_t ids[kFusedMaxSlots];         // slot j -> expert
   float w[kFusedMaxSlots];             // slot j -> router weight
   int32_t slot_at[kFusedMaxSlots];     // sorted position p -> slot
   int32_t pos_of[kFusedMaxSlots];      // slot j -> sorted position
   float ydot[kFusedMaxSlots][16];      // down outputs of the block's rows, per slot
+  float xs[64 * kXsRow];               // the token's activations, lane l's 32 at l * kXsRow
   uint32_t tag;                        // the call's tag
 };
 
@@ -104,6 +125,53 @@ __device__ inline void stage_h_row(const uint64_t *src, uint32_t tag, float *hs,
   for (int i = 0; i < LPR; i++) hs[i * kChunkPad + lane] = __uint_as_float((uint32_t)v[i]);
 }
 
+// Fills the bank table (one thread).
+__device__ inline void fill_banks(const LayerArgs &L, BankLds *banks) {
+  const int H = L.hidden, I = L.inter;
+#pragma unroll
+  for (int b = 0; b < MOE_MAX_BANKS; b++) {
+    if (b >= L.n_banks) break;
+    const BankArgs &B = L.banks[b];
+    BankLds &D = banks[b];
+    D.first = B.first;
+    D.qt = B.qtype;
+#pragma unroll
+    for (int w = 0; w < 3; w++) {
+      const int rows = w == kDown ? H : I, cols = w == kDown ? I : H;
+      const uint8_t *const *src = w == kGate ? B.gate : (w == kUp ? B.up : B.down);
+      D.base[w][0] = src[0], D.base[w][1] = src[1], D.base[w][2] = src[2];
+      D.bytes[w][0] = stream0_bytes(B.qtype, rows, cols);
+      D.bytes[w][1] = stream1_bytes(B.qtype, rows, cols);
+      D.bytes[w][2] = stream2_bytes(B.qtype, rows, cols);
+    }
+  }
+}
+
+// The bank of expert e (as bank_of).
+__device__ inline int bank_index(const LayerArgs &L, int e) {
+  int b = 0;
+#pragma unroll
+  for (int i = 1; i < MOE_MAX_BANKS; i++)
+    if (i < L.n_banks && e >= L.banks[i].first) b = i;
+  return b;
+}
+
+__device__ __forceinline__ uint64_t uniform64(uint64_t v) {
+  return ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32)) << 32) |
+         (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+}
+
+// Matrix w of expert e in bank B (the same bases and offsets as expert_mat), in scalar
+// registers; the bases are marked global again (loads through them are global loads).
+__device__ __forceinline__ QMat bank_mat(const BankLds &B, int e, int w) {
+  const uint64_t x = (uint64_t)(e - uniform(B.first));
+  QMat m;
+  m.s0 = (const uint8_t *)(const __attribute__((address_space(1))) uint8_t *)(uniform64((uint64_t)B.base[w][0]) + x * uniform64(B.bytes[w][0]));
+  m.s1 = (const uint8_t *)(const __attribute__((address_space(1))) uint8_t *)(uniform64((uint64_t)B.base[w][1]) + x * uniform64(B.bytes[w][1]));
+  m.s2 = (const uint8_t *)(const __attribute__((address_space(1))) uint8_t *)(uniform64((uint64_t)B.base[w][2]) + x * uniform64(B.bytes[w][2]));
+  return m;
+}
+
 template <int LPR>
 __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, const float *__restrict__ logits,
                                                                     const float *__restrict__ x, int E, int k,
@@ -131,6 +199,11 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
   const TableRegs tr = tables_load(L.grids, formats, threadIdx.x - 64, blockDim.x - 64);
   uint32_t tag = 0;
   if (threadIdx.x == 64) tag = call_tag(sync);
+  // waves 1..: the activations, one float4 per thread (hidden 2048), staged in LDS with
+  // the tables
+  const int xt = threadIdx.x - 64;
+  float4 xv;
+  if (xt >= 0 && xt < 512) xv = ((const float4 *)x)[xt];
 
   // ---- 1. routing, in every workgroup, by wave 0; the other waves expand the grid
   // tables into LDS meanwhile
@@ -161,32 +234,43 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
     if (lane < kprime) {
       S.pos_of[lane] = rank;
       S.slot_at[rank] = lane;
+      S.pos[rank] = PosRec{my, lane, bank_index(L, my), 0};
     }
   } else {
     tables_store(tr, formats, TL, lds, threadIdx.x - 64, blockDim.x - 64, false);
-    if (threadIdx.x == 64) S.tag = tag;
+    if (xt >= 0 && xt < 512) *(float4 *)&S.xs[(xt >> 3) * kXsRow + (xt & 7) * 4] = xv;
+    if (threadIdx.x == 64) {
+      S.tag = tag;
+      fill_banks(L, S.banks);
+    }
   }
   __syncthreads();
   tag = S.tag;
 
   // ---- 2. gate / up items dealt over the grid's waves (at most one per wave when the
-  // grid has as many waves as items): the wave's first item, then the activations, are
-  // issued before anything waits (nothing younger is in flight when the item's loads
-  // are issued); later items are issued one at a time
+  // grid has as many waves as items): the wave's first item is issued before anything
+  // waits, its activations come from LDS; later items are issued one at a time
   const int q = lane, lq = lane % LPR, sub = lane / LPR;
-  const int ipe = I / kWideRows, n_items = kprime * ipe, nw = gridDim.x * kFusedWaves;
+  constexpr int ipe = 64 * LPR / kWideRows;  // items per expert (inter = 64 LPR rows)
+  const int n_items = kprime * ipe, nw = gridDim.x * kFusedWaves;
   const int item0 = blockIdx.x * kFusedWaves + wave;
   WideItem It;
   int cur_tok = 0;
   bool gs_ok = false;
   auto issue = [&](int item) {
-    const int p = item / ipe, slot = uniform(S.slot_at[p]);
-    It.W = WorkRec{uniform(S.ids[slot]), p, p + 1, slot};
-    wide_issue(L, It, item - p * ipe, q);
+    const int p = item / ipe;
+    const int e = uniform(S.pos[p].e), slot = uniform(S.pos[p].slot);
+    const BankLds &B = S.banks[uniform(S.pos[p].bank)];
+    It.W = WorkRec{e, p, p + 1, slot};
+    wide_issue_mats(It, bank_mat(B, e, kGate), bank_mat(B, e, kUp), uniform(B.qt), H, item - p * ipe, q);
   };
-  if (item0 < n_items) issue(item0);
   X32 X;
-  load_x32(x + 32 * lane, X);
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const float4 f = *(const float4 *)&S.xs[lane * kXsRow + 4 * i];
+    X.v[4 * i] = f.x, X.v[4 * i + 1] = f.y, X.v[4 * i + 2] = f.z, X.v[4 * i + 3] = f.w;
+  }
+  if (item0 < n_items) issue(item0);
   for (int item = item0; item < n_items; item += nw) {
     if (item != item0) issue(item);
     if (It.qt == MOE_Q_IQ2XS_LIKE)
@@ -203,12 +287,12 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
   RowRaw Rd0;
   int dqt0 = 0;
   if (down_wave && wave < kprime && tile < tiles) {
-    const int e = uniform(S.ids[wave]);
-    const BankArgs &B = bank_of(L, e);
-    const QMat Wd = expert_mat(B, e, kDown, H, I);
-    dqt0 = B.qtype;
-    Rd0 = B.qtype == MOE_Q_IQ2XS_LIKE ? load_row<MOE_Q_IQ2XS_LIKE>(Wd, I, tile * RPP + sub, lq)
-                                      : load_row<MOE_Q_IQ1M_LIKE>(Wd, I, tile * RPP + sub, lq);
+    const PosRec &P = S.pos[uniform(S.pos_of[wave])];
+    const BankLds &B = S.banks[uniform(P.bank)];
+    const QMat Wd = bank_mat(B, uniform(P.e), kDown);
+    dqt0 = uniform(B.qt);
+    Rd0 = dqt0 == MOE_Q_IQ2XS_LIKE ? load_row<MOE_Q_IQ2XS_LIKE>(Wd, I, tile * RPP + sub, lq)
+                                   : load_row<MOE_Q_IQ1M_LIKE>(Wd, I, tile * RPP + sub, lq);
   }
   float acc_in = 0.0f;
   if (threadIdx.x < RPP && tile < tiles) acc_in = acc[tile * RPP + threadIdx.x];
@@ -226,10 +310,10 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
         R = Rd0;
         qt = dqt0;
       } else {
-        const int e = uniform(S.ids[j]);
-        const BankArgs &B = bank_of(L, e);
-        const QMat Wd = expert_mat(B, e, kDown, H, I);
-        qt = B.qtype;
+        const PosRec &P = S.pos[uniform(S.pos_of[j])];
+        const BankLds &B = S.banks[uniform(P.bank)];
+        const QMat Wd = bank_mat(B, uniform(P.e), kDown);
+        qt = uniform(B.qt);
         R = qt == MOE_Q_IQ2XS_LIKE ? load_row<MOE_Q_IQ2XS_LIKE>(Wd, I, tile * RPP + sub, lq)
                                    : load_row<MOE_Q_IQ1M_LIKE>(Wd, I, tile * RPP + sub, lq);
       }
