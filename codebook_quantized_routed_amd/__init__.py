@@ -19,7 +19,14 @@ IQ1M_LIKE = 2
 MAX_BANKS = 4
 MAX_K = 16
 MAX_IDS = 1024
-MATVEC_MAX_TOKENS = 1  # experts with more tokens run on the matrix cores (MOE_MATVEC_MAX_TOKENS)
+MATVEC_MAX_TOKENS = 1  # above SMALL_BATCH_TOKENS: experts with more tokens run on the matrix cores
+SMALL_BATCH_TOKENS = 16  # calls of at most this many tokens run every expert on the mat-vec kernels
+
+
+def matvec_max_tokens(T: int) -> int:
+    """Experts with at most this many of a call's T tokens run on the mat-vec kernels
+    (m(T) in include/moe.h)."""
+    return T if T <= SMALL_BATCH_TOKENS else MATVEC_MAX_TOKENS
 MFMA_TILE_TOKENS = 16  # tokens per matrix-core tile (MOE_MFMA_TILE_TOKENS)
 DECODE_SYNC_BYTES = 4352  # synchronisation words at the start of a decode workspace (MOE_DECODE_SYNC_BYTES)
 

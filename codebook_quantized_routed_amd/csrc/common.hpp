@@ -32,11 +32,17 @@ struct WorkRec {
   int e, p0, p1, slot0;
 };
 
-// Upper bounds on the experts with more than MOE_MATVEC_MAX_TOKENS slots (each has at
+// Experts with at most this many of a call's T tokens run on the mat-vec kernels.
+__host__ __device__ inline int matvec_max_tokens(int T) {
+  return T <= MOE_SMALL_BATCH_TOKENS ? T : MOE_MATVEC_MAX_TOKENS;
+}
+
+// Upper bounds on the experts with more than matvec_max_tokens(T) slots (each has at
 // most one slot per token) and on their tiles of MOE_MFMA_TILE_TOKENS.
 __host__ __device__ inline int max_wide_experts(int T, int kprime, int n_ids) {
-  if (T <= MOE_MATVEC_MAX_TOKENS) return 0;
-  const long by_slots = (long)T * kprime / (MOE_MATVEC_MAX_TOKENS + 1);
+  const int m = matvec_max_tokens(T);
+  if (T <= m) return 0;
+  const long by_slots = (long)T * kprime / (m + 1);
   return (int)(by_slots < n_ids ? by_slots : n_ids);
 }
 __host__ __device__ inline int max_mfma_tiles(int T, int kprime, int n_ids) {

@@ -243,6 +243,19 @@ __device__ __forceinline__ void wide_issue_mats(WideItem &It, const QMat &Wg, co
   }
 }
 
+// The same for an item known to have format QT: no format branch, so the compiler can
+// count the item's loads exactly and wait for an older item without waiting for it.
+template <int QT>
+__device__ __forceinline__ void wide_issue_fmt(WideItem &It, const QMat &Wg, const QMat &Wu, int H, int rb, int q) {
+  It.qt = QT;
+  It.r0 = rb * kWideRows;
+#pragma unroll
+  for (int i = 0; i < kWideRows; i++) {
+    It.g[i] = load_row32<QT>(Wg, H, It.r0 + i, q);
+    It.u[i] = load_row32<QT>(Wu, H, It.r0 + i, q);
+  }
+}
+
 __device__ __forceinline__ void wide_issue(const LayerArgs &L, WideItem &It, int rb, int q) {
   const int H = L.hidden, I = L.inter;
   const BankArgs &B = bank_of(L, It.W.e);
@@ -252,15 +265,22 @@ __device__ __forceinline__ void wide_issue(const LayerArgs &L, WideItem &It, int
 // COHERENT: h holds 64-bit (value bits, tag) pairs, each stored with one agent-scope
 // relaxed atomic store (written through to the coherence point), for readers in other
 // workgroups of the same launch; otherwise h holds floats.
+// A token's activations: token t's slice of lane q starts at x + t * tok_stride +
+// q * lane_stride (global memory: hidden and 32; LDS staging: its own padded layout).
+struct XSource {
+  const float *x;
+  int tok_stride, lane_stride;
+};
+
 template <int QT, bool COHERENT = false>
 __device__ __forceinline__ void wide_run(const LayerArgs &L, WideItem &It, X32 &X, int &cur_tok, bool &gs_ok, int q,
-                                         int kprime, const float *x, const int32_t *sorted_slot, const uint8_t *lds,
-                                         const TableLayout &TL, void *h, uint32_t tag = 0) {
-  const int H = L.hidden, I = L.inter;
+                                         int kprime, const XSource &xsrc, const int32_t *sorted_slot,
+                                         const uint8_t *lds, const TableLayout &TL, void *h, uint32_t tag = 0) {
+  const int I = L.inter;
   for (int p = It.W.p0; p < It.W.p1; p++) {
     const int tok = (p == It.W.p0 ? It.W.slot0 : sload(sorted_slot + p)) / kprime;
     if (tok != cur_tok) {
-      load_x32(x + (size_t)tok * H + 32 * q, X);
+      load_x32(xsrc.x + (size_t)tok * xsrc.tok_stride + q * xsrc.lane_stride, X);
       cur_tok = tok;
       gs_ok = false;
     }

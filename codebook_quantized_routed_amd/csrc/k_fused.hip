@@ -56,15 +56,6 @@ static_assert(offsetof(FusedSync, error) == 128 && offsetof(FusedSync, group) ==
 // 2048), stored at l * kXsRow floats (the padding spreads the lanes over the banks).
 constexpr int kXsRow = 36;
 
-// The layer's banks, copied from the kernel arguments into LDS during routing (static
-// indexing, so the copy reads scalar registers): per matrix and stream the base and the
-// bytes of one expert.
-struct BankLds {
-  const uint8_t *base[3][3];  // [gate, up, down][stream]
-  uint64_t bytes[3][3];
-  int32_t first, qt, pad[2];
-};
-
 // The expert at one sorted position: its id, slot and bank.
 struct PosRec {
   int32_t e, slot, bank, pad;
@@ -123,53 +114,6 @@ __device__ inline void stage_h_row(const uint64_t *src, uint32_t tag, float *hs,
   }
 #pragma unroll
   for (int i = 0; i < LPR; i++) hs[i * kChunkPad + lane] = __uint_as_float((uint32_t)v[i]);
-}
-
-// Fills the bank table (one thread).
-__device__ inline void fill_banks(const LayerArgs &L, BankLds *banks) {
-  const int H = L.hidden, I = L.inter;
-#pragma unroll
-  for (int b = 0; b < MOE_MAX_BANKS; b++) {
-    if (b >= L.n_banks) break;
-    const BankArgs &B = L.banks[b];
-    BankLds &D = banks[b];
-    D.first = B.first;
-    D.qt = B.qtype;
-#pragma unroll
-    for (int w = 0; w < 3; w++) {
-      const int rows = w == kDown ? H : I, cols = w == kDown ? I : H;
-      const uint8_t *const *src = w == kGate ? B.gate : (w == kUp ? B.up : B.down);
-      D.base[w][0] = src[0], D.base[w][1] = src[1], D.base[w][2] = src[2];
-      D.bytes[w][0] = stream0_bytes(B.qtype, rows, cols);
-      D.bytes[w][1] = stream1_bytes(B.qtype, rows, cols);
-      D.bytes[w][2] = stream2_bytes(B.qtype, rows, cols);
-    }
-  }
-}
-
-// The bank of expert e (as bank_of).
-__device__ inline int bank_index(const LayerArgs &L, int e) {
-  int b = 0;
-#pragma unroll
-  for (int i = 1; i < MOE_MAX_BANKS; i++)
-    if (i < L.n_banks && e >= L.banks[i].first) b = i;
-  return b;
-}
-
-__device__ __forceinline__ uint64_t uniform64(uint64_t v) {
-  return ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32)) << 32) |
-         (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
-}
-
-// Matrix w of expert e in bank B (the same bases and offsets as expert_mat), in scalar
-// registers; the bases are marked global again (loads through them are global loads).
-__device__ __forceinline__ QMat bank_mat(const BankLds &B, int e, int w) {
-  const uint64_t x = (uint64_t)(e - uniform(B.first));
-  QMat m;
-  m.s0 = (const uint8_t *)(const __attribute__((address_space(1))) uint8_t *)(uniform64((uint64_t)B.base[w][0]) + x * uniform64(B.bytes[w][0]));
-  m.s1 = (const uint8_t *)(const __attribute__((address_space(1))) uint8_t *)(uniform64((uint64_t)B.base[w][1]) + x * uniform64(B.bytes[w][1]));
-  m.s2 = (const uint8_t *)(const __attribute__((address_space(1))) uint8_t *)(uniform64((uint64_t)B.base[w][2]) + x * uniform64(B.bytes[w][2]));
-  return m;
 }
 
 template <int LPR>
@@ -274,9 +218,9 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
   for (int item = item0; item < n_items; item += nw) {
     if (item != item0) issue(item);
     if (It.qt == MOE_Q_IQ2XS_LIKE)
-      wide_run<MOE_Q_IQ2XS_LIKE, true>(L, It, X, cur_tok, gs_ok, q, kprime, x, sorted_slot, lds, TL, h, tag);
+      wide_run<MOE_Q_IQ2XS_LIKE, true>(L, It, X, cur_tok, gs_ok, q, kprime, XSource{x, H, 32}, sorted_slot, lds, TL, h, tag);
     else
-      wide_run<MOE_Q_IQ1M_LIKE, true>(L, It, X, cur_tok, gs_ok, q, kprime, x, sorted_slot, lds, TL, h, tag);
+      wide_run<MOE_Q_IQ1M_LIKE, true>(L, It, X, cur_tok, gs_ok, q, kprime, XSource{x, H, 32}, sorted_slot, lds, TL, h, tag);
   }
 
   // ---- 3. the down rows of the wave's first slot (slot = wave) in the workgroup's first

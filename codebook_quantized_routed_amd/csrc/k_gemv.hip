@@ -125,49 +125,105 @@ __global__ void __launch_bounds__(256) k_gateup(LayerArgs L, const float *__rest
 }
 
 // gate + up for hidden 2048 (one row per wave, 32 columns per lane; see the item
-// layout in gemv_dev.hpp): one item per wave and grid step, the first item's loads
-// issued before the table build.
-__global__ void __launch_bounds__(256) k_gateup_wide(LayerArgs L, const float *__restrict__ x, int kprime,
-                                                     const int32_t *__restrict__ sorted_slot,
-                                                     const WorkRec *__restrict__ work, int max_tokens, int n_ids,
-                                                     float *__restrict__ h) {
+// layout in gemv_dev.hpp), persistent: at most one workgroup of kWideWaves waves per
+// compute unit, so the grid tables are built once per compute unit; wave w of
+// workgroup b takes items kWideWaves b + w, then every stride-th, and keeps the loads
+// of its next two items in flight while it computes one (a single item of lookahead
+// left each item waiting out the memory latency).  With at most kXStageTokens tokens,
+// the tokens' activations are staged in LDS.
+constexpr int kWideWaves = 12;
+static_assert(64 * kWideWaves >= 2048 / 4 && 2 * 64 * kWideWaves >= MOE_MAX_IDS,
+              "staging: one float4 of each token per thread; two work records per thread");
+constexpr int kXStageTokens = 8;
+constexpr int kXLaneRow = 36;                 // floats per lane slice in the staging
+constexpr int kXTokRow = 64 * kXLaneRow;      // floats per staged token
+
+// LDS after the grid tables: the staged activations (room for kXStageTokens tokens,
+// when staged), then the work records (room for MOE_MAX_IDS).  Fixed sizes let the
+// copies be unconditional, so their loads issue back to back.
+__host__ __device__ inline size_t wide_stage_bytes(int T) {
+  return T <= kXStageTokens ? (size_t)kXStageTokens * kXTokRow * sizeof(float) : 0;
+}
+constexpr size_t kWideRecsBytes = (size_t)MOE_MAX_IDS * sizeof(WorkRec);
+
+template <bool STAGED, int QT>
+__global__ void __launch_bounds__(64 * kWideWaves) k_gateup_wide(LayerArgs L, const float *__restrict__ x, int T,
+                                                                 int kprime, const int32_t *__restrict__ sorted_slot,
+                                                                 const WorkRec *__restrict__ work, int max_tokens,
+                                                                 int n_ids, float *__restrict__ h) {
   extern __shared__ __align__(16) uint8_t lds[];
+  __shared__ BankLds banks[MOE_MAX_BANKS];
   const int q = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
-  const int formats = layer_formats(L);
-  const TableLayout TL = table_layout(formats);
-  const TableRegs tr = tables_load(L.grids, formats);
-  const int ipe = L.inter / kWideRows, stride = gridDim.x * 4;
-  int item = blockIdx.x * 4 + wave;
-  const int a0 = min(item / ipe, n_ids - 1);  // within the n_ids + 1 records before the count is known
-  const WorkRec rec0 = load_work(work, 1 + a0);
-  const int total = sload(&work[0].e) * ipe;
-  if ((int)blockIdx.x * 4 >= total) return;  // no item for this workgroup (uniform)
-  WideItem It;
+  const TableLayout TL = table_layout(QT);
+  const TableRegs tr = tables_load(L.grids, QT);
+  const int ipe = L.inter / kWideRows, stride = gridDim.x * kWideWaves;
+  const int n1 = sload(&work[0].e), total = n1 * ipe;
+  if ((int)blockIdx.x * kWideWaves >= total) return;  // no item for this workgroup (uniform)
+  // the work records and the bank table in LDS: items are issued from there (two LDS
+  // reads) instead of a scalar load and kernel-argument loads each.  The records and
+  // the staged activations go through registers into LDS before any item is issued.
+  WorkRec *recs = (WorkRec *)(lds + TL.bytes + wide_stage_bytes(T));
+  float *xs = (float *)(lds + TL.bytes);
+  {
+    // all copies unconditional (clamped sources), loads first: one wait covers them
+    constexpr int kXf4 = 2048 / 4;  // float4 per token (hidden 2048)
+    const WorkRec r0 = work[1 + min((int)threadIdx.x, n1 - 1)];  // n1 <= MOE_MAX_IDS <= 2 blockDim.x
+    const WorkRec r1 = work[1 + min((int)(threadIdx.x + blockDim.x), n1 - 1)];
+    if (STAGED && threadIdx.x < kXf4) {  // thread i < 512 takes float4 i of every token
+      const float4 *xf = (const float4 *)x + threadIdx.x;
+      const int tl = T - 1;
+      const float4 x0 = xf[0], x1 = xf[min(1, tl) * kXf4], x2 = xf[min(2, tl) * kXf4], x3 = xf[min(3, tl) * kXf4],
+                   x4 = xf[min(4, tl) * kXf4], x5 = xf[min(5, tl) * kXf4], x6 = xf[min(6, tl) * kXf4],
+                   x7 = xf[min(7, tl) * kXf4];
+      const int c = 4 * threadIdx.x;  // column c goes to lane c / 32's slice
+      float4 *d = (float4 *)(xs + (c >> 5) * kXLaneRow + (c & 31));
+      static_assert(kXStageTokens == 8, "eight staged tokens");
+      d[0] = x0, d[kXTokRow / 4] = x1, d[2 * kXTokRow / 4] = x2, d[3 * kXTokRow / 4] = x3;
+      d[4 * kXTokRow / 4] = x4, d[5 * kXTokRow / 4] = x5, d[6 * kXTokRow / 4] = x6, d[7 * kXTokRow / 4] = x7;
+    }
+    recs[threadIdx.x] = r0;
+    if (threadIdx.x + blockDim.x < MOE_MAX_IDS) recs[threadIdx.x + blockDim.x] = r1;
+  }
+  if (threadIdx.x == 0) fill_banks(L, banks);
+  tables_store(tr, QT, TL, lds);  // also publishes the records, the activations and the bank table
+  // three items in flight per wave: A is computed while B and C load.  Items of the
+  // other format are skipped (a layer with both formats runs this kernel once per format).
+  // (items are passed by value: a by-reference hand-off put them in scratch memory, whose
+  // loads share the vector-memory counter and made every item wait for all in flight)
+  auto issue = [&](int it) {
+    WideItem D;
+    D.qt = 0;
+    if (it < total) {
+      const int a = it / ipe;
+      D.W = WorkRec{uniform(recs[a].e), uniform(recs[a].p0), uniform(recs[a].p1), uniform(recs[a].slot0)};
+      const BankLds &Bk = banks[bank_index(L, D.W.e)];
+      if (uniform(Bk.qt) == QT)
+        wide_issue_fmt<QT>(D, bank_mat(Bk, D.W.e, kGate), bank_mat(Bk, D.W.e, kUp), L.hidden, it - a * ipe, q);
+    }
+    return D;
+  };
+  const XSource xsrc = STAGED ? XSource{xs, kXTokRow, kXLaneRow} : XSource{x, L.hidden, 32};
   X32 X;
   int cur_tok = -1;
   bool gs_ok = false;
-  bool have = item < total;
-  if (have) {
-    It.W = rec0;
-    wide_issue(L, It, item - a0 * ipe, q);
-    cur_tok = It.W.slot0 / kprime;
-    load_x32(x + (size_t)cur_tok * L.hidden + 32 * q, X);
-  }
-  tables_store(tr, formats, TL, lds);
-  while (have) {
-    if (It.W.p1 - It.W.p0 <= max_tokens) {
-      if (It.qt == MOE_Q_IQ2XS_LIKE)
-        wide_run<MOE_Q_IQ2XS_LIKE>(L, It, X, cur_tok, gs_ok, q, kprime, x, sorted_slot, lds, TL, h);
-      else
-        wide_run<MOE_Q_IQ1M_LIKE>(L, It, X, cur_tok, gs_ok, q, kprime, x, sorted_slot, lds, TL, h);
-    }
-    item += stride;
-    have = item < total;
-    if (have) {
-      const int a = item / ipe;
-      It.W = load_work(work, 1 + a);
-      wide_issue(L, It, item - a * ipe, q);
-    }
+  auto run = [&](WideItem &D) {
+    if (D.qt == QT && D.W.p1 - D.W.p0 <= max_tokens)
+      wide_run<QT>(L, D, X, cur_tok, gs_ok, q, kprime, xsrc, sorted_slot, lds, TL, h);
+  };
+  // unrolled by three so that each buffer keeps its registers (no copies between them)
+  int it = blockIdx.x * kWideWaves + wave;
+  if (it >= total) return;
+  WideItem A = issue(it), B = issue(it + stride), C;
+  for (;;) {
+    C = issue(it + 2 * stride);
+    run(A);
+    if ((it += stride) >= total) break;
+    A = issue(it + 2 * stride);
+    run(B);
+    if ((it += stride) >= total) break;
+    B = issue(it + 2 * stride);
+    run(C);
+    if ((it += stride) >= total) break;
   }
 }
 
@@ -346,8 +402,32 @@ hipError_t launch_gateup_gemv(const LayerArgs &L, const float *x, int T, int kpr
   const long max_active = n_ids < (long)T * kprime ? n_ids : (long)T * kprime;
   const size_t shmem = table_layout(layer_formats(L)).bytes;
   if (L.hidden == 2048) {
-    hipLaunchKernelGGL(k_gateup_wide, dim3(grid_for_passes(max_active * (L.inter / kWideRows))), dim3(256), shmem, s,
-                       L, x, kprime, sorted_slot, work, max_tokens, n_ids, h);
+    int dev = 0, cus = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err != hipSuccess) return err;
+    const long need = (max_active * (L.inter / kWideRows) + kWideWaves - 1) / kWideWaves;
+    const unsigned grid = (unsigned)(need < cus ? need : cus);
+    const size_t recs = kWideRecsBytes;
+    const dim3 g(grid < 1 ? 1 : grid), b(64 * kWideWaves);
+    for (int qt : {MOE_Q_IQ2XS_LIKE, MOE_Q_IQ1M_LIKE}) {
+      if (!(L.formats & qt)) continue;
+      const size_t bytes = table_layout(qt).bytes + wide_stage_bytes(T) + recs;
+      if (T <= kXStageTokens && qt == MOE_Q_IQ2XS_LIKE)
+        hipLaunchKernelGGL((k_gateup_wide<true, MOE_Q_IQ2XS_LIKE>), g, b, bytes, s, L, x, T, kprime, sorted_slot, work,
+                           max_tokens, n_ids, h);
+      else if (T <= kXStageTokens)
+        hipLaunchKernelGGL((k_gateup_wide<true, MOE_Q_IQ1M_LIKE>), g, b, bytes, s, L, x, T, kprime, sorted_slot, work,
+                           max_tokens, n_ids, h);
+      else if (qt == MOE_Q_IQ2XS_LIKE)
+        hipLaunchKernelGGL((k_gateup_wide<false, MOE_Q_IQ2XS_LIKE>), g, b, bytes, s, L, x, T, kprime, sorted_slot, work,
+                           max_tokens, n_ids, h);
+      else
+        hipLaunchKernelGGL((k_gateup_wide<false, MOE_Q_IQ1M_LIKE>), g, b, bytes, s, L, x, T, kprime, sorted_slot, work,
+                           max_tokens, n_ids, h);
+      err = hipGetLastError();
+      if (err != hipSuccess) return err;
+    }
     return hipGetLastError();
   }
   MOE_LPR_DISPATCH(lpr, k_gateup, dim3(grid_for_passes(max_active * (L.inter / rpp))), dim3(256), shmem, s, L, x,

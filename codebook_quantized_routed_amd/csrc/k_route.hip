@@ -63,7 +63,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, GroupLds &S) {
 }
 
 // ids: global or LDS.  Must be called by all 1024 threads.
-__device__ void group_block(const int32_t *ids, int n, int n_ids, int32_t *__restrict__ counts,
+__device__ void group_block(const int32_t *ids, int n, int n_ids, int max_narrow, int32_t *__restrict__ counts,
                             int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_slot,
                             int32_t *__restrict__ slot_pos, WorkRec *__restrict__ work, GroupLds &S) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -88,7 +88,7 @@ __device__ void group_block(const int32_t *ids, int n, int n_ids, int32_t *__res
   }
   const int excl = block_exclusive_scan(c, S);
   const int n_total = S.total;
-  const bool wide = c > MOE_MATVEC_MAX_TOKENS;
+  const bool wide = c > max_narrow;
   const int tiles = wide ? (c + MOE_MFMA_TILE_TOKENS - 1) / MOE_MFMA_TILE_TOKENS : 0;
   const int nex = block_exclusive_scan(c > 0 && !wide ? 1 : 0, S);
   const int n_narrow = S.total;
@@ -152,7 +152,7 @@ __global__ void __launch_bounds__(1024) k_group(const int32_t *__restrict__ ids,
                                                 int32_t *__restrict__ sorted_slot, int32_t *__restrict__ slot_pos,
                                                 WorkRec *__restrict__ work) {
   __shared__ GroupLds S;
-  group_block(ids, T * kprime, n_ids, counts, offsets, sorted_slot, slot_pos, work, S);
+  group_block(ids, T * kprime, n_ids, matvec_max_tokens(T), counts, offsets, sorted_slot, slot_pos, work, S);
 }
 
 // Small batches: top-k and grouping in one workgroup; the ids stay in LDS between them.
@@ -176,9 +176,9 @@ __global__ void __launch_bounds__(1024) k_route_group_small(const float *__restr
                    ids_l + t * kprime, nullptr, TS[wave]);
   __syncthreads();
   if (T * kprime <= kTinySlots)
-    group_tiny(ids_l, T * kprime, E + add_shared, counts, offsets, sorted_slot, slot_pos, work);
+    group_tiny(ids_l, T * kprime, E + add_shared, matvec_max_tokens(T), counts, offsets, sorted_slot, slot_pos, work);
   else
-    group_block(ids_l, T * kprime, E + add_shared, counts, offsets, sorted_slot, slot_pos, work, S);
+    group_block(ids_l, T * kprime, E + add_shared, matvec_max_tokens(T), counts, offsets, sorted_slot, slot_pos, work, S);
 }
 
 #define MOE_VPL_DISPATCH(E, KERNEL, ...)                      \

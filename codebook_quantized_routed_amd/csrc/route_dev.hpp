@@ -195,7 +195,7 @@ __device__ __forceinline__ void topk_wave(const float *__restrict__ l, int E, in
 // records; every thread e counts the slots below and at its id.
 constexpr int kTinySlots = 64;
 
-__device__ inline void group_tiny(const int32_t *ids_l, int n, int n_ids, int32_t *__restrict__ counts,
+__device__ inline void group_tiny(const int32_t *ids_l, int n, int n_ids, int max_narrow, int32_t *__restrict__ counts,
                            int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_slot,
                            int32_t *__restrict__ slot_pos, WorkRec *__restrict__ work) {
   const int lane = threadIdx.x & 63;
@@ -208,7 +208,7 @@ __device__ inline void group_tiny(const int32_t *ids_l, int n, int n_ids, int32_
       same += o == my ? 1 : 0;
       first &= (o == my && j < lane) ? 0 : 1;
     }
-    const bool wide = same > MOE_MATVEC_MAX_TOKENS;
+    const bool wide = same > max_narrow;
     const uint64_t firsts = __ballot(lane < n && first);
     const uint64_t wides = __ballot(lane < n && first && wide);
     // first set: distinct experts below mine; tiles: the tiles of wide experts below mine

@@ -58,15 +58,19 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 #define MOE_MAX_BANKS 4
 #define MOE_MAX_K 16        /* routed experts per token */
 #define MOE_MAX_IDS 1024    /* E + has_shared */
-/* Experts with at most this many tokens in a call run on the mat-vec kernels (each
- * weight decoded once per token); experts with more run on the matrix-core grouped
- * GEMM in tiles of up to MOE_MFMA_TILE_TOKENS tokens (each weight decoded once per
- * tile).  The work list written by moe_route_group keeps the two sets apart. */
+/* Which experts run where.  In a call of T tokens, experts with at most m(T) tokens
+ * run on the mat-vec kernels (each weight decoded once per token, the work spread over
+ * the expert's rows); experts with more run on the matrix-core grouped GEMM in tiles of
+ * up to MOE_MFMA_TILE_TOKENS tokens (each weight decoded once per tile).  m(T) = T for
+ * small batches, T <= MOE_SMALL_BATCH_TOKENS (every expert on the mat-vec kernels: too
+ * few tiles would leave most of the GPU idle), else MOE_MATVEC_MAX_TOKENS.  The work
+ * list written by moe_route_group keeps the two sets apart. */
 #define MOE_MATVEC_MAX_TOKENS 1
+#define MOE_SMALL_BATCH_TOKENS 16
 #define MOE_MFMA_TILE_TOKENS 16
 
 typedef enum {
@@ -149,7 +153,7 @@ size_t moe_workspace_bytes(int32_t T, int32_t kprime, int32_t hidden, int32_t in
  * s = t*kprime + j ordered by (expert id, s); d_slot_pos: its inverse; d_work
  * [moe_work_ints(T, kprime, E + add_shared)]: the work list of the FFN calls, records
  * of 4 ints.  With n_ids = E + add_shared:
- *   record 0 = (n1, T*kprime, n2, nt): n1 experts with 1..MOE_MATVEC_MAX_TOKENS slots,
+ *   record 0 = (n1, T*kprime, n2, nt): n1 experts with 1..m(T) slots (see above),
  *     n2 experts with more, nt tiles;
  *   records 1..n1: (expert id, offsets[e], offsets[e+1], d_sorted_slot[offsets[e]]) of
  *     the first set, ascending id;
@@ -178,7 +182,7 @@ moe_status moe_expert_ffn_q(const moe_layer *layer, const float *d_x, int32_t T,
 /* Gate and up with the SiLU epilogue ("Red Metal dev8", step 4, first half): for every
  * sorted position p as above, d_h[p] = SiLU(Wg_e x_t) * (Wu_e x_t), fp32
  * [T*kprime][inter].  Weights are decoded in registers: experts with at most
- * MOE_MATVEC_MAX_TOKENS tokens on the mat-vec kernel, the others on the matrix cores
+ * m(T) tokens on the mat-vec kernel, the others on the matrix cores
  * (fp16 weights, exact, times activations split into two fp16 halves, fp32 sums;
  * activations must lie within the fp16 range, |x| < 65504). */
 moe_status moe_expert_gateup_q(const moe_layer *layer, const float *d_x, int32_t T, int32_t kprime,

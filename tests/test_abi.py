@@ -42,19 +42,23 @@ def test_binding_constants_match_header():
     assert int(defs["MOE_MAX_K"]) == moe.MAX_K
     assert int(defs["MOE_MAX_IDS"]) == moe.MAX_IDS
     assert int(defs["MOE_MATVEC_MAX_TOKENS"]) == moe.MATVEC_MAX_TOKENS
+    assert int(defs["MOE_SMALL_BATCH_TOKENS"]) == moe.SMALL_BATCH_TOKENS
     assert int(defs["MOE_MFMA_TILE_TOKENS"]) == moe.MFMA_TILE_TOKENS
     assert int(defs["MOE_DECODE_SYNC_BYTES"]) == moe.DECODE_SYNC_BYTES
     assert moe.decode_workspace_bytes(11, 512) - 11 * 512 * 8 == moe.DECODE_SYNC_BYTES
 
 
 def test_version_strings_sizes():
-    assert moe.abi_version() == 4
+    assert moe.abi_version() == 5
     for st in moe.STATUS:
         assert lib.moe_status_string(st)
     assert moe.grids_bytes() >= 512 * 8 + 2048 * 8
     assert moe.workspace_bytes(1, 11, 2048, 512) == 11 * 512 * 4
     # the work list: n_ids + 1 records, then room for the matrix-core tiles
     assert moe.work_ints(1, 11, 513) == 4 * 514                       # one token: no expert above 1 slot
+    assert moe.work_ints(16, 11, 513) == 4 * 514                      # small batch: every expert on the mat-vec path
+    n17 = min(513, 17 * 11 // (moe.MATVEC_MAX_TOKENS + 1))
+    assert moe.work_ints(17, 11, 513) == 4 * (514 + n17 + (17 * 11 + 15) // 16)
     n_wide = min(513, 256 * 10 // (moe.MATVEC_MAX_TOKENS + 1))
     assert moe.work_ints(256, 10, 512) == 4 * (513 + min(512, n_wide) + (2560 + 15) // 16)
     assert moe.work_ints(0, 11, 513) == 0

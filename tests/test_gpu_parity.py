@@ -112,18 +112,19 @@ def test_route_group_bit_exact(T, E, k, shared, zipf):
     np.testing.assert_array_equal(g["offsets"], offsets)
     np.testing.assert_array_equal(g["sorted_slot"], ss)
     np.testing.assert_array_equal(g["slot_pos"], sp)
-    check_work(g["work"], counts, offsets, ss)
+    check_work(g["work"], counts, offsets, ss, T)
 
 
-def check_work(work, counts, offsets, ss):
-    """Work list: record 0 = (n1, slots, n2, tiles); the experts with 1..MATVEC_MAX_TOKENS
-    slots in records 1..n1, ascending id, as (e, offsets[e], offsets[e+1], first slot);
-    after the n_ids + 1 records, the other experts' tiles of MFMA_TILE_TOKENS positions,
-    ascending (id, start)."""
+def check_work(work, counts, offsets, ss, T):
+    """Work list: record 0 = (n1, slots, n2, tiles); the experts with 1..m(T) slots in
+    records 1..n1, ascending id, as (e, offsets[e], offsets[e+1], first slot); after the
+    n_ids + 1 records, the other experts' tiles of MFMA_TILE_TOKENS positions, ascending
+    (id, start)."""
     n_ids = len(counts)
+    m = moe.matvec_max_tokens(T)
     act = np.flatnonzero(counts)
-    narrow = act[counts[act] <= moe.MATVEC_MAX_TOKENS]
-    wide = act[counts[act] > moe.MATVEC_MAX_TOKENS]
+    narrow = act[counts[act] <= m]
+    wide = act[counts[act] > m]
     tiles = [(e, p, min(p + moe.MFMA_TILE_TOKENS, offsets[e + 1]), 0)
              for e in wide for p in range(offsets[e], offsets[e + 1], moe.MFMA_TILE_TOKENS)]
     rec = work.reshape(-1, 4)
@@ -153,7 +154,7 @@ def test_route_ties_and_explicit_mode():
     counts, offsets, ss, sp = O.group(full, 9)
     np.testing.assert_array_equal(g["sorted_slot"], ss)
     np.testing.assert_array_equal(g["offsets"], offsets)
-    check_work(g["work"], counts, offsets, ss)
+    check_work(g["work"], counts, offsets, ss, 2)
 
 
 # ------------------------------------------------------------------------- whole layer
@@ -219,7 +220,7 @@ def test_decode_path_matches_split_path(layers, ogrids, name):
     acc0 = synth.activations(T, H, tag=f"D/{name}/acc")
     a = run_layer(dl, x, k, shared, logits=lg, acc=acc0)
     b = run_layer(dl, x, k, shared, logits=lg, acc=acc0, decode=True)
-    if a["counts"].max() <= moe.MATVEC_MAX_TOKENS:
+    if a["counts"].max() <= moe.matvec_max_tokens(T):  # every expert on the mat-vec kernels
         assert np.array_equal(a["acc"].view(np.uint32), b["acc"].view(np.uint32))
     else:
         ref = O.moe_layer(tab, ogrids, x, k, shared, logits=lg, acc=acc0)
@@ -251,8 +252,9 @@ def test_prefill_field_shape_sampled(grids, ogrids, zipf):
     ids, _ = O.route(lg, k, False)
     np.testing.assert_array_equal(g["ids"], ids)
     counts = g["counts"]
-    log(f"  experts on matrix cores: {(counts > moe.MATVEC_MAX_TOKENS).sum()}, mat-vec: "
-        f"{((counts > 0) & (counts <= moe.MATVEC_MAX_TOKENS)).sum()}, max tokens {counts.max()}")
+    m = moe.matvec_max_tokens(T)
+    log(f"  experts on matrix cores: {(counts > m).sum()}, mat-vec: {((counts > 0) & (counts <= m)).sum()}, "
+        f"max tokens {counts.max()}")
     # sample: the tokens of the busiest expert's first and last pass, plus spread tokens
     busiest = int(np.argmax(counts))
     on_busiest = np.flatnonzero((ids == busiest).any(axis=1))
