@@ -170,7 +170,7 @@ def decode_workspace_bytes(kprime: int, inter: int) -> int:
 def layer_decode_q(layer: Layer, logits, x, k, add_shared, ids, w, counts, offsets, sorted_slot, slot_pos, work, acc,
                    ws, stream=None):
     """One decode step (one token) of the layer in one launch; ws: decode_workspace_bytes
-    bytes, its first 256 zero before the first call."""
+    bytes, zero before the first call (reused as is by later calls)."""
     nbytes = ws.numel() * ws.element_size()
     _check("moe_layer_decode_q",
            lib.moe_layer_decode_q(C.byref(layer), _ptr(logits), _ptr(x), k, add_shared, _ptr(ids), _ptr(w),
