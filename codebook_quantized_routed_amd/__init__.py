@@ -29,6 +29,7 @@ def matvec_max_tokens(T: int) -> int:
     return T if T <= SMALL_BATCH_TOKENS else MATVEC_MAX_TOKENS
 MFMA_TILE_TOKENS = 16  # tokens per matrix-core tile (MOE_MFMA_TILE_TOKENS)
 DECODE_SYNC_BYTES = 4352  # synchronisation words at the start of a decode workspace (MOE_DECODE_SYNC_BYTES)
+MAX_STACK_LAYERS = 256  # MOE_MAX_STACK_LAYERS
 
 STATUS = {0: "MOE_OK", -1: "MOE_E_NULL", -2: "MOE_E_SHAPE", -3: "MOE_E_QTYPE", -4: "MOE_E_ALIGN",
           -5: "MOE_E_WORKSPACE", -6: "MOE_E_HIP"}
@@ -36,7 +37,8 @@ STATUS = {0: "MOE_OK", -1: "MOE_E_NULL", -2: "MOE_E_SHAPE", -3: "MOE_E_QTYPE", -
 EXPORTS = ["moe_abi_version", "moe_status_string", "moe_last_hip_error", "moe_last_hip_error_string", "moe_grids_bytes", "moe_grids_expand", "moe_work_ints", "moe_workspace_bytes",
            "moe_route_group", "moe_expert_ffn_q", "moe_expert_gateup_q", "moe_expert_down_q",
            "moe_expert_down_accumulate_q", "moe_decode_workspace_bytes", "moe_layer_decode_q", "moe_accumulate",
-           "moe_dequant_f32", "moe_rmsnorm"]
+           "moe_dequant_f32", "moe_rmsnorm", "moe_stack_workspace_bytes", "moe_stack_table_bytes", "moe_stack_table",
+           "moe_stack_decode_q"]
 
 
 class MoeError(RuntimeError):
@@ -84,6 +86,10 @@ def _load():
         "moe_accumulate": (C.c_int, [P, P, P, P, i32, i32, i32, P, P]),
         "moe_dequant_f32": (C.c_int, [i32, i32, i32, P, P, P, P, P, P]),
         "moe_rmsnorm": (C.c_int, [P, i32, i32, C.c_float, P, P]),
+        "moe_stack_workspace_bytes": (sz, [i32, i32, i32, i32]),
+        "moe_stack_table_bytes": (sz, [i32]),
+        "moe_stack_table": (C.c_int, [P, i32, P, sz]),
+        "moe_stack_decode_q": (C.c_int, [P, i32, P, P, P, i32, i32, C.c_float, P, P, P, sz, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -190,6 +196,45 @@ def dequant_f32(qtype, rows, cols, s0, s1, s2, grids, out, stream=None):
 
 def rmsnorm(h, T, hidden, eps, x, stream=None):
     _check("moe_rmsnorm", lib.moe_rmsnorm(_ptr(h), T, hidden, eps, _ptr(x), _stream(stream)))
+
+
+def stack_workspace_bytes(n_layers: int, kprime: int, hidden: int, inter: int) -> int:
+    return lib.moe_stack_workspace_bytes(n_layers, kprime, hidden, inter)
+
+
+def stack_table_bytes(n_layers: int) -> int:
+    return lib.moe_stack_table_bytes(n_layers)
+
+
+def stack_layers(layers) -> C.Array:
+    """A host array of the ``Layer`` descriptors of a chain, in order."""
+    arr = (Layer * len(layers))()
+    for i, L in enumerate(layers):
+        arr[i] = L
+    return arr
+
+
+def stack_prepare(layer_array, ws):
+    """Set-up of a stack decode workspace (blocking): zeroes it and copies the layers'
+    table in after the synchronisation words.  ``layer_array`` from ``stack_layers``."""
+    import torch
+    n = len(layer_array)
+    nbytes = stack_table_bytes(n)
+    host = (C.c_uint8 * nbytes)()
+    _check("moe_stack_table", lib.moe_stack_table(layer_array, n, host, nbytes))
+    ws8 = ws.view(torch.uint8)
+    ws8.zero_()
+    ws8[DECODE_SYNC_BYTES:DECODE_SYNC_BYTES + nbytes].copy_(torch.frombuffer(host, dtype=torch.uint8))
+    torch.cuda.synchronize(ws.device)
+
+
+def stack_decode_q(layer_array, logits, h_in, h_out, k, add_shared, eps, ids, w, ws, stream=None):
+    """One decode step of the chain h <- h + MoE_l(RMSNorm(h)) over every layer, one launch;
+    ``ws`` prepared by ``stack_prepare`` with the same layers."""
+    nbytes = ws.numel() * ws.element_size()
+    _check("moe_stack_decode_q",
+           lib.moe_stack_decode_q(layer_array, len(layer_array), _ptr(logits), _ptr(h_in), _ptr(h_out), k,
+                                  int(add_shared), eps, _ptr(ids), _ptr(w), _ptr(ws), nbytes, _stream(stream)))
 
 
 # ----------------------------------------------------------------------------- device data

@@ -1,5 +1,6 @@
 // extern "C" entry points: argument validation on the host, then kernel launches on the
 // caller's stream.  No allocation, no host<->device copies, no synchronization.
+#include <cstring>
 #include <initializer_list>
 
 #include "common.hpp"
@@ -228,6 +229,84 @@ moe_status moe_layer_decode_q(const moe_layer *layer, const float *d_logits, con
   clear_pending();
   return from_hip(launch_layer_decode(L, d_logits, d_x, E, k, add_shared, d_ids, d_w, d_counts, d_offsets,
                                       d_sorted_slot, d_slot_pos, (WorkRec *)d_work, d_acc, d_ws, stream));
+}
+
+size_t moe_stack_table_bytes(int32_t n_layers) {
+  if (n_layers < 1 || n_layers > MOE_MAX_STACK_LAYERS) return 0;
+  return (size_t)n_layers * sizeof(LayerArgs);
+}
+
+size_t moe_stack_workspace_bytes(int32_t n_layers, int32_t kprime, int32_t hidden, int32_t inter) {
+  if (n_layers < 1 || n_layers > MOE_MAX_STACK_LAYERS || kprime < 1 || kprime > MOE_MAX_K + 1 || !width_ok(hidden) ||
+      !width_ok(inter))
+    return 0;
+  return stack_pairs_offset(n_layers) + (size_t)n_layers * ((size_t)kprime * inter + hidden) * sizeof(uint64_t);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Every layer valid and of the one shape the stack kernel runs; each layer's kernel
+// arguments into tab[l] when tab is given, the union of their formats into *formats.
+moe_status check_stack(const moe_layer *layers, int n_layers, LayerArgs *tab, int *formats) {
+  if (!layers) return MOE_E_NULL;
+  if (n_layers < 1 || n_layers > MOE_MAX_STACK_LAYERS) return MOE_E_SHAPE;
+  *formats = 0;
+  for (int l = 0; l < n_layers; l++) {
+    LayerArgs L;
+    const moe_status st = check_layer(&layers[l], &L);
+    if (st != MOE_OK) return st;
+    const moe_layer &a = layers[l], &b = layers[0];
+    if (a.hidden != 2048 || (a.inter != 256 && a.inter != 512) || a.n_experts > 512) return MOE_E_SHAPE;
+    if (a.inter != b.inter || a.n_experts != b.n_experts || a.has_shared != b.has_shared || a.grids != b.grids)
+      return MOE_E_SHAPE;
+    *formats |= L.formats;
+    if (tab) tab[l] = L;
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_stack_table(const moe_layer *layers, int32_t n_layers, void *h_table, size_t table_bytes) {
+  if (!h_table) return MOE_E_NULL;
+  int formats = 0;
+  moe_status st = check_stack(layers, n_layers, nullptr, &formats);
+  if (st != MOE_OK) return st;
+  if (table_bytes < moe_stack_table_bytes(n_layers)) return MOE_E_SHAPE;
+  for (int l = 0; l < n_layers; l++) {  // through a copy: h_table need not be aligned
+    LayerArgs L;
+    st = check_layer(&layers[l], &L);
+    if (st != MOE_OK) return st;
+    memcpy((uint8_t *)h_table + (size_t)l * sizeof(LayerArgs), &L, sizeof(LayerArgs));
+  }
+  return MOE_OK;
+}
+
+moe_status moe_stack_decode_q(const moe_layer *layers, int32_t n_layers, const float *d_logits, const float *d_h_in,
+                              float *d_h_out, int32_t k, int32_t add_shared, float eps, int32_t *d_ids, float *d_w,
+                              void *d_ws, size_t ws_bytes, hipStream_t stream) {
+  if (!d_logits || !d_h_in || !d_h_out || !d_ws) return MOE_E_NULL;
+  if ((d_ids == nullptr) != (d_w == nullptr)) return MOE_E_NULL;
+  const void *ptrs[] = {d_logits, d_h_in, d_h_out, d_ids, d_w, d_ws};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return MOE_E_ALIGN;
+  int formats = 0;
+  const moe_status st = check_stack(layers, n_layers, nullptr, &formats);
+  if (st != MOE_OK) return st;
+  const int E = layers[0].n_experts, H = layers[0].hidden, I = layers[0].inter;
+  if (k < 1 || k > MOE_MAX_K || k > E || add_shared != layers[0].has_shared) return MOE_E_SHAPE;
+  if (!(eps >= 0.0f)) return MOE_E_SHAPE;
+  const uintptr_t a = (uintptr_t)d_h_in, b = (uintptr_t)d_h_out, n = (uintptr_t)H * sizeof(float);
+  if (a < b + n && b < a + n) return MOE_E_SHAPE;
+  if (ws_bytes < moe_stack_workspace_bytes(n_layers, k + add_shared, H, I)) return MOE_E_WORKSPACE;
+  clear_pending();
+  return from_hip(launch_stack_decode((const LayerArgs *)((const uint8_t *)d_ws + fused_sync_bytes()), n_layers,
+                                      formats, (const uint8_t *)layers[0].grids, I, d_logits, d_h_in, d_h_out, E, k, add_shared, eps,
+                                      d_ids, d_w, d_ws, stream));
 }
 
 moe_status moe_accumulate(const float *d_y, const float *d_w, const int32_t *d_ids, const int32_t *d_slot_pos,

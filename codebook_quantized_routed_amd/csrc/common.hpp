@@ -168,6 +168,15 @@ hipError_t launch_down_mfma(const LayerArgs &L, const float *h, int T, int kprim
 hipError_t launch_down_accumulate(const LayerArgs &L, const float *h, int T, int kprime, const int32_t *ids,
                                   const float *w, const int32_t *slot_pos, float *acc, hipStream_t s);
 size_t fused_sync_bytes();
+// Stack workspace: the synchronisation words, the device copy of the layer table (at a
+// 256-byte boundary), then per layer the h pairs [kprime][inter] and the residual
+// pairs [hidden].
+inline size_t stack_pairs_offset(int n_layers) {
+  return ((fused_sync_bytes() + (size_t)n_layers * sizeof(LayerArgs)) + 255) & ~(size_t)255;
+}
+hipError_t launch_stack_decode(const LayerArgs *d_tab, int n_layers, int formats, const uint8_t *grids, int inter,
+                               const float *logits, const float *h_in, float *h_out, int E, int k, int add_shared,
+                               float eps, int32_t *ids, float *w, void *ws, hipStream_t s);
 hipError_t launch_layer_decode(const LayerArgs &L, const float *logits, const float *x, int E, int k, int add_shared,
                                int32_t *ids, float *w, int32_t *counts, int32_t *offsets, int32_t *sorted_slot,
                                int32_t *slot_pos, WorkRec *work, float *acc, void *ws, hipStream_t s);

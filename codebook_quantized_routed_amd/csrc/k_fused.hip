@@ -306,6 +306,241 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
   }
 }
 
+// ============================================================================ stack
+// The decode step of a stack of layers for one token in a single launch:
+// h <- h + MoE_l(RMSNorm(h)) for l = 0 .. L-1 ("Red Lite dev16 — complete
+// full-attention parity", sections "Implemented path" and "Build and field validation":
+// the routed MoE follows the post-attention RMSNorm and feeds the residual stream;
+// cross-layer scheduling is the pages' next step).  Per layer, every workgroup:
+//  1. issues the loads of its gate / up items (waves 0..kDownWaves-1, one item each at
+//     the field shape) -- the routing of the layer is already known;
+//  2. stages the layer's input residual (layer 0: the caller's h; later layers: the
+//     previous layer's output rows, tagged pairs written by every workgroup) and
+//     computes RMSNorm with the arithmetic of k_rmsnorm;
+//  3. runs its gate / up items (h as tagged pairs, as k_layer_decode) while wave
+//     kDownWaves routes the next layer (its logits do not depend on h) and copies the
+//     next layer's bank table;
+//  4. down + the weighted accumulation for its block of output rows, added to the
+//     input residual and stored as tagged pairs for the next layer (the last layer:
+//     plain floats to the caller's output).
+// Each layer has its own h and residual regions in the workspace, so the call's tag
+// alone tells a value of this call from an older one.  The arithmetic is that of
+// k_rmsnorm followed by k_layer_decode, so the result is the same bits as that chain.
+
+struct RouteLds {
+  PosRec pos[kFusedMaxSlots];
+  int32_t ids[kFusedMaxSlots];
+  float w[kFusedMaxSlots];
+  int32_t slot_at[kFusedMaxSlots];
+  int32_t pos_of[kFusedMaxSlots];
+};
+
+struct StackLds {
+  BankLds banks[2][MOE_MAX_BANKS];  // this layer's and the next layer's
+  RouteLds route[2];
+  TopkLds topk;
+  float ydot[kFusedMaxSlots][16];
+  float hres[2048];                 // the layer's input residual
+  float part[4];
+  uint32_t tag;
+};
+
+// One wave: the token's routing of one layer into R (as k_layer_decode's wave 0), the
+// selection also to ids_out / w_out when given.
+__device__ inline void route_wave(const float *logits, const LayerArgs &L, int E, int k, int add_shared,
+                                  int32_t *ids_out, float *w_out, RouteLds &R, TopkLds &T) {
+  const int lane = threadIdx.x & 63, kprime = k + add_shared;
+  const TopkVals<8> tv = topk_load<8>(logits, E);
+  topk_select<8>(tv, E, k, add_shared, ids_out, w_out, R.ids, R.w, T);
+  __builtin_amdgcn_wave_barrier();
+  const int my = lane < kprime ? R.ids[lane] : 0x7FFFFFFF;
+  int rank = 0;
+  for (int j = 0; j < kprime; j++) {
+    const int o = __builtin_amdgcn_readlane(my, j);
+    rank += (o < my || (o == my && j < lane)) ? 1 : 0;
+  }
+  if (lane < kprime) {
+    R.pos_of[lane] = rank;
+    R.slot_at[rank] = lane;
+    R.pos[rank] = PosRec{my, lane, bank_index(L, my), 0};
+  }
+}
+
+// Four residual values (tagged pairs written by other workgroups), read again until
+// all carry the call's tag (bounded).
+__device__ inline float4 load_pairs4(const uint64_t *src, uint32_t tag, FusedSync *s) {
+  uint64_t v[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) v[i] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int spin = 0;; spin++) {
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < 4; i++) ok = ok && (uint32_t)(v[i] >> 32) == tag;
+    if (__ballot(!ok) == 0ull) break;
+    if (spin == kSpinLimit) {
+      if ((threadIdx.x & 63) == 0) __hip_atomic_store(&s->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+      if ((uint32_t)(v[i] >> 32) != tag) v[i] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return make_float4(__uint_as_float((uint32_t)v[0]), __uint_as_float((uint32_t)v[1]), __uint_as_float((uint32_t)v[2]),
+                     __uint_as_float((uint32_t)v[3]));
+}
+
+template <int LPR>
+__global__ void __launch_bounds__(64 * kFusedWaves) k_stack_decode(
+    const LayerArgs *__restrict__ tab, int n_layers, int formats, const uint8_t *__restrict__ grids,
+    const float *__restrict__ logits, const float *__restrict__ h_in, float *__restrict__ h_out, int E, int k,
+    int add_shared, float eps, int32_t *__restrict__ ids_out, float *__restrict__ w_out, FusedSync *__restrict__ sync,
+    uint64_t *__restrict__ hp, uint64_t *__restrict__ rp) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  __shared__ StackLds S;
+  constexpr int H = 2048, I = 64 * LPR, RPP = 64 / LPR, HS = LPR * kChunkPad;
+  constexpr int ipe = I / kWideRows;
+  const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
+  const int kprime = k + add_shared;
+  const TableLayout TL = table_layout(formats);
+  float *hs = (float *)(lds + TL.bytes) + wave * HS;
+  const TableRegs tr = tables_load(grids, formats, threadIdx.x - 64, blockDim.x - 64);
+  uint32_t tag = 0;
+  if (threadIdx.x == 64) tag = call_tag(sync);
+  if (wave == 0) {
+    route_wave(logits, tab[0], E, k, add_shared, blockIdx.x == 0 ? ids_out : nullptr, w_out, S.route[0], S.topk);
+  } else {
+    tables_store(tr, formats, TL, lds, threadIdx.x - 64, blockDim.x - 64, false);
+    if (threadIdx.x == 64) {
+      S.tag = tag;
+      fill_banks(tab[0], S.banks[0]);
+    }
+  }
+  __syncthreads();
+  tag = S.tag;
+
+  const bool item_wave = wave < kDownWaves;  // the last wave routes the next layer instead
+  const int n_items = kprime * ipe, nw = gridDim.x * kDownWaves;
+  const int tiles = H / RPP;
+  int cur = 0;
+  for (int l = 0; l < n_layers; l++, cur ^= 1) {
+    // the lane and item indices are hidden from loop-invariant code motion: hoisted out
+    // of the layer loop, every address derived from them stayed live for all layers
+    int q = lane, item0 = blockIdx.x * kDownWaves + wave;
+    asm volatile("" : "+v"(q));
+    asm volatile("" : "+s"(item0));
+    const int lq = q % LPR, sub = q / LPR;
+    const RouteLds &R = S.route[cur];
+    const BankLds *Bk = S.banks[cur];
+    uint64_t *hpl = hp + (size_t)l * kprime * I;
+    // ---- 1. the wave's gate / up item: loads first (defined on every path, so that the
+    // previous layer's item is not carried around the loop)
+    WideItem It = {};
+    auto issue = [&](int item) {
+      const int p = item / ipe;
+      const int e = uniform(R.pos[p].e), slot = uniform(R.pos[p].slot);
+      const BankLds &B = Bk[uniform(R.pos[p].bank)];
+      It.W = WorkRec{e, p, p + 1, slot};
+      wide_issue_mats(It, bank_mat(B, e, kGate), bank_mat(B, e, kUp), uniform(B.qt), H, item - p * ipe, q);
+    };
+    if (item_wave && item0 < n_items) issue(item0);
+    // ---- 2. the input residual into LDS, and its RMSNorm scale
+    if (threadIdx.x < H / 4) {
+      const float4 v = l == 0 ? ((const float4 *)h_in)[threadIdx.x]
+                              : load_pairs4(rp + (size_t)(l - 1) * H + 4 * threadIdx.x, tag, sync);
+      *(float4 *)&S.hres[4 * threadIdx.x] = v;
+    }
+    __syncthreads();
+    if (threadIdx.x < 256) {  // as k_rmsnorm: 256 threads, columns t, t + 256, ...
+      float ss = 0.0f;
+      for (int c = threadIdx.x; c < H; c += 256) ss = fmaf(S.hres[c], S.hres[c], ss);
+      ss = group_sum<64>(ss);
+      if (lane == 0) S.part[wave] = ss;
+    }
+    __syncthreads();
+    const float tot = (S.part[0] + S.part[1]) + (S.part[2] + S.part[3]);
+    const float rs = 1.0f / sqrtf(tot / (float)H + eps);
+    // ---- 3. gate / up (waves 0 .. kDownWaves-1); the last wave routes the next layer
+    if (item_wave) {
+      X32 X;
+#pragma unroll
+      for (int i = 0; i < 32; i++) X.v[i] = S.hres[32 * lane + i] * rs;
+      for (int item = item0; item < n_items; item += nw) {
+        if (item != item0) issue(item);
+        if (It.qt == MOE_Q_IQ2XS_LIKE)
+          wide_run_one<MOE_Q_IQ2XS_LIKE>(It, X, q, I, lds, TL, hpl, tag);
+        else
+          wide_run_one<MOE_Q_IQ1M_LIKE>(It, X, q, I, lds, TL, hpl, tag);
+      }
+    } else if (l + 1 < n_layers) {
+      route_wave(logits + (size_t)(l + 1) * E, tab[l + 1], E, k, add_shared,
+                 blockIdx.x == 0 && ids_out ? ids_out + (size_t)(l + 1) * kprime : nullptr,
+                 w_out ? w_out + (size_t)(l + 1) * kprime : nullptr, S.route[cur ^ 1], S.topk);
+      if (lane == 0) fill_banks(tab[l + 1], S.banks[cur ^ 1]);
+    }
+    // ---- 4. down + accumulation for the workgroup's block(s) of output rows
+    for (int tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+#pragma unroll 1
+      for (int i = 0; i < kFusedSlotsPerWave; i++) {
+        const int j = wave + kDownWaves * i;
+        if (!item_wave || j >= kprime) break;
+        const PosRec &P = R.pos[uniform(R.pos_of[j])];
+        const BankLds &B = Bk[uniform(P.bank)];
+        const QMat Wd = bank_mat(B, uniform(P.e), kDown);
+        const int qt = uniform(B.qt);
+        const RowRaw Rw = qt == MOE_Q_IQ2XS_LIKE ? load_row<MOE_Q_IQ2XS_LIKE>(Wd, I, tile * RPP + sub, lq)
+                                                 : load_row<MOE_Q_IQ1M_LIKE>(Wd, I, tile * RPP + sub, lq);
+        stage_h_row<LPR>(hpl + (size_t)R.pos_of[j] * I, tag, hs, sync);
+        __builtin_amdgcn_wave_barrier();
+        const float *hrow = hs + lq * kChunkPad;
+        const float v = qt == MOE_Q_IQ2XS_LIKE ? down_slot_dot<MOE_Q_IQ2XS_LIKE, LPR>(Rw, hrow, lq, lds, TL)
+                                               : down_slot_dot<MOE_Q_IQ1M_LIKE, LPR>(Rw, hrow, lq, lds, TL);
+        if (lq == 0) S.ydot[j][sub] = v;
+        __builtin_amdgcn_wave_barrier();  // the staging area is reused by the next slot
+      }
+      __syncthreads();
+      if (threadIdx.x < RPP) {
+        const int r = tile * RPP + threadIdx.x;
+        float a = S.hres[r];
+        for (int p = 0; p < kprime; p++) {
+          const int j = R.slot_at[p];
+          a = __fadd_rn(a, __fmul_rn(R.w[j], S.ydot[j][threadIdx.x]));
+        }
+        if (l + 1 < n_layers)
+          __hip_atomic_store(rp + (size_t)l * H + r, ((uint64_t)tag << 32) | __float_as_uint(a), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        else
+          h_out[r] = a;
+      }
+      __syncthreads();
+    }
+    __syncthreads();  // the next layer rewrites the residual staging and reads the other buffers
+  }
+}
+
+hipError_t launch_stack_decode(const LayerArgs *d_tab, int n_layers, int formats, const uint8_t *grids, int inter,
+                               const float *logits, const float *h_in, float *h_out, int E, int k, int add_shared,
+                               float eps, int32_t *ids, float *w, void *ws, hipStream_t s) {
+  int dev = 0, cus = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (err != hipSuccess) return err;
+  const int kprime = k + add_shared, lpr = inter / 64;
+  FusedSync *sync = (FusedSync *)ws;
+  uint64_t *hp = (uint64_t *)((uint8_t *)ws + stack_pairs_offset(n_layers));
+  uint64_t *rp = hp + (size_t)n_layers * kprime * inter;
+  const dim3 grid((unsigned)(cus < kBarGroup * kBarGroups ? cus : kBarGroup * kBarGroups)), block(64 * kFusedWaves);
+  const size_t lds_bytes = table_layout(formats).bytes + fused_stage_floats(lpr) * sizeof(float);
+  if (lpr == 8)
+    hipLaunchKernelGGL(k_stack_decode<8>, grid, block, lds_bytes, s, d_tab, n_layers, formats, grids, logits, h_in,
+                       h_out, E, k, add_shared, eps, ids, w, sync, hp, rp);
+  else
+    hipLaunchKernelGGL(k_stack_decode<4>, grid, block, lds_bytes, s, d_tab, n_layers, formats, grids, logits, h_in,
+                       h_out, E, k, add_shared, eps, ids, w, sync, hp, rp);
+  return hipGetLastError();
+}
+
 size_t fused_sync_bytes() { return sizeof(FusedSync); }
 
 size_t fused_lds_bytes(const LayerArgs &L) {

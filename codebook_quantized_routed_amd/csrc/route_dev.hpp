@@ -61,7 +61,8 @@ struct TopkLds {
 // removed (key 0 = taken / no value).
 template <int VPL>
 __device__ __forceinline__ void topk_select_rounds(uint32_t (&key)[VPL], int k, TopkLds &S) {
-  const int lane = threadIdx.x & 63;
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
   for (int j = 0; j < k; j++) {
     uint32_t lmax = key[0];
 #pragma unroll
@@ -96,7 +97,10 @@ struct TopkVals {
 
 template <int VPL>
 __device__ __forceinline__ TopkVals<VPL> topk_load(const float *__restrict__ l, int E) {
-  const int lane = threadIdx.x & 63;
+  // hidden from loop-invariant code motion (a kernel that routes in a loop would keep
+  // every lane address and bound live across the loop)
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
   TopkVals<VPL> t;
 #pragma unroll
   for (int i = 0; i < VPL; i++) t.v[i] = l[min(i * 64 + lane, E - 1)];
@@ -107,7 +111,8 @@ template <int VPL>
 __device__ __forceinline__ void topk_select(const TopkVals<VPL> &tv, int E, int k, int add_shared,
                                             int32_t *__restrict__ ids, float *__restrict__ w, int32_t *ids_copy,
                                             float *w_copy, TopkLds &S) {
-  const int lane = threadIdx.x & 63;
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
   uint32_t key[VPL], lmax = 0u;
 #pragma unroll
   for (int i = 0; i < VPL; i++) {

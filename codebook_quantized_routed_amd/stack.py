@@ -9,14 +9,17 @@ are not part of this path, so the chain here is the MoE part of each block alone
 This module only sequences calls of the C ABI (every step runs in the library's
 kernels): per layer, ``moe_rmsnorm`` then either the one-launch decode
 (``moe_layer_decode_q``, one token) or ``moe_route_group`` -> ``moe_expert_ffn_q`` ->
-``moe_accumulate`` (many tokens), with the residual stream as the accumulator.
+``moe_accumulate`` (many tokens), with the residual stream as the accumulator; or, for
+one token, every layer in one launch (``moe_stack_decode_q``), which gives the same bits
+as the per-layer sequence.
 Routing logits are inputs, one [T][E] array per layer (the router network is not part
 of the path).
 """
 from __future__ import annotations
 
 from . import (DeviceLayer, accumulate, decode_workspace_bytes, expert_ffn_q, layer_decode_q, rmsnorm,
-               route_group, work_ints, workspace_bytes)
+               route_group, stack_decode_q, stack_layers, stack_prepare, stack_workspace_bytes, work_ints,
+               workspace_bytes)
 
 RMS_EPS = 1e-6
 
@@ -55,6 +58,7 @@ class LayerStack:
         self.device = layers[0].tensors[0].device
         self._bufs = {}
         self._torch = torch
+        self._stack = None
 
     def buffers(self, T: int) -> dict:
         if T in self._bufs:
@@ -94,6 +98,26 @@ class LayerStack:
         """All layers in order: logits_per_layer[l] routes layer l."""
         for l in range(len(self.layers)):
             self.layer(l, h, logits_per_layer[l], stream)
+
+    def stack_buffers(self) -> dict:
+        """Buffers of the one-launch decode of every layer: the host layer array, the
+        prepared workspace, and each layer's selection (ids, w [L][kprime])."""
+        if self._stack is None:
+            torch, dev = self._torch, self.device
+            n = len(self.layers)
+            arr = stack_layers([l.desc for l in self.layers])
+            ws = torch.zeros(stack_workspace_bytes(n, self.kp, self.H, self.I) // 4, dtype=torch.int32, device=dev)
+            stack_prepare(arr, ws)
+            self._stack = dict(layers=arr, ws=ws, ids=torch.zeros((n, self.kp), dtype=torch.int32, device=dev),
+                               w=torch.zeros((n, self.kp), dtype=torch.float32, device=dev))
+        return self._stack
+
+    def decode(self, h_in, h_out, logits_per_layer, stream=None) -> None:
+        """One token through every layer in one launch: h_out [1][H] <- the chain applied
+        to h_in [1][H] (h_in is not written; the two must not overlap)."""
+        b = self.stack_buffers()
+        stack_decode_q(b["layers"], logits_per_layer, h_in, h_out, self.k, self.shared, self.eps, b["ids"], b["w"],
+                       b["ws"], stream)
 
 
 def device_stack(formats, banks_by_format: dict, grids, hidden: int = 2048, inter: int = 512, n_experts: int = 512,

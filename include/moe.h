@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 5
+#define MOE_ABI_VERSION 6
 #define MOE_MAX_BANKS 4
 #define MOE_MAX_K 16        /* routed experts per token */
 #define MOE_MAX_IDS 1024    /* E + has_shared */
@@ -229,6 +229,53 @@ moe_status moe_layer_decode_q(const moe_layer *layer, const float *d_logits, con
                               int32_t add_shared, int32_t *d_ids, float *d_w, int32_t *d_counts, int32_t *d_offsets,
                               int32_t *d_sorted_slot, int32_t *d_slot_pos, int32_t *d_work, float *d_acc, void *d_ws,
                               size_t ws_bytes, hipStream_t stream);
+
+/* ---- Decode of a residual chain of layers in one launch ("Red Lite dev16 -- complete
+ * full-attention parity", sections "Implemented path" and "Build and field validation":
+ * in the field model each block's routed MoE reads the post-attention RMSNorm of the
+ * hidden state and its output is added back to it; 48 such blocks are stacked).  For
+ * one token, l = 0 .. n_layers-1:
+ *     h_{l+1} = h_l + MoE_l(RMSNorm(h_l)),
+ * with MoE_l routed by its own logits row.  The attention part of the blocks is not
+ * part of this call.
+ *
+ * Workspace, moe_stack_workspace_bytes(n_layers, kprime, hidden, inter) bytes:
+ *   [0, MOE_DECODE_SYNC_BYTES)   synchronisation words, zero before the first call;
+ *   [MOE_DECODE_SYNC_BYTES, +moe_stack_table_bytes(n_layers))   the layer table, copied
+ *                                there by the caller from the host buffer that
+ *                                moe_stack_table filled;
+ *   the rest                     per-layer exchange buffers (any contents).
+ * To set up: zero the workspace, then copy the table in.  A table stays valid while
+ * the layers' device buffers do. */
+#define MOE_MAX_STACK_LAYERS 256
+size_t moe_stack_workspace_bytes(int32_t n_layers, int32_t kprime, int32_t hidden, int32_t inter);
+size_t moe_stack_table_bytes(int32_t n_layers);
+
+/* Host-only: validates the layers for moe_stack_decode_q and writes their table to the
+ * host buffer h_table (table_bytes >= moe_stack_table_bytes(n_layers); no alignment
+ * needed).  Enqueues nothing and touches no device memory. */
+moe_status moe_stack_table(const moe_layer *layers, int32_t n_layers, void *h_table, size_t table_bytes);
+
+/* One decode step of the chain for one token, in one launch.  Each layer computes,
+ * bit for bit, what moe_rmsnorm followed by moe_layer_decode_q with d_acc = the
+ * residual computes (so the chain's result equals that sequence of calls).
+ *   layers [n_layers] (host): the layers whose table the workspace holds, in order;
+ *     every layer has hidden == 2048, the same inter (256 or 512), the same n_experts
+ *     (<= 512) and has_shared, and the same d_grids pointer.
+ *   d_logits [n_layers][E]: router logits of each layer (the router is not part of
+ *     the call).
+ *   d_h_in [hidden]: h_0, read only; d_h_out [hidden]: h_{n_layers}.  The two must
+ *     not overlap (a workgroup with no work in a layer may still be reading d_h_in
+ *     when the last layer's rows are written).
+ *   d_ids / d_w [n_layers][kprime]: each layer's selection as moe_route_group writes
+ *     it, or both NULL.
+ *   eps: RMSNorm epsilon (>= 0).
+ * The synchronisation rules of moe_layer_decode_q apply to the workspace (the error
+ * word at byte 128; after an error zero the workspace and copy the table in again).
+ * Limits: 1 <= n_layers <= MOE_MAX_STACK_LAYERS. */
+moe_status moe_stack_decode_q(const moe_layer *layers, int32_t n_layers, const float *d_logits, const float *d_h_in,
+                              float *d_h_out, int32_t k, int32_t add_shared, float eps, int32_t *d_ids, float *d_w,
+                              void *d_ws, size_t ws_bytes, hipStream_t stream);
 
 /* Weighted accumulation ("Red Metal dev8", step 5: accumulator += router_weight *
  * expert_output after each expert).  d_acc[t][c] (in/out) gets w * y added for each

@@ -45,11 +45,12 @@ def test_binding_constants_match_header():
     assert int(defs["MOE_SMALL_BATCH_TOKENS"]) == moe.SMALL_BATCH_TOKENS
     assert int(defs["MOE_MFMA_TILE_TOKENS"]) == moe.MFMA_TILE_TOKENS
     assert int(defs["MOE_DECODE_SYNC_BYTES"]) == moe.DECODE_SYNC_BYTES
+    assert int(defs["MOE_MAX_STACK_LAYERS"]) == moe.MAX_STACK_LAYERS
     assert moe.decode_workspace_bytes(11, 512) - 11 * 512 * 8 == moe.DECODE_SYNC_BYTES
 
 
 def test_version_strings_sizes():
-    assert moe.abi_version() == 5
+    assert moe.abi_version() == 6
     for st in moe.STATUS:
         assert lib.moe_status_string(st)
     assert moe.grids_bytes() >= 512 * 8 + 2048 * 8
@@ -174,3 +175,48 @@ def test_layer_decode_rejects():
     assert call(d=layer(hidden=1024, n_experts=512)) == -2
     assert call(d=layer(inter=1024)) == -2
     assert call(ws_bytes=ws_need - 4) == -5
+
+
+def test_stack_table_and_rejects():
+    n = 3
+    arr = moe.stack_layers([layer(), layer(), layer()])
+    tb = moe.stack_table_bytes(n)
+    assert tb > 0 and tb % n == 0 and moe.stack_table_bytes(0) == 0 and moe.stack_table_bytes(257) == 0
+    # sync words, the table (rounded up to 256 bytes), then per layer h and residual pairs
+    ws_need = moe.stack_workspace_bytes(n, 11, 2048, 512)
+    assert ws_need == (4352 + tb + 255) // 256 * 256 + n * (11 * 512 + 2048) * 8
+    assert moe.stack_workspace_bytes(0, 11, 2048, 512) == 0
+    assert moe.stack_workspace_bytes(3, 18, 2048, 512) == 0
+    host = (C.c_uint8 * tb)()
+    assert lib.moe_stack_table(arr, n, host, tb) == 0
+    assert any(host)                                    # the table holds the layers' pointers
+    assert lib.moe_stack_table(arr, n, host, tb - 1) == -2
+    assert lib.moe_stack_table(arr, n, None, tb) == -1
+    assert lib.moe_stack_table(None, n, host, tb) == -1
+    assert lib.moe_stack_table(arr, 0, host, tb) == -2
+    for bad, code in ((layer(inter=256), -2),              # layers of different shapes
+                      (layer(grids=A + 256), -2),          # another grid table
+                      (layer(hidden=1024), -2),
+                      (layer(grids=None), -1),
+                      (layer(n_experts=600), -2)):
+        assert lib.moe_stack_table(moe.stack_layers([layer(), bad]), 2, host, tb) == code
+
+    H = 2048 * 4
+
+    def call(arr=arr, n=n, logits=A, h_in=A, h_out=A + H, k=10, add_shared=1, eps=1e-6, ids=A, w=A, ws=A,
+             ws_bytes=ws_need):
+        return lib.moe_stack_decode_q(arr, n, logits, h_in, h_out, k, add_shared, eps, ids, w, ws, ws_bytes, None)
+    assert call(logits=None) == -1
+    assert call(h_in=None) == -1
+    assert call(ws=None) == -1
+    assert call(ids=None) == -1                         # ids and w: both or neither
+    assert call(w=None) == -1
+    assert call(h_out=MIS) == -4
+    assert call(h_out=A) == -2                          # input and output overlap
+    assert call(h_out=A + H - 16) == -2
+    assert call(k=0) == -2
+    assert call(add_shared=0) == -2
+    assert call(eps=float("nan")) == -2
+    assert call(n=0) == -2
+    assert call(ws_bytes=ws_need - 8) == -5
+    assert call(arr=moe.stack_layers([layer(), layer(inter=256), layer()])) == -2

@@ -6,6 +6,11 @@ Every layer is checked against the oracle fed the GPU's own input to that layer,
 check covers each layer without compounding errors over the chain: routing ids
 bit-exact, outputs within 3e-5 of the layer's MoE output norm per row (the 2e-5 bound
 on the layer output, plus one rounding of the residual's own magnitude).
+
+The one-launch decode of the whole chain (moe_stack_decode_q) computes each layer with
+the arithmetic of moe_rmsnorm + moe_layer_decode_q, so it is checked bit for bit
+against that per-layer chain (itself checked against the oracle above), ids and
+weights of every layer included.
 """
 import numpy as np
 import pytest
@@ -118,3 +123,97 @@ def test_stack_decode_graph_replays(chain):
         other = h0.clone()  # eager work between replays
         st.layer(0, other, lg[0])
         torch.cuda.synchronize()
+
+
+def bits(t):
+    return t.cpu().numpy().view(np.uint32)
+
+
+def chain_reference(st, h0, lg):
+    """The per-layer chain from h0: final h and each layer's ids and weights."""
+    h = h0.clone()
+    ids, ws = [], []
+    for l in range(len(st.layers)):
+        st.layer(l, h, lg[l])
+        b = st.buffers(1)
+        ids.append(b["ids"][0].clone())
+        ws.append(b["w"][0].clone())
+    torch.cuda.synchronize()
+    return h, torch.stack(ids), torch.stack(ws)
+
+
+def check_stack_decode(st, h0, lg, what):
+    want, ids, ws = chain_reference(st, h0, lg)
+    out = torch.full_like(h0, float("nan"))
+    log(f"stack one-launch decode: {what}, {len(st.layers)} layers")
+    st.decode(h0, out, lg)
+    torch.cuda.synchronize()
+    b = st.stack_buffers()
+    np.testing.assert_array_equal(b["ids"].cpu().numpy(), ids.cpu().numpy(), err_msg=what)
+    assert np.array_equal(bits(b["w"]), bits(ws)), what
+    assert np.array_equal(bits(out), bits(want)), f"{what}: max diff {(out - want).abs().max().item():.3e}"
+    assert int(b["ws"][32].item()) == 0, f"{what}: a wait timed out"   # error word at byte 128
+    return out
+
+
+def test_stack_one_launch_matches_chain(chain):
+    formats, st, tabs = chain
+    lg = dev(synth.logits(N_LAYERS, 512, tag="stack-test/one/l").reshape(N_LAYERS, 1, 512))
+    h0 = dev(synth.activations(1, 2048, tag="stack-test/one/h"))
+    first = check_stack_decode(st, h0, lg, "first call")
+    again = check_stack_decode(st, h0, lg, "second call")        # the next call's tags
+    assert np.array_equal(bits(first), bits(again))
+    h1 = dev(synth.activations(1, 2048, tag="stack-test/one/h1"))
+    check_stack_decode(st, h1, lg, "another input")
+
+
+def test_stack_one_launch_graph_replays(chain):
+    formats, st, tabs = chain
+    lg = dev(synth.logits(N_LAYERS, 512, tag="stack-test/onegraph/l").reshape(N_LAYERS, 1, 512))
+    h0 = dev(synth.activations(1, 2048, tag="stack-test/onegraph/h"))
+    want, _, _ = chain_reference(st, h0, lg)
+    st.stack_buffers()                                           # set-up outside the capture
+    out = torch.zeros_like(h0)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            st.decode(h0, out, lg)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        log(f"stack one-launch graph replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out), bits(want)), f"replay {rep}"
+        other = torch.zeros_like(h0)                             # eager work between replays
+        st.decode(h0, other, lg)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(other), bits(want)), f"eager after replay {rep}"
+
+
+@pytest.fixture(scope="module")
+def small_chain(grids_compact):
+    """inter 256, 64 experts, no shared expert, k = 4; the middle layer holds both
+    formats (experts 0-31 IQ2_XS-like, 32-63 IQ1_M-like)."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    grids = device_grids(*grids_compact)
+    kw = dict(inter=256, n_experts=64, has_shared=0)
+    specs = [[(1, 64)], [(1, 32), (2, 32)], [(2, 64)]]
+    layers = []
+    for i, spec in enumerate(specs):
+        h = synth.make_layer(spec, tag=f"stack-test/small{i}", **kw)
+        layers.append(moe.DeviceLayer(h.hidden, h.inter, h.n_experts, h.has_shared, h.banks, grids))
+    yield layers
+
+
+def test_stack_one_launch_small_shape(small_chain):
+    st = S.LayerStack(small_chain, 4)
+    lg = dev(synth.logits(3, 64, tag="stack-test/small/l").reshape(3, 1, 64))
+    h0 = dev(synth.activations(1, 2048, tag="stack-test/small/h"))
+    check_stack_decode(st, h0, lg, "inter 256, mixed formats")
+    one = S.LayerStack(small_chain[1:2], 4)                      # a chain of one layer
+    check_stack_decode(one, h0, lg[1:2], "one layer")
