@@ -112,13 +112,8 @@ def main():
     import synth
 
     banks, T, k, shared, zipf, path, desc = WORKLOADS[args.workload]
-    if path == "stack":
-        return run_stack(args, desc)
-    kp = k + shared
-    n_ids = E + shared
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-
     if args.calib_copy_mb:
         src = torch.ones(args.calib_copy_mb << 18, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -126,6 +121,11 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    if path == "stack":
+        return run_stack(args, desc)
+    kp = k + shared
+    n_ids = E + shared
 
     t0 = time.time()
     layer = synth.make_layer(banks, hidden=H, inter=I, n_experts=E, has_shared=shared, tag="bench/layer")
@@ -402,39 +402,18 @@ def run_stack(args, desc):
     torch.cuda.synchronize()
     pre_ms = e0.elapsed_time(e1) / n_pre
 
-    # ---- decode: 64 steps captured in one graph
+    # ---- the one-launch decode of all layers: the same bits as the per-layer chain
+    hd_out = torch.zeros_like(h_dec0)
+    st.decode(h_dec0[0], hd_out[0], lg_dec[0])
+    torch.cuda.synchronize()
+    one_launch_exact = bool(np.array_equal(hd_out[0].cpu().numpy().view(np.uint32), outs[-1].view(np.uint32)))
+    parity["one_launch_bit_exact_vs_chain"] = one_launch_exact
+    log(f"one-launch decode bit-exact against the per-layer chain: {one_launch_exact}")
+
+    # ---- decode: 64 steps captured in one graph, per-layer chain and one launch
     hd = h_dec0.clone()
-    st.buffers(1)
-    mode = "eager"
-    if not args.no_graph:
-        try:
-            g = torch.cuda.CUDAGraph()
-            s_ = torch.cuda.Stream()
-            s_.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(s_):
-                with torch.cuda.graph(g, stream=s_):
-                    for s in range(ND):
-                        st.step(hd[s], lg_dec[s])
-            torch.cuda.synchronize()
-            g.replay()
-            torch.cuda.synchronize()
-            e0.record()
-            g.replay()
-            e1.record()
-            torch.cuda.synchronize()
-            mode = "hip-graph"
-        except Exception as exc:  # pragma: no cover - reported, then eager timing
-            log(f"graph capture failed ({exc}); timing eager launches")
-    if mode == "eager":
-        for s in range(ND):
-            st.step(hd[s], lg_dec[s])
-        torch.cuda.synchronize()
-        e0.record()
-        for s in range(ND):
-            st.step(hd[s], lg_dec[s])
-        e1.record()
-        torch.cuda.synchronize()
-    dec_ms = e0.elapsed_time(e1) / ND
+    chain_ms, mode = time_decode_steps(args, lambda s: st.step(hd[s], lg_dec[s]), ND)
+    dec_ms, mode = time_decode_steps(args, lambda s: st.decode(h_dec0[s], hd_out[s], lg_dec[s]), ND)
     per_layer_tok_s = nl / (dec_ms * 1e-3)
     achieved = dec_bytes / (dec_ms * 1e-3) / 1e9
     out = {
@@ -454,20 +433,57 @@ def run_stack(args, desc):
                    "experts": E, "shared_experts": shared, "top_k": k, "hidden": H, "inter": I,
                    "prefill_tokens": TP, "decode_steps": ND, "timing": mode},
         "decode": {"us_per_step": round(dec_ms * 1e3, 2), "stack_tokens_per_s": round(1e3 / dec_ms, 1),
+                   "kernel": "k_stack_decode (one launch, 48 layers)",
+                   "per_layer_chain_us_per_step": round(chain_ms * 1e3, 2),
                    "algorithmic_bytes_per_step": int(dec_bytes), "achieved_gbs": round(achieved, 1),
                    "frac_of_hbm_peak": round(achieved / HBM_PEAK_GBS, 4)},
         "prefill": {"ms": round(pre_ms, 3), "tokens_per_s_per_layer": round(TP * nl / (pre_ms * 1e-3), 1),
                     "stack_tokens_per_s": round(TP / (pre_ms * 1e-3), 1)},
-        "roofline": {"bound": "hbm", "kernel": "decode step (48 x (k_rmsnorm + k_layer_decode))",
+        "roofline": {"bound": "hbm", "kernel": "k_stack_decode",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "bytes_per_launch": int(dec_bytes / nl), "launch_us": round(dec_ms * 1e3 / nl, 3)},
+                     "bytes_per_launch": int(dec_bytes), "launch_us": round(dec_ms * 1e3, 3)},
         "parity": parity,
     }
     if not args.no_cpu:
         out["cpu_baseline"] = stack_cpu_baseline(host, formats, c2, c1, h_dec0.cpu().numpy(), lg_host, k, shared,
                                                  args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def time_decode_steps(args, step, n):
+    """Mean time of one decode step: the n steps captured in one graph and replayed once
+    after a warm replay (eager launches with --no-graph or when capture fails)."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if not args.no_graph:
+        try:
+            g = torch.cuda.CUDAGraph()
+            s_ = torch.cuda.Stream()
+            s_.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s_):
+                with torch.cuda.graph(g, stream=s_):
+                    for s in range(n):
+                        step(s)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / n, "hip-graph"
+        except Exception as exc:  # pragma: no cover - reported, then eager timing
+            log(f"graph capture failed ({exc}); timing eager launches")
+    for s in range(n):
+        step(s)
+    torch.cuda.synchronize()
+    e0.record()
+    for s in range(n):
+        step(s)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n, "eager"
 
 
 def check_stack_parity(host, formats, c2, c1, ins, outs, ids_gpu, lg, k, shared, bound=3e-5):

@@ -126,15 +126,23 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
 
 // Sum over each aligned group of `width` consecutive lanes (power of two <= 64); the
 // result is valid in the group's first lane only.  DPP row shifts inside 16-lane rows,
-// then cross-row shuffles; fixed order, so deterministic.
+// then the row sums combined as (r0 + r1) + (r2 + r3); fixed order, so deterministic.
+// The whole wave (width 64) reads the four row sums with readlane instead of two LDS
+// permutes, with the same additions in the same order (the same bits).
 template <int width>
 __device__ __forceinline__ float group_sum_first(float v) {
   if (width >= 2) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x101, 0xf, 0xf, false));
   if (width >= 4) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x102, 0xf, 0xf, false));
   if (width >= 8) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x104, 0xf, 0xf, false));
   if (width >= 16) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x108, 0xf, 0xf, false));
+  if constexpr (width == 64) {
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (r0 + r1) + (r2 + r3);
+  }
   if (width >= 32) v += __shfl_down(v, 16, 64);
-  if (width >= 64) v += __shfl_down(v, 32, 64);
   return v;
 }
 

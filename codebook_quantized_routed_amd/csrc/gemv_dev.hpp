@@ -312,22 +312,29 @@ __device__ __forceinline__ void wide_run(const LayerArgs &L, WideItem &It, X32 &
 
 // The same for an item of exactly one token whose activations are already in X (the
 // one-token decode kernels): h holds tagged pairs, p0 is the item's sorted position.
+// With no token loop there is nothing to hoist, so the rows are not made opaque: all
+// products first, then all sums, so that their latencies overlap.
 template <int QT>
 __device__ __forceinline__ void wide_run_one(const WideItem &It, X32 &X, int q, int I, const uint8_t *lds,
                                              const TableLayout &TL, uint64_t *h, uint32_t tag) {
   if constexpr (QT == MOE_Q_IQ1M_LIKE) group_sums32(X);
+  float vg[kWideRows], vu[kWideRows];
 #pragma unroll
   for (int i = 0; i < kWideRows; i++) {
-    Row32 g = It.g[i], u = It.u[i];
-    opaque(g);
-    opaque(u);
-    float vg = dot32<QT>(g, q, lds, TL, X);
-    float vu = dot32<QT>(u, q, lds, TL, X);
-    vg = group_sum_first<64>(vg);
-    vu = group_sum_first<64>(vu);
-    if (q == 0)
-      __hip_atomic_store(h + (size_t)It.W.p0 * I + It.r0 + i, ((uint64_t)tag << 32) | __float_as_uint(silu(vg) * vu),
-                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    vg[i] = dot32<QT>(It.g[i], q, lds, TL, X);
+    vu[i] = dot32<QT>(It.u[i], q, lds, TL, X);
+  }
+#pragma unroll
+  for (int i = 0; i < kWideRows; i++) {
+    vg[i] = group_sum_first<64>(vg[i]);
+    vu[i] = group_sum_first<64>(vu[i]);
+  }
+  if (q == 0) {
+#pragma unroll
+    for (int i = 0; i < kWideRows; i++)
+      __hip_atomic_store(h + (size_t)It.W.p0 * I + It.r0 + i,
+                         ((uint64_t)tag << 32) | __float_as_uint(silu(vg[i]) * vu[i]), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

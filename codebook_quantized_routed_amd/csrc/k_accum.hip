@@ -43,22 +43,27 @@ hipError_t launch_accumulate(const float *y, const float *w, const int32_t *ids,
 
 // "Red Lite dev16 — complete full-attention parity": the routed MoE reads the
 // post-attention RMSNorm of the hidden state.  One workgroup per row.
-__global__ void __launch_bounds__(256) k_rmsnorm(const float *h, int H, float eps,
+// Thread t of 512 sums, with fmaf in column order, the squares of columns
+// 4t .. 4t+3, 4t+2048 .. 4t+2051, ...; the waves' sums (first lane of a DPP/readlane
+// tree) are combined as ((w0 + w1) + (w2 + w3)) + ((w4 + w5) + (w6 + w7)).  The decode
+// of a stack of layers computes the same scale with the same operations.
+__global__ void __launch_bounds__(512) k_rmsnorm(const float *h, int H, float eps,
                                                  float *x) {  // h and x may alias
-  __shared__ float part[4];
+  __shared__ float part[8];
   const float *hr = h + (size_t)blockIdx.x * H;
   float ss = 0.0f;
-  for (int c = threadIdx.x; c < H; c += blockDim.x) ss = fmaf(hr[c], hr[c], ss);
-  ss = group_sum<64>(ss);
+  for (int c = 4 * threadIdx.x; c < H; c += 2048)
+    for (int j = 0; j < 4 && c + j < H; j++) ss = fmaf(hr[c + j], hr[c + j], ss);
+  ss = group_sum_first<64>(ss);
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
   __syncthreads();
-  float tot = (part[0] + part[1]) + (part[2] + part[3]);
-  float r = 1.0f / sqrtf(tot / (float)H + eps);
+  const float tot = ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
+  const float r = 1.0f / sqrtf(tot / (float)H + eps);
   for (int c = threadIdx.x; c < H; c += blockDim.x) x[(size_t)blockIdx.x * H + c] = hr[c] * r;
 }
 
 hipError_t launch_rmsnorm(const float *h, int T, int H, float eps, float *x, hipStream_t s) {
-  hipLaunchKernelGGL(k_rmsnorm, dim3(T), dim3(256), 0, s, h, H, eps, x);
+  hipLaunchKernelGGL(k_rmsnorm, dim3(T), dim3(512), 0, s, h, H, eps, x);
   return hipGetLastError();
 }
 

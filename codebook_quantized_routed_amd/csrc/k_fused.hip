@@ -312,17 +312,18 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
 // full-attention parity", sections "Implemented path" and "Build and field validation":
 // the routed MoE follows the post-attention RMSNorm and feeds the residual stream;
 // cross-layer scheduling is the pages' next step).  Per layer, every workgroup:
-//  1. issues the loads of its gate / up items (waves 0..kDownWaves-1, one item each at
-//     the field shape) -- the routing of the layer is already known;
-//  2. stages the layer's input residual (layer 0: the caller's h; later layers: the
+//  1. stages the layer's input residual (layer 0: the caller's h; later layers: the
 //     previous layer's output rows, tagged pairs written by every workgroup) and
 //     computes RMSNorm with the arithmetic of k_rmsnorm;
-//  3. runs its gate / up items (h as tagged pairs, as k_layer_decode) while wave
-//     kDownWaves routes the next layer (its logits do not depend on h) and copies the
-//     next layer's bank table;
-//  4. down + the weighted accumulation for its block of output rows, added to the
+//  2. runs its gate / up items (waves 0..kDownWaves-1, one item each at the field
+//     shape; h as tagged pairs, as k_layer_decode) while wave kDownWaves routes the
+//     next layer (its logits do not depend on h) and copies the next layer's bank table;
+//  3. down + the weighted accumulation for its block of output rows, added to the
 //     input residual and stored as tagged pairs for the next layer (the last layer:
-//     plain floats to the caller's output).
+//     plain floats to the caller's output);
+//  4. issues the loads of its first gate / up item of the next layer, whose routing is
+//     now known, so that they arrive during the hand-off of the residual (with fewer
+//     workgroups than row blocks: at the start of the next layer instead).
 // Each layer has its own h and residual regions in the workspace, so the call's tag
 // alone tells a value of this call from an older one.  The arithmetic is that of
 // k_rmsnorm followed by k_layer_decode, so the result is the same bits as that chain.
@@ -341,7 +342,8 @@ struct StackLds {
   TopkLds topk;
   float ydot[kFusedMaxSlots][16];
   float hres[2048];                 // the layer's input residual
-  float part[4];
+  float xs[64 * kXsRow];            // the same values, lane l's 32 at l * kXsRow (no bank conflicts)
+  float part[8];
   uint32_t tag;
 };
 
@@ -390,7 +392,7 @@ __device__ inline float4 load_pairs4(const uint64_t *src, uint32_t tag, FusedSyn
                      __uint_as_float((uint32_t)v[3]));
 }
 
-template <int LPR>
+template <int LPR, bool ONE_TILE>
 __global__ void __launch_bounds__(64 * kFusedWaves) k_stack_decode(
     const LayerArgs *__restrict__ tab, int n_layers, int formats, const uint8_t *__restrict__ grids,
     const float *__restrict__ logits, const float *__restrict__ h_in, float *__restrict__ h_out, int E, int k,
@@ -422,51 +424,65 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_stack_decode(
   const bool item_wave = wave < kDownWaves;  // the last wave routes the next layer instead
   const int n_items = kprime * ipe, nw = gridDim.x * kDownWaves;
   const int tiles = H / RPP;
+  // ONE_TILE: the launch has at least as many workgroups as tiles of output rows
+  // The loads of gate / up item `item` of the layer routed in Rr / Bb.
+  WideItem It = {};
+  auto issue = [&](const RouteLds &Rr, const BankLds *Bb, int item, int q) {
+    const int p = item / ipe;
+    const int e = uniform(Rr.pos[p].e), slot = uniform(Rr.pos[p].slot);
+    const BankLds &B = Bb[uniform(Rr.pos[p].bank)];
+    It.W = WorkRec{e, p, p + 1, slot};
+    wide_issue_mats(It, bank_mat(B, e, kGate), bank_mat(B, e, kUp), uniform(B.qt), H, item - p * ipe, q);
+  };
+  // ---- 1. the wave's first gate / up item of layer 0 (of later layers: issued during
+  // the previous layer's accumulation, as soon as that layer's routing is visible)
+  if (item_wave && blockIdx.x * kDownWaves + wave < n_items) issue(S.route[0], S.banks[0], blockIdx.x * kDownWaves + wave, lane);
   int cur = 0;
   for (int l = 0; l < n_layers; l++, cur ^= 1) {
     // the lane and item indices are hidden from loop-invariant code motion: hoisted out
     // of the layer loop, every address derived from them stayed live for all layers
-    int q = lane, item0 = blockIdx.x * kDownWaves + wave;
+    int q = lane, item0 = blockIdx.x * kDownWaves + wave, tid = threadIdx.x;
     asm volatile("" : "+v"(q));
     asm volatile("" : "+s"(item0));
+    asm volatile("" : "+v"(tid));
     const int lq = q % LPR, sub = q / LPR;
     const RouteLds &R = S.route[cur];
     const BankLds *Bk = S.banks[cur];
     uint64_t *hpl = hp + (size_t)l * kprime * I;
-    // ---- 1. the wave's gate / up item: loads first (defined on every path, so that the
-    // previous layer's item is not carried around the loop)
-    WideItem It = {};
-    auto issue = [&](int item) {
-      const int p = item / ipe;
-      const int e = uniform(R.pos[p].e), slot = uniform(R.pos[p].slot);
-      const BankLds &B = Bk[uniform(R.pos[p].bank)];
-      It.W = WorkRec{e, p, p + 1, slot};
-      wide_issue_mats(It, bank_mat(B, e, kGate), bank_mat(B, e, kUp), uniform(B.qt), H, item - p * ipe, q);
-    };
-    if (item_wave && item0 < n_items) issue(item0);
-    // ---- 2. the input residual into LDS, and its RMSNorm scale
-    if (threadIdx.x < H / 4) {
-      const float4 v = l == 0 ? ((const float4 *)h_in)[threadIdx.x]
-                              : load_pairs4(rp + (size_t)(l - 1) * H + 4 * threadIdx.x, tag, sync);
-      *(float4 *)&S.hres[4 * threadIdx.x] = v;
+    if constexpr (!ONE_TILE) {
+      if (l > 0) It = WideItem{};  // not carried around the loop
+      if (l > 0 && item_wave && item0 < n_items) issue(R, Bk, item0, q);
     }
-    __syncthreads();
-    if (threadIdx.x < 256) {  // as k_rmsnorm: 256 threads, columns t, t + 256, ...
-      float ss = 0.0f;
-      for (int c = threadIdx.x; c < H; c += 256) ss = fmaf(S.hres[c], S.hres[c], ss);
-      ss = group_sum<64>(ss);
+    // ---- 2. the input residual into LDS, and its RMSNorm scale
+    if (tid < H / 4) {  // as k_rmsnorm: thread t squares columns 4t .. 4t+3
+      const float4 v = l == 0 ? ((const float4 *)h_in)[tid]
+                              : load_pairs4(rp + (size_t)(l - 1) * H + 4 * tid, tag, sync);
+      *(float4 *)&S.hres[4 * tid] = v;
+      *(float4 *)&S.xs[(tid >> 3) * kXsRow + (tid & 7) * 4] = v;
+      float ss = fmaf(v.x, v.x, 0.0f);
+      ss = fmaf(v.y, v.y, ss);
+      ss = fmaf(v.z, v.z, ss);
+      ss = fmaf(v.w, v.w, ss);
+      ss = group_sum_first<64>(ss);
       if (lane == 0) S.part[wave] = ss;
     }
     __syncthreads();
-    const float tot = (S.part[0] + S.part[1]) + (S.part[2] + S.part[3]);
+    const float tot =
+        ((S.part[0] + S.part[1]) + (S.part[2] + S.part[3])) + ((S.part[4] + S.part[5]) + (S.part[6] + S.part[7]));
     const float rs = 1.0f / sqrtf(tot / (float)H + eps);
     // ---- 3. gate / up (waves 0 .. kDownWaves-1); the last wave routes the next layer
     if (item_wave) {
       X32 X;
 #pragma unroll
-      for (int i = 0; i < 32; i++) X.v[i] = S.hres[32 * lane + i] * rs;
+      for (int i = 0; i < 8; i++) {
+        const float4 f = *(const float4 *)&S.xs[lane * kXsRow + 4 * i];
+        X.v[4 * i] = f.x * rs;
+        X.v[4 * i + 1] = f.y * rs;
+        X.v[4 * i + 2] = f.z * rs;
+        X.v[4 * i + 3] = f.w * rs;
+      }
       for (int item = item0; item < n_items; item += nw) {
-        if (item != item0) issue(item);
+        if (item != item0) issue(R, Bk, item, q);
         if (It.qt == MOE_Q_IQ2XS_LIKE)
           wide_run_one<MOE_Q_IQ2XS_LIKE>(It, X, q, I, lds, TL, hpl, tag);
         else
@@ -479,7 +495,7 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_stack_decode(
       if (lane == 0) fill_banks(tab[l + 1], S.banks[cur ^ 1]);
     }
     // ---- 4. down + accumulation for the workgroup's block(s) of output rows
-    for (int tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+    auto tile_down = [&](int tile) {
 #pragma unroll 1
       for (int i = 0; i < kFusedSlotsPerWave; i++) {
         const int j = wave + kDownWaves * i;
@@ -499,12 +515,14 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_stack_decode(
         __builtin_amdgcn_wave_barrier();  // the staging area is reused by the next slot
       }
       __syncthreads();
-      if (threadIdx.x < RPP) {
-        const int r = tile * RPP + threadIdx.x;
+    };
+    auto tile_accumulate = [&](int tile, bool sync_after) {
+      if (tid < RPP) {
+        const int r = tile * RPP + tid;
         float a = S.hres[r];
         for (int p = 0; p < kprime; p++) {
           const int j = R.slot_at[p];
-          a = __fadd_rn(a, __fmul_rn(R.w[j], S.ydot[j][threadIdx.x]));
+          a = __fadd_rn(a, __fmul_rn(R.w[j], S.ydot[j][tid]));
         }
         if (l + 1 < n_layers)
           __hip_atomic_store(rp + (size_t)l * H + r, ((uint64_t)tag << 32) | __float_as_uint(a), __ATOMIC_RELAXED,
@@ -512,7 +530,24 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_stack_decode(
         else
           h_out[r] = a;
       }
+      if (sync_after) __syncthreads();
+    };
+    const bool next_item = l + 1 < n_layers && item_wave && item0 < n_items;
+    if constexpr (ONE_TILE) {
+      // at most one tile per workgroup: the next layer's first gate / up loads go out as
+      // soon as its routing is visible (after the down barrier), under the accumulation,
+      // the residual hand-off and the RMSNorm
+      if (blockIdx.x < tiles) {
+        tile_down(blockIdx.x);
+        tile_accumulate(blockIdx.x, false);
+      }
+      if (next_item) issue(S.route[cur ^ 1], S.banks[cur ^ 1], item0, q);
       __syncthreads();
+    } else {
+      for (int tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+        tile_down(tile);
+        tile_accumulate(tile, true);
+      }
     }
     __syncthreads();  // the next layer rewrites the residual staging and reads the other buffers
   }
@@ -532,12 +567,11 @@ hipError_t launch_stack_decode(const LayerArgs *d_tab, int n_layers, int formats
   uint64_t *rp = hp + (size_t)n_layers * kprime * inter;
   const dim3 grid((unsigned)(cus < kBarGroup * kBarGroups ? cus : kBarGroup * kBarGroups)), block(64 * kFusedWaves);
   const size_t lds_bytes = table_layout(formats).bytes + fused_stage_floats(lpr) * sizeof(float);
-  if (lpr == 8)
-    hipLaunchKernelGGL(k_stack_decode<8>, grid, block, lds_bytes, s, d_tab, n_layers, formats, grids, logits, h_in,
-                       h_out, E, k, add_shared, eps, ids, w, sync, hp, rp);
-  else
-    hipLaunchKernelGGL(k_stack_decode<4>, grid, block, lds_bytes, s, d_tab, n_layers, formats, grids, logits, h_in,
-                       h_out, E, k, add_shared, eps, ids, w, sync, hp, rp);
+  const bool one_tile = grid.x >= (unsigned)(2048 / (64 / lpr));
+  auto kern = lpr == 8 ? (one_tile ? k_stack_decode<8, true> : k_stack_decode<8, false>)
+                       : (one_tile ? k_stack_decode<4, true> : k_stack_decode<4, false>);
+  hipLaunchKernelGGL(kern, grid, block, lds_bytes, s, d_tab, n_layers, formats, grids, logits, h_in, h_out, E, k,
+                     add_shared, eps, ids, w, sync, hp, rp);
   return hipGetLastError();
 }
 
