@@ -67,6 +67,9 @@ def lib():
             "orc_moe_layer_f64": (i32, [P, P, P, P, P, P, i32, i32, i32, i32, i32, P, P]),
             "orc_rmsnorm": (i32, [P, i32, i32, C.c_float, P]),
             "orc_rmsnorm_f64": (i32, [P, i32, i32, C.c_double, P]),
+            "orc_router": (i32, [P, P, P, i32, i32, i32, P, P]),
+            "orc_router_f64": (i32, [P, P, P, i32, i32, i32, P, P]),
+            "orc_dot_abs": (i32, [P, P, i32, i32, i32, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -291,3 +294,47 @@ def rmsnorm_f64(h: np.ndarray, eps: float = 1e-6) -> np.ndarray:
 
 def threads_available() -> int:
     return len(os.sched_getaffinity(0))
+
+
+def router(x: np.ndarray, wr: np.ndarray, wsg=None):
+    """Router projection: (logits [T][E] fp32, shared weight [T] fp32 or None)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    wr = np.ascontiguousarray(wr, dtype=np.float32)
+    T, H = x.shape
+    E = wr.shape[0]
+    assert wr.shape == (E, H)
+    lg = np.empty((T, E), np.float32)
+    sw = None
+    if wsg is not None:
+        wsg = np.ascontiguousarray(wsg, dtype=np.float32).reshape(H)
+        sw = np.empty(T, np.float32)
+    _chk(lib().orc_router(_p(x), _p(wr), _p(wsg) if wsg is not None else None, T, H, E, _p(lg),
+                          _p(sw) if sw is not None else None), "router")
+    return lg, sw
+
+
+def router_f64(x: np.ndarray, wr: np.ndarray, wsg=None):
+    """The router projection summed in double: (logits [T][E], shared weight [T] or None)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    wr = np.ascontiguousarray(wr, dtype=np.float32)
+    T, H = x.shape
+    E = wr.shape[0]
+    lg = np.empty((T, E), np.float64)
+    sw = None
+    if wsg is not None:
+        wsg = np.ascontiguousarray(wsg, dtype=np.float32).reshape(H)
+        sw = np.empty(T, np.float64)
+    _chk(lib().orc_router_f64(_p(x), _p(wr), _p(wsg) if wsg is not None else None, T, H, E, _p(lg),
+                              _p(sw) if sw is not None else None), "router_f64")
+    return lg, sw
+
+
+def dot_abs(x: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """sum_c |x[t][c] * w[e][c]| [T][E]: the scale of the rounding error of each dot."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    T, H = x.shape
+    E = w.shape[0]
+    out = np.empty((T, E), np.float64)
+    _chk(lib().orc_dot_abs(_p(x), _p(w), T, H, E, _p(out)), "dot_abs")
+    return out

@@ -454,3 +454,60 @@ int orc_rmsnorm_f64(const double *h, int T, int H, double eps, double *x) {
   }
   return 0;
 }
+
+/* ------------------------------------------------------------------ router projection
+ * "Red Lite dev9 — native runtime foundation", closing paragraph, and "Red Lite dev10 —
+ * standalone native Metal path", section "What dev10 does not yet claim": the router
+ * network that feeds the top-k path is the pages' next step.  Read here as one linear
+ * map, logits[t][e] = sum_c x[t][c] * wr[e][c] (wr row-major [E][H]), plus, optionally,
+ * a gate on the shared expert: s[t] = 1 / (1 + exp(-sum_c x[t][c] * wsg[c])), used as
+ * the shared expert's weight in place of 1.0 (the pages say nothing on such a gate).
+ * fp32 sums in column order, a separate multiply and add per term. */
+
+static float dot_f32(const float *a, const float *b, int n) {
+  float s = 0.0f;
+  for (int c = 0; c < n; c++) {
+    float p = a[c] * b[c];
+    s = s + p;
+  }
+  return s;
+}
+
+static double dot_f64(const float *a, const float *b, int n) {
+  double s = 0.0;
+  for (int c = 0; c < n; c++) s += (double)a[c] * (double)b[c];
+  return s;
+}
+
+int orc_router(const float *x, const float *wr, const float *wsg, int T, int H, int E, float *logits, float *sw) {
+  if (!x || !wr || !logits || T < 1 || H < 1 || E < 1 || (wsg && !sw)) return -1;
+  for (int t = 0; t < T; t++) {
+    const float *xt = x + (size_t)t * H;
+    for (int e = 0; e < E; e++) logits[(size_t)t * E + e] = dot_f32(xt, wr + (size_t)e * H, H);
+    if (wsg) sw[t] = 1.0f / (1.0f + expf(-dot_f32(xt, wsg, H)));
+  }
+  return 0;
+}
+
+int orc_router_f64(const float *x, const float *wr, const float *wsg, int T, int H, int E, double *logits,
+                   double *sw) {
+  if (!x || !wr || !logits || T < 1 || H < 1 || E < 1 || (wsg && !sw)) return -1;
+  for (int t = 0; t < T; t++) {
+    const float *xt = x + (size_t)t * H;
+    for (int e = 0; e < E; e++) logits[(size_t)t * E + e] = dot_f64(xt, wr + (size_t)e * H, H);
+    if (wsg) sw[t] = 1.0 / (1.0 + exp(-dot_f64(xt, wsg, H)));
+  }
+  return 0;
+}
+
+/* Sum of |x[t][c] * w[c]| over c: the scale of a dot product's rounding error. */
+int orc_dot_abs(const float *x, const float *w, int T, int H, int E, double *out) {
+  if (!x || !w || !out || T < 1 || H < 1 || E < 1) return -1;
+  for (int t = 0; t < T; t++)
+    for (int e = 0; e < E; e++) {
+      double s = 0.0;
+      for (int c = 0; c < H; c++) s += fabs((double)x[(size_t)t * H + c] * (double)w[(size_t)e * H + c]);
+      out[(size_t)t * E + e] = s;
+    }
+  return 0;
+}

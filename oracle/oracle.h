@@ -96,6 +96,14 @@ int orc_moe_layer_f64(const orc_expert *experts, const orc_grids *g, const doubl
 int orc_rmsnorm(const float *h, int T, int H, float eps, float *x);
 int orc_rmsnorm_f64(const double *h, int T, int H, double eps, double *x);
 
+/* Router projection: logits [T][E] = x [T][H] times wr [E][H] transposed; with wsg [H]
+ * (else NULL), sw [T] = sigmoid(x . wsg), the shared expert's weight.  fp32 sums in
+ * column order; the _f64 variant sums in double.  orc_dot_abs: sum_c |x[t][c] w[e][c]|. */
+int orc_router(const float *x, const float *wr, const float *wsg, int T, int H, int E, float *logits, float *sw);
+int orc_router_f64(const float *x, const float *wr, const float *wsg, int T, int H, int E, double *logits,
+                   double *sw);
+int orc_dot_abs(const float *x, const float *w, int T, int H, int E, double *out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -238,3 +238,15 @@ def logits(T: int, E: int, seed: int = SEED_INPUT, tag: str = "logits", zipf_alp
         rank[np.argsort(keys, kind="stable")] = np.arange(1, E + 1)
         z = (z.astype(np.float64) - zipf_alpha * np.log(rank)[None, :]).astype(np.float32)
     return np.ascontiguousarray(z)
+
+
+def router_weights(E: int, H: int, seed: int = SEED_BANK, tag: str = "router") -> np.ndarray:
+    """fp32 router matrix [E][H] with entries N(0, 1/H): for activations ~N(0, 1) the
+    logits are then about N(0, 1), the distribution the routed-layer workloads use."""
+    w = normal(seed, tag, E * H).astype(np.float64) / math.sqrt(H)
+    return np.ascontiguousarray(w.astype(np.float32).reshape(E, H))
+
+
+def shared_gate_weights(H: int, seed: int = SEED_BANK, tag: str = "router/shared-gate") -> np.ndarray:
+    """fp32 gate vector [H] of the shared expert, entries N(0, 1/H)."""
+    return router_weights(1, H, seed, tag).reshape(H)
