@@ -53,7 +53,8 @@ KERNEL_SOURCES = ("codebook_quantized_routed_amd/csrc/common.hpp", "codebook_qua
                   "codebook_quantized_routed_amd/csrc/matvec_common.hpp",
                   "codebook_quantized_routed_amd/csrc/gemv_dev.hpp", "codebook_quantized_routed_amd/csrc/route_dev.hpp",
                   "codebook_quantized_routed_amd/csrc/k_fused.hip")
-TRAFFIC_FILES = {"decode_iq2": "profiles/hbm_traffic_decode_iq2_t1.txt"}
+TRAFFIC_FILES = {"decode_iq2": "profiles/hbm_traffic_decode_iq2_t1.txt",
+                 "stack48": "profiles/hbm_traffic_stack48_decode.txt"}
 
 
 def log(msg):
@@ -243,6 +244,27 @@ def main():
     if fused:  # the three-call path of the same steps, for comparison
         kms.update({name: back_to_back(fn) for name, fn in split})
 
+    # ---- the router projection in front of the path (logits from the token's x), timed
+    # alone over ROUTER_COPIES copies of the fp32 router matrix (more bytes than the
+    # last-level cache holds, so each launch reads its matrix from HBM)
+    wr_host = synth.router_weights(E, H, tag="bench/router")
+    wsg_host = synth.shared_gate_weights(H, tag="bench/router/gate")
+    wrs = [torch.from_numpy(wr_host).to(dev) for _ in range(ROUTER_COPIES)]
+    wsg = torch.from_numpy(wsg_host).to(dev) if shared else None
+    rlg = torch.zeros((T, E), dtype=torch.float32, device=dev)
+    rsw = torch.zeros(T, dtype=torch.float32, device=dev) if shared else None
+
+    def k_router(i, b):
+        moe.router_logits(xs[i], wrs[i % ROUTER_COPIES], T, H, E, rlg, wsg, rsw)
+
+    k_router(0, None)
+    torch.cuda.synchronize()
+    router_parity = check_router_parity(xs[0].cpu().numpy(), wr_host, wsg_host if shared else None,
+                                        rlg.cpu().numpy(), None if rsw is None else rsw.cpu().numpy())
+    log(f"router parity: {router_parity}")
+    kms["router"] = back_to_back(k_router)
+    router_bytes = (E + (1 if shared else 0)) * H * 4
+
     # ---- whole-step timing
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     mode = "eager"
@@ -315,6 +337,11 @@ def main():
         dn_name: {"achieved_gbs": round(dn_b / (kms[dn_name] * 1e-3) / 1e9, 1), "bytes_per_launch": int(dn_b),
                   "launch_us": round(kms[dn_name] * 1e3, 3)},
         "route_group": {"launch_us": round(kms["route_group"] * 1e3, 3)},
+        "router": {"kernel": "k_router (logits = x W_r^T, fp32 weights; shared-expert gate)",
+                   "launch_us": round(kms["router"] * 1e3, 3), "bytes_per_launch": router_bytes,
+                   "achieved_gbs": round(router_bytes / (kms["router"] * 1e-3) / 1e9, 1),
+                   "frac_of_hbm_peak": round(router_bytes / (kms["router"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                   "traffic": measured_traffic(args.workload, "k_router"), "parity": router_parity},
         "parity": parity,
     }
     if path == "prefill":
@@ -329,6 +356,25 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def check_router_parity(x, wr, wsg, lg_gpu, sw_gpu, bound=64 * 2.0 ** -24):
+    """GPU logits (and gate) against the oracle's fp64 dots, per element relative to
+    sum_c |x_c w_c| (the scale of an fp32 dot's rounding error)."""
+    import oracle as O
+    l64, s64 = O.router_f64(x, wr, wsg)
+    scale = O.dot_abs(x, wr)
+    worst = float((np.abs(lg_gpu.astype(np.float64) - l64) / scale).max())
+    ok = worst <= bound
+    out = {"logits_checked": int(l64.size), "max_err_over_abs_dot": float(f"{worst:.3e}"), "bound": bound}
+    if wsg is not None:
+        gs = O.dot_abs(x, wsg.reshape(1, -1))[:, 0]
+        gerr = float(np.max(np.abs(sw_gpu.astype(np.float64) - s64) - 0.25 * bound * gs))
+        ok = ok and gerr <= 2.0 ** -23
+        out["gate_checked"] = int(s64.size)
+    out["pass"] = bool(ok)
+    return out
+
+
+ROUTER_COPIES = 80
 STACK_PREFILL_T = 1024
 STACK_DECODE_STEPS = 64
 
@@ -441,7 +487,7 @@ def run_stack(args, desc):
                     "stack_tokens_per_s": round(TP / (pre_ms * 1e-3), 1)},
         "roofline": {"bound": "hbm", "kernel": "k_stack_decode",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic("stack48", "k_stack_decode"),
                      "bytes_per_launch": int(dec_bytes), "launch_us": round(dec_ms * 1e3, 3)},
         "parity": parity,
     }

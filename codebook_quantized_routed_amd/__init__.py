@@ -38,7 +38,7 @@ EXPORTS = ["moe_abi_version", "moe_status_string", "moe_last_hip_error", "moe_la
            "moe_route_group", "moe_expert_ffn_q", "moe_expert_gateup_q", "moe_expert_down_q",
            "moe_expert_down_accumulate_q", "moe_decode_workspace_bytes", "moe_layer_decode_q", "moe_accumulate",
            "moe_dequant_f32", "moe_rmsnorm", "moe_stack_workspace_bytes", "moe_stack_table_bytes", "moe_stack_table",
-           "moe_stack_decode_q"]
+           "moe_stack_decode_q", "moe_router_logits", "moe_shared_weight"]
 
 
 class MoeError(RuntimeError):
@@ -90,6 +90,8 @@ def _load():
         "moe_stack_table_bytes": (sz, [i32]),
         "moe_stack_table": (C.c_int, [P, i32, P, sz]),
         "moe_stack_decode_q": (C.c_int, [P, i32, P, P, P, i32, i32, C.c_float, P, P, P, sz, P]),
+        "moe_router_logits": (C.c_int, [P, P, P, i32, i32, i32, P, P, P]),
+        "moe_shared_weight": (C.c_int, [P, i32, i32, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -196,6 +198,17 @@ def dequant_f32(qtype, rows, cols, s0, s1, s2, grids, out, stream=None):
 
 def rmsnorm(h, T, hidden, eps, x, stream=None):
     _check("moe_rmsnorm", lib.moe_rmsnorm(_ptr(h), T, hidden, eps, _ptr(x), _stream(stream)))
+
+
+def router_logits(x, wr, T, hidden, E, logits, wsg=None, shared_w=None, stream=None):
+    """logits [T][E] = x [T][hidden] wr[E][hidden]^T; with wsg, shared_w [T] = sigmoid(x . wsg)."""
+    _check("moe_router_logits", lib.moe_router_logits(_ptr(x), _ptr(wr), _ptr(wsg), T, hidden, E, _ptr(logits),
+                                                      _ptr(shared_w), _stream(stream)))
+
+
+def shared_weight(shared_w, T, kprime, w, stream=None):
+    """w[t][kprime - 1] = shared_w[t] (the gated shared expert's weight)."""
+    _check("moe_shared_weight", lib.moe_shared_weight(_ptr(shared_w), T, kprime, _ptr(w), _stream(stream)))
 
 
 def stack_workspace_bytes(n_layers: int, kprime: int, hidden: int, inter: int) -> int:

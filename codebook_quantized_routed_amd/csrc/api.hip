@@ -4,6 +4,7 @@
 #include <initializer_list>
 
 #include "common.hpp"
+#include "router.hpp"
 
 using namespace moe;
 
@@ -318,6 +319,26 @@ moe_status moe_accumulate(const float *d_y, const float *d_w, const int32_t *d_i
   if (T < 1 || T > 65536 || kprime < 1 || kprime > MOE_MAX_K + 1 || hidden < 1 || hidden % 256) return MOE_E_SHAPE;
   clear_pending();
   return from_hip(launch_accumulate(d_y, d_w, d_ids, d_slot_pos, T, kprime, hidden, d_acc, stream));
+}
+
+moe_status moe_router_logits(const float *d_x, const float *d_wr, const float *d_wsg, int32_t T, int32_t hidden,
+                             int32_t E, float *d_logits, float *d_shared_w, hipStream_t stream) {
+  if (!d_x || !d_wr || !d_logits) return MOE_E_NULL;
+  if ((d_wsg == nullptr) != (d_shared_w == nullptr)) return MOE_E_NULL;
+  const void *ptrs[] = {d_x, d_wr, d_wsg, d_logits, d_shared_w};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return MOE_E_ALIGN;
+  if (T < 1 || T > 65536 || !width_ok(hidden) || E < 1 || E > MOE_MAX_IDS) return MOE_E_SHAPE;
+  clear_pending();
+  return from_hip(launch_router(d_x, d_wr, d_wsg, T, hidden, E, d_logits, d_shared_w, stream));
+}
+
+moe_status moe_shared_weight(const float *d_shared_w, int32_t T, int32_t kprime, float *d_w, hipStream_t stream) {
+  if (!d_shared_w || !d_w) return MOE_E_NULL;
+  if (!aligned16(d_shared_w) || !aligned16(d_w)) return MOE_E_ALIGN;
+  if (T < 1 || T > 65536 || kprime < 2 || kprime > MOE_MAX_K + 1) return MOE_E_SHAPE;
+  clear_pending();
+  return from_hip(launch_shared_weight(d_shared_w, T, kprime, d_w, stream));
 }
 
 moe_status moe_dequant_f32(int32_t qtype, int32_t rows, int32_t cols, const void *d_s0, const void *d_s1,

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 6
+#define MOE_ABI_VERSION 7
 #define MOE_MAX_BANKS 4
 #define MOE_MAX_K 16        /* routed experts per token */
 #define MOE_MAX_IDS 1024    /* E + has_shared */
@@ -284,6 +284,24 @@ moe_status moe_stack_decode_q(const moe_layer *layers, int32_t n_layers, const f
  * maps a slot to its sorted position. */
 moe_status moe_accumulate(const float *d_y, const float *d_w, const int32_t *d_ids, const int32_t *d_slot_pos,
                           int32_t T, int32_t kprime, int32_t hidden, float *d_acc, hipStream_t stream);
+
+/* Router projection ("Red Lite dev9 — native runtime foundation", closing paragraph, and
+ * "Red Lite dev10 — standalone native Metal path", section "What dev10 does not yet
+ * claim": the router network in front of the top-k path, read as one linear map):
+ *   d_logits[t][e] = sum_c d_x[t][c] * d_wr[e][c]      fp32 [T][E]
+ * d_x [T][hidden] fp32; d_wr [E][hidden] fp32 row-major.  With d_wsg [hidden] (else
+ * NULL), also d_shared_w[t] = 1 / (1 + exp(-sum_c d_x[t][c] * d_wsg[c])), a gate for the
+ * shared expert (the pages say nothing on one; NULL keeps the weight 1.0).  Each dot is
+ * fp32 with a fixed summation order that depends on hidden only, so a token's logits
+ * are the same bits in any batch.  d_wsg and d_shared_w: both or neither.
+ * Limits: 1 <= T <= 65536, hidden in {256, 512, 1024, 2048}, 1 <= E <= MOE_MAX_IDS. */
+moe_status moe_router_logits(const float *d_x, const float *d_wr, const float *d_wsg, int32_t T, int32_t hidden,
+                             int32_t E, float *d_logits, float *d_shared_w, hipStream_t stream);
+
+/* The gated shared expert's weight: d_w[t][kprime - 1] = d_shared_w[t] for every token
+ * (d_w as moe_route_group wrote it with add_shared = 1, whose last slot is the shared
+ * expert with weight 1.0).  Limits: 1 <= T <= 65536, 2 <= kprime <= MOE_MAX_K + 1. */
+moe_status moe_shared_weight(const float *d_shared_w, int32_t T, int32_t kprime, float *d_w, hipStream_t stream);
 
 /* Bit-exact dequantization of one matrix to fp32, row-major rows x cols (debug/test). */
 moe_status moe_dequant_f32(int32_t qtype, int32_t rows, int32_t cols, const void *d_s0, const void *d_s1,

@@ -50,7 +50,7 @@ def test_binding_constants_match_header():
 
 
 def test_version_strings_sizes():
-    assert moe.abi_version() == 6
+    assert moe.abi_version() == 7
     for st in moe.STATUS:
         assert lib.moe_status_string(st)
     assert moe.grids_bytes() >= 512 * 8 + 2048 * 8
@@ -220,3 +220,21 @@ def test_stack_table_and_rejects():
     assert call(n=0) == -2
     assert call(ws_bytes=ws_need - 8) == -5
     assert call(arr=moe.stack_layers([layer(), layer(inter=256), layer()])) == -2
+
+
+def test_router_rejects():
+    def call(x=A, wr=A, wsg=A, T=1, H=2048, E=512, lg=A, sw=A):
+        return lib.moe_router_logits(x, wr, wsg, T, H, E, lg, sw, None)
+    assert call(x=None) == -1
+    assert call(lg=None) == -1
+    assert call(wsg=None) == -1                         # gate vector and gate output: both or neither
+    assert call(sw=None) == -1
+    assert call(wr=MIS) == -4
+    assert call(T=0) == -2
+    assert call(H=300) == -2
+    assert call(E=0) == -2
+    assert call(E=1025) == -2
+    assert lib.moe_shared_weight(None, 1, 11, A, None) == -1
+    assert lib.moe_shared_weight(A, 1, 1, A, None) == -2
+    assert lib.moe_shared_weight(A, 0, 11, A, None) == -2
+    assert lib.moe_shared_weight(A, 1, 11, MIS, None) == -4
