@@ -13,7 +13,7 @@ import numpy as np
 
 from . import build as _build
 
-IQ2XS, IQ1M = 1, 2
+IQ2XS, IQ1M, IQ1S = 1, 2, 4
 
 
 class QMat(C.Structure):

@@ -60,6 +60,9 @@ int orc_grids_expand(const uint16_t *c2, const uint16_t *c1, orc_grids *g) {
  * IQ1_M-like, per 8 weights an 11-bit grid index and a delta sign, a 3-bit scale per
  * 16 weights and an fp16 scale per 256 weights:
  *     w = d * (2s + 1) * (grid[idx][j] +/- 0.125)
+ * IQ1_S-like ("Red Lite dev10", section "Quant grids": IQ1_M reuses the IQ1_S grid; the
+ * packing is a reading): the same grid and formula, but one 3-bit scale and one delta
+ * sign per 32 weights, packed with the four groups' index high bits in a u16. 
  * Both products have at most 22 significant bits, so they are exact in fp32. */
 
 static int popcount7(unsigned v) {
@@ -87,6 +90,16 @@ static wparts weight_parts(const orc_qmat *m, const orc_grids *g, int r, int c) 
     p.d = (double)orc_f16_to_f32(dh);
     p.scale = (double)(2 * s + 1) * 0.125;
     p.value = neg ? -gv : gv;
+  } else if (m->qtype == ORC_IQ1S) {
+    uint8_t ql = ((const uint8_t *)m->s0)[(size_t)r * ng + grp];
+    uint16_t qh = ((const uint16_t *)m->s1)[(size_t)r * (ng / 4) + grp / 4];
+    uint16_t dh = ((const uint16_t *)m->s2)[(size_t)r * nb + b];
+    unsigned idx = ql | (((qh >> (3 * (grp % 4))) & 7u) << 8);
+    int dneg = (qh >> 15) & 1;
+    int s = (qh >> 12) & 7;
+    p.d = (double)orc_f16_to_f32(dh);
+    p.scale = (double)(2 * s + 1);
+    p.value = (double)g->iq1[idx * 8 + j] + (dneg ? -0.125 : 0.125);
   } else {
     uint8_t ql = ((const uint8_t *)m->s0)[(size_t)r * ng + grp];
     uint8_t qhb = ((const uint8_t *)m->s1)[(size_t)r * (ng / 2) + grp / 2];
@@ -114,7 +127,7 @@ double orc_weight_f64(const orc_qmat *m, const orc_grids *g, int r, int c) {
 
 static int check_mat(const orc_qmat *m) {
   if (!m || !m->s0 || !m->s1 || !m->s2) return -1;
-  if (m->qtype != ORC_IQ2XS && m->qtype != ORC_IQ1M) return -3;
+  if (m->qtype != ORC_IQ2XS && m->qtype != ORC_IQ1M && m->qtype != ORC_IQ1S) return -3;
   if (m->rows <= 0 || m->cols <= 0 || m->cols % 256) return -2;
   return 0;
 }

@@ -29,7 +29,7 @@
 extern "C" {
 #endif
 
-enum { ORC_IQ2XS = 1, ORC_IQ1M = 2 };
+enum { ORC_IQ2XS = 1, ORC_IQ1M = 2, ORC_IQ1S = 4 };
 
 typedef struct {
   int32_t qtype, rows, cols, pad_;

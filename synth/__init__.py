@@ -26,6 +26,13 @@ IQ1_M-like (qtype 2), 56 bytes per 256 weights:
   sd  u64[rows][NB]    bits 0-15 binary16 d; bits 16+3i..18+3i = 3-bit scale of the
                        16-weight sub-block i
 
+IQ1_S-like (qtype 4), 50 bytes per 256 weights, the same 2048 x 8 ternary grid:
+  ql  u8[rows][NG]     grid index bits 0-7
+  qh  u16[rows][NG/4]  one word per 32-weight sub-block: bits 3i..3i+2 = index bits
+                       8-10 of the sub-block's group i (i = 0..3), bits 12-14 = 3-bit
+                       scale, bit 15 = delta sign of the whole sub-block (1 = minus)
+  d   u16[rows][NB]    binary16 super-block scale
+
 Compact grids: one u16 per grid row, symbol j (0, 1 or 2) in bits 2j..2j+1.
 IQ2_XS-like: 512 distinct rows; IQ1_M-like: 2048 distinct rows.
 """
@@ -38,7 +45,8 @@ import numpy as np
 
 QTYPE_IQ2XS = 1
 QTYPE_IQ1M = 2
-QTYPE_NAMES = {QTYPE_IQ2XS: "iq2xs", QTYPE_IQ1M: "iq1m"}
+QTYPE_IQ1S = 4
+QTYPE_NAMES = {QTYPE_IQ2XS: "iq2xs", QTYPE_IQ1M: "iq1m", QTYPE_IQ1S: "iq1s"}
 
 GRID_ROWS = {QTYPE_IQ2XS: 512, QTYPE_IQ1M: 2048}
 
@@ -137,6 +145,8 @@ def stream_bytes(qtype: int, rows: int, cols: int) -> tuple[int, int, int]:
         return rows * ng * 2, rows * nb * 4, rows * nb * 2
     if qtype == QTYPE_IQ1M:
         return rows * ng, rows * ng // 2, rows * nb * 8
+    if qtype == QTYPE_IQ1S:
+        return rows * ng, rows * (ng // 4) * 2, rows * nb * 2
     raise ValueError(f"unknown qtype {qtype}")
 
 
@@ -145,7 +155,8 @@ def matrix_bytes(qtype: int, rows: int, cols: int) -> int:
 
 
 # d0 * U(0.75, 1.25) with d0 = C / sqrt(cols) puts the weight RMS near 1/sqrt(cols).
-_D_CONST = {QTYPE_IQ2XS: 3.29e-4 * math.sqrt(2048.0), QTYPE_IQ1M: 2.90e-3 * math.sqrt(2048.0)}
+_D_CONST = {QTYPE_IQ2XS: 3.29e-4 * math.sqrt(2048.0), QTYPE_IQ1M: 2.90e-3 * math.sqrt(2048.0),
+            QTYPE_IQ1S: 2.90e-3 * math.sqrt(2048.0)}
 
 
 def _fp16_scales(seed: int, tag: str, n: int, qtype: int, cols: int) -> np.ndarray:
@@ -160,7 +171,7 @@ def qbank(qtype: int, n: int, rows: int, cols: int, seed: int, tag: str) -> list
     s0 = random_bytes(seed, tag + "/s0", n * b0).reshape(n, b0)
     s1 = random_bytes(seed, tag + "/s1", n * b1).reshape(n, b1)
     nb_total = n * rows * (cols // 256)
-    if qtype == QTYPE_IQ2XS:
+    if qtype in (QTYPE_IQ2XS, QTYPE_IQ1S):
         s2 = _fp16_scales(seed, tag, nb_total, qtype, cols).view(np.uint8).reshape(n, b2).copy()
     else:
         raw = random_bytes(seed, tag + "/s2", n * b2).view(np.uint64).copy()

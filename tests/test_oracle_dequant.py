@@ -154,7 +154,63 @@ def test_iq1_exhaustive_codes_and_scales(ogrids):
     assert len(pairs) == 4096 * 8
 
 
-@pytest.mark.parametrize("qtype", [synth.QTYPE_IQ2XS, synth.QTYPE_IQ1M])
+def encode_iq1s(idx11, dneg32, scales32, d16):
+    """idx11: [rows][NG]; dneg32, scales32: [rows][NG/4] (one per 32-weight sub-block);
+    d16: [rows][NB]."""
+    rows, ng = idx11.shape
+    ql = (idx11 & 0xFF).astype(np.uint8)
+    hi = (idx11 >> 8) & 7
+    qh = (hi[:, 0::4] | (hi[:, 1::4] << 3) | (hi[:, 2::4] << 6) | (hi[:, 3::4] << 9)
+          | (scales32.astype(np.int64) << 12) | (dneg32.astype(np.int64) << 15)).astype(np.uint16)
+    return [ql.ravel(), qh.view(np.uint8).ravel(), d16.astype(np.uint16).view(np.uint8).ravel()]
+
+
+def test_iq1s_exhaustive_codes_and_scales(ogrids):
+    """Every 11-bit index under every (3-bit scale, delta sign) of its sub-block: the
+    weights are d * (2s + 1) * (grid value +/- 1/8), one scale and sign per 32 weights."""
+    rows, cols = 128, 2048
+    ng, nb = cols // 8, cols // 256
+    idx11 = np.arange(rows * ng, dtype=np.int64).reshape(rows, ng) % 2048   # depends on (row % 8, group)
+    # (scale, sign) of sub-block sb of row r: (r // 8 + sb) % 16, so that each index, met
+    # once per 8 rows, sees all 16 combinations over the 128 rows
+    combo = (np.arange(rows)[:, None] // 8 + np.arange(ng // 4)[None, :]) % 16
+    scales32, dneg32 = combo & 7, combo >> 3
+    d = np.full((rows, nb), 0x3C00, dtype=np.uint16)
+    m = O.qmat(O.IQ1S, rows, cols, encode_iq1s(idx11, dneg32, scales32, d))
+    W = O.dequant(m, ogrids)
+    g1 = ogrids.iq1_array()
+    grp = W.reshape(rows, ng, 8)
+    s_of_group = np.repeat(scales32, 4, axis=1)
+    n_of_group = np.repeat(dneg32, 4, axis=1)
+    unit = (2 * s_of_group + 1).astype(np.float32)
+    q = grp / unit[:, :, None]
+    assert np.array_equal(q * unit[:, :, None], grp)
+    delta = np.where(n_of_group.astype(bool), -0.125, 0.125)
+    np.testing.assert_array_equal(q - delta[:, :, None], g1[idx11].astype(np.float32))
+    # every index meets every (scale, sign)
+    triples = np.unique((idx11 * 16 + s_of_group * 2 + n_of_group).ravel())
+    assert len(triples) == 2048 * 16
+
+
+def test_iq1s_equals_iq1m_with_repeated_fields(ogrids):
+    """An IQ1_S-like matrix and the IQ1_M-like matrix whose per-16 scales and per-8 delta
+    signs repeat the per-32 ones dequantize to the same bits (the two formats share the
+    grid and the formula; IQ1_S-like is the coarser packing)."""
+    rows, cols = 32, 512
+    s = synth.qbank(synth.QTYPE_IQ1S, 1, rows, cols, 5, "iq1s-vs-iq1m")
+    ql, qh, d = (a[0] for a in s)
+    ng, nb = cols // 8, cols // 256
+    qh16 = qh.view(np.uint16).reshape(rows, ng // 4).astype(np.int64)
+    idx11 = ql.reshape(rows, ng).astype(np.int64) | (np.stack([(qh16 >> (3 * i)) & 7 for i in range(4)], 2)
+                                                       .reshape(rows, ng) << 8)
+    dneg = np.repeat((qh16 >> 15) & 1, 4, axis=1)
+    sc16 = np.repeat((qh16 >> 12) & 7, 2, axis=1).reshape(rows, nb, 16)
+    m_s = O.qmat(O.IQ1S, rows, cols, [ql, qh, d])
+    m_m = O.qmat(O.IQ1M, rows, cols, encode_iq1(idx11, dneg, sc16, d.view(np.uint16).reshape(rows, nb)))
+    np.testing.assert_array_equal(O.dequant(m_s, ogrids), O.dequant(m_m, ogrids))
+
+
+@pytest.mark.parametrize("qtype", [synth.QTYPE_IQ2XS, synth.QTYPE_IQ1M, synth.QTYPE_IQ1S])
 def test_seeded_weights_alphabet_and_exactness(ogrids, qtype):
     """Seeded matrices: values lie in the scaled alphabet, fp32 == fp64 weight (exactness),
     and doubling every super-block scale doubles every weight bit-exactly."""
@@ -168,7 +224,7 @@ def test_seeded_weights_alphabet_and_exactness(ogrids, qtype):
             assert float(W[r, c]) == O.weight_f64(m, ogrids, r, c)
     # double d: binary16 exponent + 1 (all d are normal and far from the top)
     s2 = streams[2].copy()
-    if qtype == synth.QTYPE_IQ2XS:
+    if qtype in (synth.QTYPE_IQ2XS, synth.QTYPE_IQ1S):
         dd = s2.view(np.uint16)
         dd += np.uint16(1 << 10)
     else:
@@ -184,6 +240,12 @@ def test_seeded_weights_alphabet_and_exactness(ogrids, qtype):
         s_ = np.repeat(nib.reshape(rows, -1), 32, axis=1)
         q = W / (d * (2 * s_ + 1) * 0.125)
         assert set(np.unique(np.abs(q)).tolist()) <= {8.0, 25.0, 43.0}
+    elif qtype == synth.QTYPE_IQ1S:
+        d = np.repeat(streams[2].view(np.float16).astype(np.float32).reshape(rows, cols // 256), 256, axis=1)
+        qh = streams[1].view(np.uint16).reshape(rows, cols // 32).astype(np.int64)
+        s_ = np.repeat((qh >> 12) & 7, 32, axis=1)
+        q = W / (d * (2 * s_ + 1))
+        assert set(np.unique(q).tolist()) <= {-1.125, -0.875, -0.125, 0.125, 0.875, 1.125}
     else:
         sd = streams[2].view(np.uint64).reshape(rows, cols // 256)
         d = np.repeat((sd & np.uint64(0xFFFF)).astype(np.uint16).view(np.float16).astype(np.float32), 256, axis=1)

@@ -67,10 +67,11 @@ def test_permuting_selected_list_is_bit_identical(small, ogrids):
         np.testing.assert_array_equal(got, base)
 
 
-def test_tiny_layer_brute_force_numpy(ogrids):
+@pytest.mark.parametrize("banks", [[(synth.QTYPE_IQ2XS, 2), (synth.QTYPE_IQ1M, 2)],
+                                   [(synth.QTYPE_IQ1S, 2), (synth.QTYPE_IQ2XS, 2)]])
+def test_tiny_layer_brute_force_numpy(ogrids, banks):
     """H = I = 256, E = 4, every expert selected: numpy float64 / scipy softmax reference."""
-    layer = synth.make_layer([(synth.QTYPE_IQ2XS, 2), (synth.QTYPE_IQ1M, 2)], hidden=256, inter=256,
-                             n_experts=4, has_shared=1, tag="tiny")
+    layer = synth.make_layer(banks, hidden=256, inter=256, n_experts=4, has_shared=1, tag="tiny")
     tab = O.ExpertTable(layer)
     T, k = 5, 3
     x = synth.activations(T, 256, tag="tiny/x")
