@@ -39,6 +39,9 @@ WORKLOADS = {
                            "256 tokens, top-10"),
     "prefill_mixed_t256_zipf": ([(1, 256), (2, 256)], 256, 10, 0, 1.1, "prefill",
                                 "as prefill_mixed_t256 with Zipf(1.1)-skewed router logits"),
+    "decode_iq1s": ([(4, 512)], 1, 10, 1, 0.0, "decode",
+                    "decode layer, IQ1_S-like experts (repacked to the IQ1_M-like layout when loaded), hidden 2048, "
+                    "512 experts + 1 shared, inter 512, 1 token, top-10; algorithmic bytes of the IQ1_S-like format"),
     "stack48": (None, 1, 10, 1, 0.0, "stack",
                 "stack of 48 routed layers (11 IQ2_XS-like, 37 IQ1_M-like), 512 experts + 1 shared each, hidden 2048, "
                 "inter 512, top-10, h <- h + MoE(RMSNorm(h)); 1024-token prefill, then 64 single-token decode steps"),

@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 IQ2XS_LIKE = 1
 IQ1M_LIKE = 2
+IQ1S_LIKE = 4  # repacked into IQ1M_LIKE banks when a layer is loaded
 MAX_BANKS = 4
 MAX_K = 16
 MAX_IDS = 1024
@@ -38,7 +39,7 @@ EXPORTS = ["moe_abi_version", "moe_status_string", "moe_last_hip_error", "moe_la
            "moe_route_group", "moe_expert_ffn_q", "moe_expert_gateup_q", "moe_expert_down_q",
            "moe_expert_down_accumulate_q", "moe_decode_workspace_bytes", "moe_layer_decode_q", "moe_accumulate",
            "moe_dequant_f32", "moe_rmsnorm", "moe_stack_workspace_bytes", "moe_stack_table_bytes", "moe_stack_table",
-           "moe_stack_decode_q", "moe_router_logits", "moe_shared_weight"]
+           "moe_stack_decode_q", "moe_router_logits", "moe_shared_weight", "moe_repack_iq1s"]
 
 
 class MoeError(RuntimeError):
@@ -92,6 +93,7 @@ def _load():
         "moe_stack_decode_q": (C.c_int, [P, i32, P, P, P, i32, i32, C.c_float, P, P, P, sz, P]),
         "moe_router_logits": (C.c_int, [P, P, P, i32, i32, i32, P, P, P]),
         "moe_shared_weight": (C.c_int, [P, i32, i32, P, P]),
+        "moe_repack_iq1s": (C.c_int, [P, P, P, i32, i32, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -211,6 +213,12 @@ def shared_weight(shared_w, T, kprime, w, stream=None):
     _check("moe_shared_weight", lib.moe_shared_weight(_ptr(shared_w), T, kprime, _ptr(w), _stream(stream)))
 
 
+def repack_iq1s(ql, qh, d, rows, cols, ql_out, qh_out, sd_out, stream=None):
+    """IQ1_S-like streams of rows x cols -> the IQ1_M-like layout (same weights, exactly)."""
+    _check("moe_repack_iq1s", lib.moe_repack_iq1s(_ptr(ql), _ptr(qh), _ptr(d), rows, cols, _ptr(ql_out), _ptr(qh_out),
+                                                  _ptr(sd_out), _stream(stream)))
+
+
 def stack_workspace_bytes(n_layers: int, kprime: int, hidden: int, inter: int) -> int:
     return lib.moe_stack_workspace_bytes(n_layers, kprime, hidden, inter)
 
@@ -273,11 +281,21 @@ class DeviceLayer:
         self.bytes = 0
         for i, b in enumerate(banks):
             bd = d.banks[i]
-            bd.qtype, bd.first_expert, bd.n_experts = b.qtype, b.first, b.n
+            # IQ1_S-like banks are repacked on the device into the IQ1_M-like layout
+            bd.qtype = IQ1M_LIKE if b.qtype == IQ1S_LIKE else b.qtype
+            bd.first_expert, bd.n_experts = b.first, b.n
             for name in ("gate", "up", "down"):
                 arr = getattr(bd, name)
-                for j, host in enumerate(getattr(b, name)):
-                    t = torch.from_numpy(host.reshape(-1)).to(device)
+                streams = [torch.from_numpy(host.reshape(-1)).to(device) for host in getattr(b, name)]
+                if b.qtype == IQ1S_LIKE:
+                    rows, cols = (inter, hidden) if name != "down" else (hidden, inter)
+                    n_rows = b.n * rows
+                    out = [streams[0], torch.empty(n_rows * cols // 16, dtype=torch.uint8, device=device),
+                           torch.empty(n_rows * cols // 256 * 8, dtype=torch.uint8, device=device)]
+                    repack_iq1s(streams[0], streams[1], streams[2], n_rows, cols, out[0], out[1], out[2])
+                    torch.cuda.synchronize(out[0].device)
+                    streams = out
+                for j, t in enumerate(streams):
                     self.tensors.append(t)
                     self.bytes += t.numel()
                     arr[j] = t.data_ptr()

@@ -4,6 +4,7 @@
 #include <initializer_list>
 
 #include "common.hpp"
+#include "repack.hpp"
 #include "router.hpp"
 
 using namespace moe;
@@ -339,6 +340,20 @@ moe_status moe_shared_weight(const float *d_shared_w, int32_t T, int32_t kprime,
   if (T < 1 || T > 65536 || kprime < 2 || kprime > MOE_MAX_K + 1) return MOE_E_SHAPE;
   clear_pending();
   return from_hip(launch_shared_weight(d_shared_w, T, kprime, d_w, stream));
+}
+
+moe_status moe_repack_iq1s(const void *d_ql, const void *d_qh, const void *d_d, int32_t rows, int32_t cols,
+                           void *d_ql_out, void *d_qh_out, void *d_sd_out, hipStream_t stream) {
+  if (!d_ql || !d_qh || !d_d || !d_ql_out || !d_qh_out || !d_sd_out) return MOE_E_NULL;
+  const void *ptrs[] = {d_ql, d_qh, d_d, d_ql_out, d_qh_out, d_sd_out};
+  for (const void *p : ptrs)
+    if (!aligned16(p)) return MOE_E_ALIGN;
+  if (rows < 1 || cols < 256 || cols % 256) return MOE_E_SHAPE;
+  const size_t n_blocks = (size_t)rows * (cols / 256);
+  if (n_blocks >= ((size_t)1 << 31)) return MOE_E_SHAPE;
+  clear_pending();
+  return from_hip(launch_repack_iq1s((const uint8_t *)d_ql, (const uint16_t *)d_qh, (const uint16_t *)d_d, n_blocks,
+                                     (uint8_t *)d_ql_out, (uint8_t *)d_qh_out, (uint64_t *)d_sd_out, stream));
 }
 
 moe_status moe_dequant_f32(int32_t qtype, int32_t rows, int32_t cols, const void *d_s0, const void *d_s1,

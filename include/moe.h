@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 7
+#define MOE_ABI_VERSION 8
 #define MOE_MAX_BANKS 4
 #define MOE_MAX_K 16        /* routed experts per token */
 #define MOE_MAX_IDS 1024    /* E + has_shared */
@@ -302,6 +302,24 @@ moe_status moe_router_logits(const float *d_x, const float *d_wr, const float *d
  * (d_w as moe_route_group wrote it with add_shared = 1, whose last slot is the shared
  * expert with weight 1.0).  Limits: 1 <= T <= 65536, 2 <= kprime <= MOE_MAX_K + 1. */
 moe_status moe_shared_weight(const float *d_shared_w, int32_t T, int32_t kprime, float *d_w, hipStream_t stream);
+
+/* IQ1_S-like matrices (qtype 4, never passed to the other calls), 50 bytes / 256 weights,
+ * the IQ1_M-like grid: s0 = ql u8[rows][NG] (index bits 0-7); s1 = qh u16[rows][NG/4],
+ * one word per 32-weight sub-block: bits 3i..3i+2 = index bits 8-10 of its group i,
+ * bits 12-14 = 3-bit scale s, bit 15 = delta sign (1 = minus); s2 = d u16[rows][NB].
+ * weight = d * (2s + 1) * (iq1_grid[index][j] +/- 1/8).  ("Red Lite dev10 — standalone
+ * native Metal path", section "Quant grids": IQ1_M reuses the IQ1_S grid; the packing
+ * is a reading.) */
+#define MOE_Q_IQ1S_LIKE 4
+
+/* Repacks IQ1_S-like streams of `rows` rows of `cols` columns (any number of matrices of
+ * one width back to back) into the IQ1_M-like layout, exactly: every weight keeps its
+ * bits (the per-32 scale and sign are repeated per 16 and per 8).  Outputs: ql_out
+ * rows*cols/8 bytes (may equal d_ql), qh_out rows*cols/16 bytes, sd_out rows*cols/256
+ * u64.  Done once when a layer is loaded; the layer then uses MOE_Q_IQ1M_LIKE banks.
+ * Limits: rows >= 1, cols a positive multiple of 256, rows * cols / 256 < 2^31. */
+moe_status moe_repack_iq1s(const void *d_ql, const void *d_qh, const void *d_d, int32_t rows, int32_t cols,
+                           void *d_ql_out, void *d_qh_out, void *d_sd_out, hipStream_t stream);
 
 /* Bit-exact dequantization of one matrix to fp32, row-major rows x cols (debug/test). */
 moe_status moe_dequant_f32(int32_t qtype, int32_t rows, int32_t cols, const void *d_s0, const void *d_s1,

@@ -36,7 +36,7 @@ def test_exports_every_declared_function():
 
 def test_binding_constants_match_header():
     src = open(os.path.join(ROOT, "include", "moe.h")).read()
-    defs = dict(re.findall(r"#define (MOE_[A-Z_]+) (\d+)", src))
+    defs = dict(re.findall(r"#define (MOE_[A-Z0-9_]+) (\d+)", src))
     assert int(defs["MOE_ABI_VERSION"]) == moe.abi_version()
     assert int(defs["MOE_MAX_BANKS"]) == moe.MAX_BANKS
     assert int(defs["MOE_MAX_K"]) == moe.MAX_K
@@ -46,11 +46,12 @@ def test_binding_constants_match_header():
     assert int(defs["MOE_MFMA_TILE_TOKENS"]) == moe.MFMA_TILE_TOKENS
     assert int(defs["MOE_DECODE_SYNC_BYTES"]) == moe.DECODE_SYNC_BYTES
     assert int(defs["MOE_MAX_STACK_LAYERS"]) == moe.MAX_STACK_LAYERS
+    assert int(defs["MOE_Q_IQ1S_LIKE"]) == moe.IQ1S_LIKE
     assert moe.decode_workspace_bytes(11, 512) - 11 * 512 * 8 == moe.DECODE_SYNC_BYTES
 
 
 def test_version_strings_sizes():
-    assert moe.abi_version() == 7
+    assert moe.abi_version() == 8
     for st in moe.STATUS:
         assert lib.moe_status_string(st)
     assert moe.grids_bytes() >= 512 * 8 + 2048 * 8
@@ -238,3 +239,16 @@ def test_router_rejects():
     assert lib.moe_shared_weight(A, 1, 1, A, None) == -2
     assert lib.moe_shared_weight(A, 0, 11, A, None) == -2
     assert lib.moe_shared_weight(A, 1, 11, MIS, None) == -4
+
+
+def test_repack_rejects():
+    def call(ql=A, qh=A, d=A, rows=8, cols=256, o0=A, o1=A, o2=A):
+        return lib.moe_repack_iq1s(ql, qh, d, rows, cols, o0, o1, o2, None)
+    assert call(ql=None) == -1
+    assert call(o2=None) == -1
+    assert call(qh=MIS) == -4
+    assert call(o1=MIS) == -4
+    assert call(rows=0) == -2
+    assert call(cols=300) == -2
+    assert call(cols=0) == -2
+    assert call(rows=1 << 30, cols=2048) == -2        # 2^33 super-blocks

@@ -23,7 +23,7 @@ import synth  # noqa: E402
 from gpu_util import (Run, assert_rows_close, dev, device_grids, device_layer, log, run_layer,  # noqa: E402
                       y_in_slot_order)
 
-IQ2, IQ1 = synth.QTYPE_IQ2XS, synth.QTYPE_IQ1M
+IQ2, IQ1, IQ1S = synth.QTYPE_IQ2XS, synth.QTYPE_IQ1M, synth.QTYPE_IQ1S
 
 
 @pytest.fixture(scope="module")
@@ -173,7 +173,52 @@ LAYER_CASES = {
     "mixed_t128_zipf": ([(IQ2, 32), (IQ1, 32)], 2048, 512, 64, 0, 128, 10, 1.1),
     "mixed_h512_i1024_t48": ([(IQ1, 6), (IQ2, 6)], 512, 1024, 12, 1, 48, 2, 0.0),
     "decode_mixed_i256_shared": ([(IQ2, 20), (IQ1, 12)], 2048, 256, 32, 1, 1, 6, 0.0),
+    # IQ1_S-like banks, repacked into the IQ1_M-like layout when the layer is loaded
+    "decode_iq1s_top10_shared": ([(IQ1S, 512)], 2048, 512, 512, 1, 1, 10, 0.0),
+    "iq1s_mixed_t6": ([(IQ1S, 32), (IQ2, 32)], 2048, 512, 64, 1, 6, 4, 0.0),
+    "dense_iq1s_t40_shared": ([(IQ1S, 8)], 2048, 512, 8, 1, 40, 3, 0.0),
 }
+
+
+def _repack_gpu(rows, cols, streams):
+    ql, qh, d = (dev(a.reshape(-1)) for a in streams)
+    out = [torch.empty(rows * cols // 8, dtype=torch.uint8, device="cuda"),
+           torch.empty(rows * cols // 16, dtype=torch.uint8, device="cuda"),
+           torch.empty(rows * cols // 256 * 8, dtype=torch.uint8, device="cuda")]
+    moe.repack_iq1s(ql, qh, d, rows, cols, *out)
+    return out
+
+
+@pytest.mark.parametrize("n,rows,cols", [(1, 512, 2048), (1, 2048, 512), (3, 512, 2048), (1, 8, 256), (2, 24, 768)])
+def test_repack_iq1s_bit_exact(grids, ogrids, n, rows, cols):
+    """IQ1_S-like streams repacked on the GPU and dequantized as IQ1_M-like == the oracle's
+    dequantization of the IQ1_S-like streams themselves, bit for bit (n matrices back to
+    back, as in a bank)."""
+    log(f"repack iq1s n={n} {rows}x{cols}")
+    s = synth.qbank(IQ1S, n, rows, cols, 9, f"repack/{n}/{rows}/{cols}")
+    out = _repack_gpu(n * rows, cols, s)
+    g = torch.empty((n * rows, cols), dtype=torch.float32, device="cuda")
+    moe.dequant_f32(IQ1, n * rows, cols, out[0], out[1], out[2], grids, g)
+    got = g.cpu().numpy()
+    for e in range(n):
+        ref = O.dequant(O.qmat(IQ1S, rows, cols, [a[e] for a in s]), ogrids)
+        assert np.array_equal(got[e * rows:(e + 1) * rows].view(np.uint32), ref.view(np.uint32)), e
+
+
+def test_repack_iq1s_every_code(grids, ogrids):
+    """Every 11-bit index under every (scale, delta sign) of its sub-block, repacked."""
+    from test_oracle_dequant import encode_iq1s
+    rows, cols = 128, 2048
+    ng, nb = cols // 8, cols // 256
+    idx11 = np.arange(rows * ng, dtype=np.int64).reshape(rows, ng) % 2048
+    combo = (np.arange(rows)[:, None] // 8 + np.arange(ng // 4)[None, :]) % 16
+    d16 = (1e-3 * (0.5 + synth.uniform(3, "repack/d", rows * nb))).astype(np.float16).view(np.uint16).reshape(rows, nb)
+    s = encode_iq1s(idx11, combo >> 3, combo & 7, d16)
+    out = _repack_gpu(rows, cols, s)
+    g = torch.empty((rows, cols), dtype=torch.float32, device="cuda")
+    moe.dequant_f32(IQ1, rows, cols, out[0], out[1], out[2], grids, g)
+    ref = O.dequant(O.qmat(IQ1S, rows, cols, s), ogrids)
+    assert np.array_equal(g.cpu().numpy().view(np.uint32), ref.view(np.uint32))
 
 
 @pytest.fixture(scope="module")
@@ -272,7 +317,8 @@ def call_counts(ws):
     return int(counters.sum()), int(sync.view(np.uint32)[32])
 
 
-FUSED_CASES = ["decode_iq2_top10_shared", "tiny16_top4_iq2", "mixed_h2048_t24_zipf", "decode_mixed_i256_shared"]
+FUSED_CASES = ["decode_iq2_top10_shared", "tiny16_top4_iq2", "mixed_h2048_t24_zipf", "decode_mixed_i256_shared",
+               "decode_iq1s_top10_shared"]
 
 
 @pytest.mark.parametrize("name", FUSED_CASES)
