@@ -23,6 +23,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -51,11 +52,12 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = 2500.0  # dense fp16
 H, I, E = 2048, 512, 512
 ROOT = os.path.dirname(os.path.abspath(__file__))
-# Sources that define the mat-vec kernels; the counter summary below records their digest.
+# Sources of the kernels whose traffic the counter summaries record, with the digest of their code.
 KERNEL_SOURCES = ("codebook_quantized_routed_amd/csrc/common.hpp", "codebook_quantized_routed_amd/csrc/decode.hpp",
                   "codebook_quantized_routed_amd/csrc/matvec_common.hpp",
                   "codebook_quantized_routed_amd/csrc/gemv_dev.hpp", "codebook_quantized_routed_amd/csrc/route_dev.hpp",
-                  "codebook_quantized_routed_amd/csrc/k_fused.hip")
+                  "codebook_quantized_routed_amd/csrc/k_fused.hip", "codebook_quantized_routed_amd/csrc/k_gemv.hip",
+                  "codebook_quantized_routed_amd/csrc/k_router.hip")
 TRAFFIC_FILES = {"decode_iq2": "profiles/hbm_traffic_decode_iq2_t1.txt",
                  "stack48": "profiles/hbm_traffic_stack48_decode.txt"}
 
@@ -64,11 +66,19 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def _code_only(src: str) -> str:
+    """The source without comments and blank space: what the compiler sees of it."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def kernel_digest() -> str:
+    """Digest of the code (comments and spacing excluded) of the kernel sources."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f)) as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()
 
 

@@ -25,13 +25,18 @@
 // workgroup that never runs, i.e. another kernel holding compute units meanwhile), the
 // waiting wave gives up after about a second, sets the error word and finishes; the
 // results of that call are then undefined.
+//
+// The second kernel of this file, k_stack_decode, runs the decode step of a whole chain
+// of layers (RMSNorm, this layer, residual) in one launch with the same machinery.
 #include "gemv_dev.hpp"
 #include "route_dev.hpp"
 
 namespace moe {
 
 constexpr int kFusedWaves = 12;
-constexpr int kDownWaves = kFusedWaves - 1;  // the last wave polls the grid barrier
+// waves that take a slot each in the down phase (in the stack kernel the last wave
+// routes the next layer meanwhile)
+constexpr int kDownWaves = kFusedWaves - 1;
 constexpr int kFusedMaxSlots = MOE_MAX_K + 1;
 constexpr int kFusedSlotsPerWave = (kFusedMaxSlots + kDownWaves - 1) / kDownWaves;
 constexpr int kSpinLimit = 1 << 20;  // polls of a few hundred ns: a fraction of a second
