@@ -33,34 +33,45 @@ struct GroupLds {
   int hist[kGroupWaves][MOE_MAX_IDS];
   int offs[MOE_MAX_IDS];
   int arank[MOE_MAX_IDS];
-  int wave_tot[kGroupWaves];
-  int total;
+  int4 wave_tot[kGroupWaves];
+  int4 total;
 };
 
-__device__ __forceinline__ int block_exclusive_scan(int v, GroupLds &S) {
+// Inclusive prefix sum over a wave: DPP row shifts inside the 16-lane rows, then the
+// row totals carried by row broadcasts (lanes whose source falls outside take 0).
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
+}
+
+// Exclusive prefix sums of four values over the workgroup in thread order, and their
+// totals in S.total.  Integer sums: any order gives the same result.  S.wave_tot and
+// S.total are read after the last barrier: a second call needs a barrier in between.
+__device__ __forceinline__ int4 block_exclusive_scan4(int4 v, GroupLds &S) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int inc = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int n = __shfl_up(inc, o, 64);
-    if (lane >= o) inc += n;
-  }
+  const int4 inc = make_int4(wave_inclusive_scan(v.x), wave_inclusive_scan(v.y), wave_inclusive_scan(v.z),
+                             wave_inclusive_scan(v.w));
   if (lane == 63) S.wave_tot[wave] = inc;
   __syncthreads();
   if (threadIdx.x == 0) {
-    int run = 0;
+    int4 run = make_int4(0, 0, 0, 0);
     for (int i = 0; i < kGroupWaves; i++) {
-      int c = S.wave_tot[i];
+      const int4 c = S.wave_tot[i];
       S.wave_tot[i] = run;
-      run += c;
+      run.x += c.x, run.y += c.y, run.z += c.z, run.w += c.w;
     }
     S.total = run;
   }
   __syncthreads();
-  int r = S.wave_tot[wave] + inc - v;
-  __syncthreads();
-  return r;
+  const int4 b = S.wave_tot[wave];
+  return make_int4(b.x + inc.x - v.x, b.y + inc.y - v.y, b.z + inc.z - v.z, b.w + inc.w - v.w);
 }
+
 
 // ids: global or LDS.  Must be called by all 1024 threads.
 __device__ void group_block(const int32_t *ids, int n, int n_ids, int max_narrow, int32_t *__restrict__ counts,
@@ -69,8 +80,9 @@ __device__ void group_block(const int32_t *ids, int n, int n_ids, int max_narrow
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int per = (((n + kGroupWaves - 1) / kGroupWaves) + 63) / 64 * 64;
   const int lo = wave * per, hi = min(n, lo + per);
+  const int nw = min(kGroupWaves, (n + per - 1) / per);  // the waves that hold slots
 
-  for (int i = threadIdx.x; i < kGroupWaves * MOE_MAX_IDS; i += blockDim.x) (&S.hist[0][0])[i] = 0;
+  for (int i = threadIdx.x; i < nw * MOE_MAX_IDS; i += blockDim.x) (&S.hist[0][0])[i] = 0;
   __syncthreads();
   for (int s = lo + lane; s < hi; s += 64) {
     int e = ids[s];
@@ -80,22 +92,19 @@ __device__ void group_block(const int32_t *ids, int n, int n_ids, int max_narrow
   const int e = threadIdx.x;  // n_ids <= MOE_MAX_IDS == blockDim.x
   int c = 0;
   if (e < n_ids) {
-    for (int w = 0; w < kGroupWaves; w++) {
+    for (int w = 0; w < nw; w++) {
       int h = S.hist[w][e];
       S.hist[w][e] = c;
       c += h;
     }
   }
-  const int excl = block_exclusive_scan(c, S);
-  const int n_total = S.total;
   const bool wide = c > max_narrow;
   const int tiles = wide ? (c + MOE_MFMA_TILE_TOKENS - 1) / MOE_MFMA_TILE_TOKENS : 0;
-  const int nex = block_exclusive_scan(c > 0 && !wide ? 1 : 0, S);
-  const int n_narrow = S.total;
-  block_exclusive_scan(wide ? 1 : 0, S);
-  const int n_wide = S.total;
-  const int tex = block_exclusive_scan(tiles, S);
-  const int n_tiles = S.total;
+  // slots, mat-vec experts, matrix-core experts, tiles
+  const int4 ex = block_exclusive_scan4(make_int4(c, c > 0 && !wide ? 1 : 0, wide ? 1 : 0, tiles), S);
+  const int4 tot = S.total;
+  const int excl = ex.x, nex = ex.y, tex = ex.w;
+  const int n_total = tot.x, n_narrow = tot.y, n_wide = tot.z, n_tiles = tot.w;
   if (e < n_ids) {
     counts[e] = c;
     offsets[e] = excl;
@@ -117,7 +126,7 @@ __device__ void group_block(const int32_t *ids, int n, int n_ids, int max_narrow
   }
   __syncthreads();
   if (e < n_ids)
-    for (int w = 0; w < kGroupWaves; w++) S.hist[w][e] += S.offs[e];
+    for (int w = 0; w < nw; w++) S.hist[w][e] += S.offs[e];
   __syncthreads();
 
   for (int base = lo; base < hi; base += 64) {
