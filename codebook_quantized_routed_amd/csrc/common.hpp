@@ -88,6 +88,20 @@ enum Which { kGate = 0, kUp = 1, kDown = 2 };
 // computed from it (bank choice, matrix bases) stays scalar too.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Calls f(Index<0>{}), ..., f(Index<N - 1>{}): a loop whose index is a constant in the
+// body, so arrays indexed by it are split into registers before any unrolling.
+template <int I>
+struct Index {
+  static constexpr int value = I;
+};
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (I < N) {
+    f(Index<I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
 // Load of a value the whole wave shares, through the scalar cache: the address must be
 // wave-uniform and the memory must not change while the kernel runs (it was written by
 // an earlier launch).  Scalar loads wait on their own counter, so a wave can use the

@@ -344,9 +344,12 @@ __device__ __forceinline__ void wide_run_one(const WideItem &It, X32 &X, int q, 
 // padded to kChunkPad floats.
 constexpr int kDaWaves = 4;
 constexpr int kDaSlots = (MOE_MAX_K + 1 + kDaWaves - 1) / kDaWaves;  // slots per wave, at most
+constexpr int kDaFirst = 3;  // slots per wave whose weight rows are loaded up front
 constexpr int kChunkPad = 68;
 
-__host__ __device__ inline size_t down_acc_stage_bytes(int lpr) { return (size_t)kDaWaves * kDaSlots * lpr * kChunkPad * 4; }
+__host__ __device__ inline size_t down_acc_stage_bytes(int lpr, int slots_per_wave) {
+  return (size_t)kDaWaves * slots_per_wave * lpr * kChunkPad * 4;
+}
 
 template <int QT, int LPR>
 __device__ __forceinline__ float down_slot_dot(const RowRaw &R, const float *hrow, int q, const uint8_t *lds,

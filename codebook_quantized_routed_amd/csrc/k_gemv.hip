@@ -270,33 +270,42 @@ __global__ void __launch_bounds__(256) k_down(LayerArgs L, const float *__restri
 }
 
 // ----------------------------------------------------------------------------- down + accumulate
-// One workgroup of 4 waves per (token, block of RPP output rows); wave w takes the
+// One workgroup of 4 waves per (token, block of NT x RPP output rows); wave w takes the
 // token's slots w, w + 4, ...: the down rows of each slot's expert are dotted with its
-// h, and the RPP outputs are accumulated as acc += w * y in ascending expert id ("Red
-// Metal dev8", step 5), one rounded multiply and one rounded add per slot, so the
-// result equals the separate accumulation exactly.
+// h, and the outputs are accumulated as acc += w * y in ascending expert id ("Red Metal
+// dev8", step 5), one rounded multiply and one rounded add per slot, so the result
+// equals the separate accumulation exactly.  A wave reads a slot's activation chunk (and
+// its group sums) once and dots it with NT rows per lane, so the LDS tables, the h
+// staging and the chunk are built once for NT row groups.
 //
 // Every global load is issued before the first wait: LDS tables, the slots' h rows
 // (when STAGE, copied whole into the wave's LDS area in coalesced 16-byte pieces, each
 // 64-float chunk padded to 68 floats so the lanes of different chunks hit different
 // banks), the slots' weight rows, acc and w.  The slot scalars come through the scalar
 // cache, so issuing the weight loads never waits on a vector load.
-template <int LPR, bool STAGE>
+template <int NT>
+struct SlotRows {  // one slot's weight rows of a lane, one per row group
+  RowRaw r[NT];
+};
+
+template <int LPR, bool STAGE, int NT>
 __global__ void __launch_bounds__(256) k_down_acc(LayerArgs L, const float *__restrict__ h, int kprime,
                                                   const int32_t *__restrict__ ids, const float *__restrict__ w,
                                                   const int32_t *__restrict__ slot_pos, float *__restrict__ acc) {
   extern __shared__ __align__(16) uint8_t lds[];
   constexpr int RPP = 64 / LPR, HS = LPR * kChunkPad, F4 = LPR * 16;  // F4: float4 pieces of one h row
-  __shared__ float ydot[MOE_MAX_K + 1][RPP];
+  constexpr int ROWS = NT * RPP;
+  __shared__ float ydot[MOE_MAX_K + 1][ROWS];
   __shared__ float wsorted[MOE_MAX_K + 1];
   __shared__ int order[MOE_MAX_K + 1];
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6), q = lane % LPR, sub = lane / LPR;
-  const int H = L.hidden, I = L.inter, tiles = H / RPP;
+  const int H = L.hidden, I = L.inter, tiles = H / ROWS;
   const int t = blockIdx.x / tiles, tile = blockIdx.x - t * tiles;
-  const int r = tile * RPP + sub;
+  const int r0 = tile * ROWS + sub;
   const int formats = layer_formats(L);
   const TableLayout TL = table_layout(formats);
-  float *hs = (float *)(lds + TL.bytes) + wave * kDaSlots * HS;
+  const int ns = (kprime + kDaWaves - 1) / kDaWaves;  // staged slots per wave
+  float *hs = (float *)(lds + TL.bytes) + wave * ns * HS;
   const TableRegs tr = tables_load(L.grids, formats);
   const int32_t *tok_ids = ids + (size_t)t * kprime;
   const int32_t *tok_pos = slot_pos + (size_t)t * kprime;
@@ -316,23 +325,28 @@ __global__ void __launch_bounds__(256) k_down_acc(LayerArgs L, const float *__re
       }
     }
   }
-  RowRaw R[kDaSlots];
+  // weight rows of the first kDaFirst slots (every slot when kprime <= 12); the rows of a
+  // later slot are loaded just before its dot products
+  SlotRows<NT> R[kDaFirst];
   int qt[kDaSlots];
+  auto load_slot = [&](SlotRows<NT> &Rs, int j) __attribute__((always_inline)) {
+    const int e = sload(tok_ids + j);
+    const BankArgs &B = bank_of(L, e);
+    const QMat Wd = expert_mat(B, e, kDown, H, I);
 #pragma unroll
-  for (int i = 0; i < kDaSlots; i++) {
+    for (int g = 0; g < NT; g++)
+      Rs.r[g] = B.qtype == MOE_Q_IQ2XS_LIKE ? load_row<MOE_Q_IQ2XS_LIKE>(Wd, I, r0 + g * RPP, q)
+                                            : load_row<MOE_Q_IQ1M_LIKE>(Wd, I, r0 + g * RPP, q);
+    return B.qtype;
+  };
+  static_for<kDaFirst>([&](auto ic) __attribute__((always_inline)) {
+    constexpr int i = decltype(ic)::value;
     const int j = wave + kDaWaves * i;
-    qt[i] = 0;
-    if (j < kprime) {
-      const int e = sload(tok_ids + j);
-      const BankArgs &B = bank_of(L, e);
-      const QMat Wd = expert_mat(B, e, kDown, H, I);
-      qt[i] = B.qtype;
-      R[i] = B.qtype == MOE_Q_IQ2XS_LIKE ? load_row<MOE_Q_IQ2XS_LIKE>(Wd, I, r, q)
-                                         : load_row<MOE_Q_IQ1M_LIKE>(Wd, I, r, q);
-    }
-  }
+    R[i] = SlotRows<NT>{};
+    qt[i] = j < kprime ? load_slot(R[i], j) : 0;
+  });
   float acc_in = 0.0f;
-  if (threadIdx.x < RPP) acc_in = acc[(size_t)t * H + tile * RPP + threadIdx.x];
+  if (threadIdx.x < ROWS) acc_in = acc[(size_t)t * H + tile * ROWS + threadIdx.x];
   if (threadIdx.x < kprime) {
     const int j = threadIdx.x, me = tok_ids[j];
     const float wj = w[(size_t)t * kprime + j];
@@ -359,21 +373,44 @@ __global__ void __launch_bounds__(256) k_down_acc(LayerArgs L, const float *__re
   }
   tables_store(tr, formats, TL, lds);  // ends with the workgroup barrier
 
+  // a slot's dot products: its activation chunk (and group sums) read once, NT rows
+  auto slot_dots = [&](const SlotRows<NT> &Rs, int qts, const float *hrow, int j) __attribute__((always_inline)) {
+    XChunk X;
+    if (qts == MOE_Q_IQ2XS_LIKE) {
+      load_x<MOE_Q_IQ2XS_LIKE>(hrow, X);
 #pragma unroll
-  for (int i = 0; i < kDaSlots; i++) {
+      for (int g = 0; g < NT; g++) {
+        const float v = group_sum_first<LPR>(dot_chunk<MOE_Q_IQ2XS_LIKE>(Rs.r[g], q, lds, TL, X));
+        if (q == 0) ydot[j][g * RPP + sub] = v;
+      }
+    } else {
+      load_x<MOE_Q_IQ1M_LIKE>(hrow, X);
+#pragma unroll
+      for (int g = 0; g < NT; g++) {
+        const float v = group_sum_first<LPR>(dot_chunk<MOE_Q_IQ1M_LIKE>(Rs.r[g], q, lds, TL, X));
+        if (q == 0) ydot[j][g * RPP + sub] = v;
+      }
+    }
+  };
+  static_for<kDaSlots>([&](auto ic) __attribute__((always_inline)) {
+    constexpr int i = decltype(ic)::value;
     const int j = wave + kDaWaves * i;
     if (j < kprime) {
       const float *hrow = STAGE ? hs + i * HS + q * kChunkPad : h + (size_t)p[i] * I + 64 * q;
-      const float v = qt[i] == MOE_Q_IQ2XS_LIKE ? down_slot_dot<MOE_Q_IQ2XS_LIKE, LPR>(R[i], hrow, q, lds, TL)
-                                                : down_slot_dot<MOE_Q_IQ1M_LIKE, LPR>(R[i], hrow, q, lds, TL);
-      if (q == 0) ydot[j][sub] = v;
+      if constexpr (i < kDaFirst) {
+        slot_dots(R[i], qt[i], hrow, j);
+      } else {
+        SlotRows<NT> Rl;
+        const int qtl = load_slot(Rl, j);
+        slot_dots(Rl, qtl, hrow, j);
+      }
     }
-  }
+  });
   __syncthreads();
-  if (threadIdx.x < RPP) {
+  if (threadIdx.x < ROWS) {
     float a = acc_in;
     for (int o = 0; o < kprime; o++) a = __fadd_rn(a, __fmul_rn(wsorted[o], ydot[order[o]][threadIdx.x]));
-    acc[(size_t)t * H + tile * RPP + threadIdx.x] = a;
+    acc[(size_t)t * H + tile * ROWS + threadIdx.x] = a;
   }
 }
 
@@ -445,27 +482,44 @@ hipError_t launch_down_gemv(const LayerArgs &L, const float *h, int T, int kprim
   return hipGetLastError();
 }
 
+// Row groups per down + accumulate workgroup: as many as keep at least two workgroups per
+// compute unit in flight (fewer, larger workgroups build the LDS tables and read each
+// activation chunk fewer times).
+static int down_acc_groups(int T, int tiles8, int cus) {
+  for (int nt : {4, 2}) {
+    if (tiles8 % nt == 0 && (long)T * (tiles8 / nt) >= 2L * cus) return nt;
+  }
+  return 1;
+}
+
+#define MOE_DA_LAUNCH(LPR_V, STAGE_V, NT_V, SHM)                                                                \
+  hipLaunchKernelGGL((k_down_acc<LPR_V, STAGE_V, NT_V>), dim3((unsigned)(T * (L.hidden / ((64 / LPR_V) * NT_V)))), \
+                     dim3(64 * kDaWaves), SHM, s, L, h, kprime, ids, w, slot_pos, acc)
+
 hipError_t launch_down_accumulate(const LayerArgs &L, const float *h, int T, int kprime, const int32_t *ids,
                                   const float *w, const int32_t *slot_pos, float *acc, hipStream_t s) {
   const int lpr = lanes_per_row(L.inter), rpp = 64 / lpr;
   const size_t tables = table_layout(layer_formats(L)).bytes;
-  const dim3 grid((unsigned)(T * (L.hidden / rpp))), block(64 * kDaWaves);
+  int dev = 0, cus = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (err != hipSuccess) return err;
+  const int nt = down_acc_groups(T, L.hidden / rpp, cus);
   // h is staged in LDS for inter <= 512 (at most 43.5 KB per workgroup)
-  switch (lpr) {
-    case 4:
-      hipLaunchKernelGGL((k_down_acc<4, true>), grid, block, tables + down_acc_stage_bytes(4), s, L, h, kprime, ids, w,
-                         slot_pos, acc);
-      break;
-    case 8:
-      hipLaunchKernelGGL((k_down_acc<8, true>), grid, block, tables + down_acc_stage_bytes(8), s, L, h, kprime, ids, w,
-                         slot_pos, acc);
-      break;
-    case 16:
-      hipLaunchKernelGGL((k_down_acc<16, false>), grid, block, tables, s, L, h, kprime, ids, w, slot_pos, acc);
-      break;
-    default:
-      hipLaunchKernelGGL((k_down_acc<32, false>), grid, block, tables, s, L, h, kprime, ids, w, slot_pos, acc);
-      break;
+  const int ns = (kprime + kDaWaves - 1) / kDaWaves;
+  switch (lpr * 8 + nt) {
+    case 4 * 8 + 4: MOE_DA_LAUNCH(4, true, 4, tables + down_acc_stage_bytes(4, ns)); break;
+    case 4 * 8 + 2: MOE_DA_LAUNCH(4, true, 2, tables + down_acc_stage_bytes(4, ns)); break;
+    case 4 * 8 + 1: MOE_DA_LAUNCH(4, true, 1, tables + down_acc_stage_bytes(4, ns)); break;
+    case 8 * 8 + 4: MOE_DA_LAUNCH(8, true, 4, tables + down_acc_stage_bytes(8, ns)); break;
+    case 8 * 8 + 2: MOE_DA_LAUNCH(8, true, 2, tables + down_acc_stage_bytes(8, ns)); break;
+    case 8 * 8 + 1: MOE_DA_LAUNCH(8, true, 1, tables + down_acc_stage_bytes(8, ns)); break;
+    case 16 * 8 + 4: MOE_DA_LAUNCH(16, false, 4, tables); break;
+    case 16 * 8 + 2: MOE_DA_LAUNCH(16, false, 2, tables); break;
+    case 16 * 8 + 1: MOE_DA_LAUNCH(16, false, 1, tables); break;
+    case 32 * 8 + 4: MOE_DA_LAUNCH(32, false, 4, tables); break;
+    case 32 * 8 + 2: MOE_DA_LAUNCH(32, false, 2, tables); break;
+    default: MOE_DA_LAUNCH(32, false, 1, tables); break;
   }
   return hipGetLastError();
 }

@@ -179,6 +179,10 @@ LAYER_CASES = {
     "decode_iq1s_top10_shared": ([(IQ1S, 512)], 2048, 512, 512, 1, 1, 10, 0.0),
     "iq1s_mixed_t6": ([(IQ1S, 32), (IQ2, 32)], 2048, 512, 64, 1, 6, 4, 0.0),
     "dense_iq1s_t40_shared": ([(IQ1S, 8)], 2048, 512, 8, 1, 40, 3, 0.0),
+    # the widest routing (16 experts + the shared one): a wave of the fused down +
+    # accumulate holds more slots than it loads up front
+    "top16_shared_t8": ([(IQ2, 32), (IQ1, 32)], 2048, 512, 64, 1, 8, 16, 0.0),
+    "top13_t5": ([(IQ1, 24), (IQ2, 24)], 2048, 512, 48, 0, 5, 13, 0.0),
 }
 
 
