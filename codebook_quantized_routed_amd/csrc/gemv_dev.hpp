@@ -272,7 +272,7 @@ struct XSource {
   int tok_stride, lane_stride;
 };
 
-template <int QT, bool COHERENT = false>
+template <int QT, bool COHERENT = false, bool XGS = false>
 __device__ __forceinline__ void wide_run(const LayerArgs &L, WideItem &It, X32 &X, int &cur_tok, bool &gs_ok, int q,
                                          int kprime, const XSource &xsrc, const int32_t *sorted_slot,
                                          const uint8_t *lds, const TableLayout &TL, void *h, uint32_t tag = 0) {
@@ -280,32 +280,44 @@ __device__ __forceinline__ void wide_run(const LayerArgs &L, WideItem &It, X32 &
   for (int p = It.W.p0; p < It.W.p1; p++) {
     const int tok = (p == It.W.p0 ? It.W.slot0 : sload(sorted_slot + p)) / kprime;
     if (tok != cur_tok) {
-      load_x32(xsrc.x + (size_t)tok * xsrc.tok_stride + q * xsrc.lane_stride, X);
+      const float *xl = xsrc.x + (size_t)tok * xsrc.tok_stride + q * xsrc.lane_stride;
+      load_x32(xl, X);
+      if constexpr (XGS && QT == MOE_Q_IQ1M_LIKE) {  // the group sums follow the slice
+        const float4 g = *(const float4 *)(xl + 32);
+        X.gs8[0] = g.x, X.gs8[1] = g.y, X.gs8[2] = g.z, X.gs8[3] = g.w;
+      }
       cur_tok = tok;
-      gs_ok = false;
+      gs_ok = XGS;
     }
-    if constexpr (QT == MOE_Q_IQ1M_LIKE) {  // group sums of the current activations, once
+    if constexpr (QT == MOE_Q_IQ1M_LIKE && !XGS) {  // group sums of the current activations, once
       if (!gs_ok) group_sums32(X);
       gs_ok = true;
     }
+    float vg[kWideRows], vu[kWideRows];
 #pragma unroll
     for (int i = 0; i < kWideRows; i++) {
       Row32 g = It.g[i], u = It.u[i];
       opaque(g);
       opaque(u);
-      float vg = dot32<QT>(g, q, lds, TL, X);
-      float vu = dot32<QT>(u, q, lds, TL, X);
-      vg = group_sum_first<64>(vg);
-      vu = group_sum_first<64>(vu);
-      if (q == 0) {
-        const size_t at = (size_t)p * I + It.r0 + i;
-        const float v = silu(vg) * vu;
-        if constexpr (COHERENT)
-          __hip_atomic_store((uint64_t *)h + at, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-        else
-          ((float *)h)[at] = v;
+      // wave-uniform sums, held in scalar registers until the rows are finished
+      vg[i] = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(group_sum_first<64>(dot32<QT>(g, q, lds, TL, X)))));
+      vu[i] = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(group_sum_first<64>(dot32<QT>(u, q, lds, TL, X)))));
+    }
+    // lane i < kWideRows finishes row r0 + i: one SiLU for all the item's rows
+    if (q < kWideRows) {
+      float g = vg[0], u = vu[0];
+#pragma unroll
+      for (int i = 1; i < kWideRows; i++) {
+        g = q == i ? vg[i] : g;
+        u = q == i ? vu[i] : u;
       }
+      const size_t at = (size_t)p * I + It.r0 + q;
+      const float v = silu(g) * u;
+      if constexpr (COHERENT)
+        __hip_atomic_store((uint64_t *)h + at, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      else
+        ((float *)h)[at] = v;
     }
   }
 }

@@ -135,7 +135,7 @@ constexpr int kWideWaves = 12;
 static_assert(64 * kWideWaves >= 2048 / 4 && 2 * 64 * kWideWaves >= MOE_MAX_IDS,
               "staging: one float4 of each token per thread; two work records per thread");
 constexpr int kXStageTokens = 8;
-constexpr int kXLaneRow = 36;                 // floats per lane slice in the staging
+constexpr int kXLaneRow = 36;                 // floats per lane slice in the staging (32 + 4 group sums)
 constexpr int kXTokRow = 64 * kXLaneRow;      // floats per staged token
 
 // LDS after the grid tables: the staged activations (room for kXStageTokens tokens,
@@ -186,6 +186,18 @@ __global__ void __launch_bounds__(64 * kWideWaves) k_gateup_wide(LayerArgs L, co
   }
   if (threadIdx.x == 0) fill_banks(L, banks);
   tables_store(tr, QT, TL, lds);  // also publishes the records, the activations and the bank table
+  if constexpr (STAGED && QT == MOE_Q_IQ1M_LIKE) {
+    // the 8-column group sums (times 1/8) of every staged lane slice, in the slice's
+    // padding: thread i < 512 takes slice i % 64 of token i / 64, summing in column order
+    if (threadIdx.x < kXStageTokens * 64) {
+      float *sl = xs + (threadIdx.x >> 6) * kXTokRow + (threadIdx.x & 63) * kXLaneRow;
+      X32 Xs;
+      load_x32(sl, Xs);
+      group_sums32(Xs);
+      *(float4 *)(sl + 32) = make_float4(Xs.gs8[0], Xs.gs8[1], Xs.gs8[2], Xs.gs8[3]);
+    }
+    __syncthreads();
+  }
   // three items in flight per wave: A is computed while B and C load.  Items of the
   // other format are skipped (a layer with both formats runs this kernel once per format).
   // (items are passed by value: a by-reference hand-off put them in scratch memory, whose
@@ -208,7 +220,7 @@ __global__ void __launch_bounds__(64 * kWideWaves) k_gateup_wide(LayerArgs L, co
   bool gs_ok = false;
   auto run = [&](WideItem &D) {
     if (D.qt == QT && D.W.p1 - D.W.p0 <= max_tokens)
-      wide_run<QT>(L, D, X, cur_tok, gs_ok, q, kprime, xsrc, sorted_slot, lds, TL, h);
+      wide_run<QT, false, STAGED>(L, D, X, cur_tok, gs_ok, q, kprime, xsrc, sorted_slot, lds, TL, h);
   };
   // unrolled by three so that each buffer keeps its registers (no copies between them)
   int it = blockIdx.x * kWideWaves + wave;
