@@ -107,7 +107,11 @@ __device__ __forceinline__ TopkVals<VPL> topk_load(const float *__restrict__ l, 
   return t;
 }
 
-template <int VPL>
+// TAU_BITS: bits of tau per search step (1, 2 or 4).  Fewer steps shorten the chain of
+// ballot -> scalar count -> select, more ballots per step cost issue slots: one bit is
+// the faster where the wave has its SIMD mostly to itself, two where it shares it with
+// busy waves (the next layer's routing inside the stack kernel).
+template <int VPL, int TAU_BITS = 1>
 __device__ __forceinline__ void topk_select(const TopkVals<VPL> &tv, int E, int k, int add_shared,
                                             int32_t *__restrict__ ids, float *__restrict__ w, int32_t *ids_copy,
                                             float *w_copy, TopkLds &S) {
@@ -120,11 +124,17 @@ __device__ __forceinline__ void topk_select(const TopkVals<VPL> &tv, int E, int 
     lmax = max(lmax, key[i]);
   }
   // tau: the largest t with at least k lane maxima >= t (the set of such t is closed
-  // downwards, so it is found bit by bit from the top).  At least k lanes hold a key.
+  // downwards, so it is found from the top, TAU_BITS bits per step: the count of the
+  // 2^TAU_BITS - 1 nonzero digits that keep at least k maxima is the largest such digit,
+  // and their ballots are independent of each other).  At least k lanes hold a key.
+  static_assert(TAU_BITS == 1 || TAU_BITS == 2 || TAU_BITS == 4, "tau digits must tile 32 bits");
   uint32_t tau = 0u;
-  for (int b = 31; b >= 0; b--) {
-    const uint32_t c = tau | (1u << b);
-    if (__popcll(__ballot(lmax >= c)) >= k) tau = c;
+#pragma unroll
+  for (int sh = 32 - TAU_BITS; sh >= 0; sh -= TAU_BITS) {
+    uint32_t digit = 0u;
+#pragma unroll
+    for (uint32_t j = 1; j < (1u << TAU_BITS); j++) digit += __popcll(__ballot(lmax >= (tau | (j << sh)))) >= k ? 1u : 0u;
+    tau |= digit << sh;
   }
   // candidates: keys >= tau (invalid keys are 0 < tau), packed in (i, lane) order
   int pos[VPL], total = 0;
