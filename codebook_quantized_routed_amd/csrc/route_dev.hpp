@@ -44,15 +44,16 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
 // largest key (those k maxima are k keys >= tau), so every selected key is >= tau.
 // tau comes from a bitwise search over ballots; the few keys >= tau (about k to 2k for
 // N(0,1) logits) are packed into LDS, one per lane, and each is ranked against the
-// others by (key descending, id ascending) through lane reads; rank < k is selected.
+// others by (key descending, id ascending) from broadcast LDS reads; rank < k is selected.
 // If more than 64 keys reach tau (heavy ties), the selection falls back to k rounds of
 // a wave-wide arg-max.  Both give the same result.
 // Outputs: ids / w (global, skipped when ids is null) and the optional copies.
 constexpr int kCand = 64;
 
 struct TopkLds {
-  uint32_t cand_key[kCand];
-  int cand_id[kCand];
+  // candidate j: (key << 32) | ~id, so one unsigned compare orders by (key descending,
+  // id ascending)
+  alignas(16) uint64_t cand[kCand];
   uint32_t sel_key[MOE_MAX_K];
   int sel_id[MOE_MAX_K];
 };
@@ -147,22 +148,20 @@ __device__ __forceinline__ void topk_select(const TopkVals<VPL> &tv, int E, int 
   if (total <= kCand) {
 #pragma unroll
     for (int i = 0; i < VPL; i++)
-      if (key[i] >= tau) {
-        S.cand_key[pos[i]] = key[i];
-        S.cand_id[pos[i]] = i * 64 + lane;
-      }
+      if (key[i] >= tau) S.cand[pos[i]] = ((uint64_t)key[i] << 32) | (uint32_t)~(uint32_t)(i * 64 + lane);
     __builtin_amdgcn_wave_barrier();
-    const uint32_t ck = lane < total ? S.cand_key[lane] : 0u;
-    const int cid = lane < total ? S.cand_id[lane] : 0x7FFFFFFF;
+    // each lane ranks its candidate against all of them, two per 16-byte read (every
+    // lane reads the same address: one broadcast read)
+    const uint64_t mine = lane < total ? S.cand[lane] : 0u;
     int rank = 0;
-    for (int j = 0; j < total; j++) {
-      const uint32_t ok = (uint32_t)__builtin_amdgcn_readlane((int)ck, j);
-      const int oid = __builtin_amdgcn_readlane(cid, j);
-      rank += (ok > ck || (ok == ck && oid < cid)) ? 1 : 0;
+    for (int j = 0; j < total; j += 2) {
+      const uint4 pr = *(const uint4 *)&S.cand[j];
+      rank += (((uint64_t)pr.y << 32) | pr.x) > mine ? 1 : 0;
+      rank += (j + 1 < total && (((uint64_t)pr.w << 32) | pr.z) > mine) ? 1 : 0;
     }
     if (lane < total && rank < k) {
-      S.sel_key[rank] = ck;
-      S.sel_id[rank] = cid;
+      S.sel_key[rank] = (uint32_t)(mine >> 32);
+      S.sel_id[rank] = (int)~(uint32_t)mine;
     }
   } else {
     topk_select_rounds<VPL>(key, k, S);
