@@ -38,6 +38,20 @@ constexpr int kFusedWaves = 12;
 // routes the next layer meanwhile)
 constexpr int kDownWaves = kFusedWaves - 1;
 constexpr int kFusedMaxSlots = MOE_MAX_K + 1;
+
+// Position of the lane's slot among the token's slots in (expert id, slot) order, from
+// the expert ids held one per lane (lanes past the last slot hold 0x7FFFFFFF, which no
+// slot counts).  Unrolled over the largest slot count, so the lane reads issue back to
+// back instead of one per loop trip.
+__device__ __forceinline__ int slot_rank(int my, int lane) {
+  int rank = 0;
+#pragma unroll
+  for (int j = 0; j < kFusedMaxSlots; j++) {
+    const int o = __builtin_amdgcn_readlane(my, j);
+    rank += (o < my || (o == my && j < lane)) ? 1 : 0;
+  }
+  return rank;
+}
 constexpr int kFusedSlotsPerWave = (kFusedMaxSlots + kDownWaves - 1) / kDownWaves;
 constexpr int kSpinLimit = 1 << 20;  // polls of a few hundred ns: a fraction of a second
 
@@ -175,11 +189,7 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
     }
     __builtin_amdgcn_wave_barrier();
     const int my = lane < kprime ? S.ids[lane] : 0x7FFFFFFF;
-    int rank = 0;
-    for (int j = 0; j < kprime; j++) {
-      const int o = __builtin_amdgcn_readlane(my, j);
-      rank += (o < my || (o == my && j < lane)) ? 1 : 0;
-    }
+    const int rank = slot_rank(my, lane);
     if (lane < kprime) {
       S.pos_of[lane] = rank;
       S.slot_at[rank] = lane;
@@ -361,11 +371,7 @@ __device__ inline void route_wave(const float *logits, const LayerArgs &L, int E
   topk_select<8, 2>(tv, E, k, add_shared, ids_out, w_out, R.ids, R.w, T);
   __builtin_amdgcn_wave_barrier();
   const int my = lane < kprime ? R.ids[lane] : 0x7FFFFFFF;
-  int rank = 0;
-  for (int j = 0; j < kprime; j++) {
-    const int o = __builtin_amdgcn_readlane(my, j);
-    rank += (o < my || (o == my && j < lane)) ? 1 : 0;
-  }
+  const int rank = slot_rank(my, lane);
   if (lane < kprime) {
     R.pos_of[lane] = rank;
     R.slot_at[rank] = lane;

@@ -175,8 +175,11 @@ __device__ __forceinline__ void topk_select(const TopkVals<VPL> &tv, int E, int 
     top = from_orderable(S.sel_key[0]);
     ex = expf(__fsub_rn(from_orderable(S.sel_key[lane]), top));
   }
+  // the sum in selection order; lanes k.. hold +0, which leaves the (positive) sum as it
+  // is, so the loop runs over the largest k, unrolled, with its lane reads back to back
   float sum = 0.0f;
-  for (int j = 0; j < k; j++) sum = __fadd_rn(sum, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j)));
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_K; j++) sum = __fadd_rn(sum, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j)));
   if (lane < k) {
     const float wl = __fdiv_rn(ex, sum);
     if (ids) {
