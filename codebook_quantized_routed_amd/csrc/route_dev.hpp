@@ -111,8 +111,10 @@ __device__ __forceinline__ TopkVals<VPL> topk_load(const float *__restrict__ l, 
 // TAU_BITS: bits of tau per search step (1, 2 or 4).  Fewer steps shorten the chain of
 // ballot -> scalar count -> select, more ballots per step cost issue slots: one bit is
 // the faster where the wave has its SIMD mostly to itself, two where it shares it with
-// busy waves (the next layer's routing inside the stack kernel).
-template <int VPL, int TAU_BITS = 1>
+// busy waves (the next layer's routing inside the stack kernel).  TAU_LOW: tau's bits
+// below this one are not searched (stay zero).  Measured: 16 is the faster in the
+// routing kernels, 0 in the fused decode kernels; the selection is the same.
+template <int VPL, int TAU_BITS = 1, int TAU_LOW = 0>
 __device__ __forceinline__ void topk_select(const TopkVals<VPL> &tv, int E, int k, int add_shared,
                                             int32_t *__restrict__ ids, float *__restrict__ w, int32_t *ids_copy,
                                             float *w_copy, TopkLds &S) {
@@ -124,14 +126,19 @@ __device__ __forceinline__ void topk_select(const TopkVals<VPL> &tv, int E, int 
     key[i] = i * 64 + lane < E ? orderable(tv.v[i]) : 0u;
     lmax = max(lmax, key[i]);
   }
-  // tau: the largest t with at least k lane maxima >= t (the set of such t is closed
-  // downwards, so it is found from the top, TAU_BITS bits per step: the count of the
-  // 2^TAU_BITS - 1 nonzero digits that keep at least k maxima is the largest such digit,
-  // and their ballots are independent of each other).  At least k lanes hold a key.
-  static_assert(TAU_BITS == 1 || TAU_BITS == 2 || TAU_BITS == 4, "tau digits must tile 32 bits");
+  // tau: the largest t whose low TAU_LOW bits are zero with at least k lane maxima
+  // >= t (the set of such t is closed downwards, so it is found from the top, TAU_BITS
+  // bits per step: the count of the 2^TAU_BITS - 1 nonzero digits that keep at least k
+  // maxima is the largest such digit, and their ballots are independent of each other).
+  // It is at most the k-th largest lane maximum, so still a lower bound on the k-th
+  // largest key; the low bits would only trim the candidates (stopping at bit 16, after
+  // the sign, the exponent and 7 mantissa bits, leaves about one more for normal
+  // logits).  At least k lanes hold a key.
+  static_assert(TAU_BITS == 1 || TAU_BITS == 2 || TAU_BITS == 4, "tau digits must tile the searched bits");
+  static_assert((32 - TAU_LOW) % TAU_BITS == 0, "tau digits must tile the searched bits");
   uint32_t tau = 0u;
 #pragma unroll
-  for (int sh = 32 - TAU_BITS; sh >= 0; sh -= TAU_BITS) {
+  for (int sh = 32 - TAU_BITS; sh >= TAU_LOW; sh -= TAU_BITS) {
     uint32_t digit = 0u;
 #pragma unroll
     for (uint32_t j = 1; j < (1u << TAU_BITS); j++) digit += __popcll(__ballot(lmax >= (tau | (j << sh)))) >= k ? 1u : 0u;
@@ -203,7 +210,7 @@ template <int VPL>
 __device__ __forceinline__ void topk_wave(const float *__restrict__ l, int E, int k, int add_shared,
                                           int32_t *__restrict__ ids, float *__restrict__ w, int32_t *ids_copy,
                                           float *w_copy, TopkLds &S) {
-  topk_select<VPL>(topk_load<VPL>(l, E), E, k, add_shared, ids, w, ids_copy, w_copy, S);
+  topk_select<VPL, 1, 16>(topk_load<VPL>(l, E), E, k, add_shared, ids, w, ids_copy, w_copy, S);
 }
 
 // Grouping of at most 64 slots (decode): the same outputs as group_block, computed
