@@ -338,15 +338,18 @@ __device__ __forceinline__ void wide_run_one(const WideItem &It, X32 &X, int q, 
   }
 #pragma unroll
   for (int i = 0; i < kWideRows; i++) {
-    vg[i] = group_sum_first<64>(vg[i]);
-    vu[i] = group_sum_first<64>(vu[i]);
+    vg[i] = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(group_sum_first<64>(vg[i]))));
+    vu[i] = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(group_sum_first<64>(vu[i]))));
   }
-  if (q == 0) {
+  if (q < kWideRows) {  // lane i finishes row r0 + i: one SiLU for all the item's rows
+    float g = vg[0], u = vu[0];
 #pragma unroll
-    for (int i = 0; i < kWideRows; i++)
-      __hip_atomic_store(h + (size_t)It.W.p0 * I + It.r0 + i,
-                         ((uint64_t)tag << 32) | __float_as_uint(silu(vg[i]) * vu[i]), __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = 1; i < kWideRows; i++) {
+      g = q == i ? vg[i] : g;
+      u = q == i ? vu[i] : u;
+    }
+    __hip_atomic_store(h + (size_t)It.W.p0 * I + It.r0 + q, ((uint64_t)tag << 32) | __float_as_uint(silu(g) * u),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

@@ -72,7 +72,8 @@ static_assert(sizeof(FusedSync) == 4352, "h follows the synchronisation words");
 static_assert(offsetof(FusedSync, error) == 128 && offsetof(FusedSync, group) == 256, "documented offsets");
 
 // Activations staged in LDS: lane l of a wave takes columns 32 l .. 32 l + 31 (hidden
-// 2048), stored at l * kXsRow floats (the padding spreads the lanes over the banks).
+// 2048), stored at l * kXsRow floats (the padding spreads the lanes over the banks; in
+// k_layer_decode it holds the lane's four 8-column group sums).
 constexpr int kXsRow = 36;
 
 // The expert at one sorted position: its id, slot and bank.
@@ -197,7 +198,16 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
     }
   } else {
     tables_store(tr, formats, TL, lds, threadIdx.x - 64, blockDim.x - 64, false);
-    if (xt >= 0 && xt < 512) *(float4 *)&S.xs[(xt >> 3) * kXsRow + (xt & 7) * 4] = xv;
+    if (xt >= 0 && xt < 512) {
+      *(float4 *)&S.xs[(xt >> 3) * kXsRow + (xt & 7) * 4] = xv;
+      // the 8-column group sums (times 1/8) in column order, into the slice padding:
+      // the even thread of a pair sums the group's first four values, the odd one
+      // (its lane neighbour) adds the last four
+      float ps = __fadd_rn(__fadd_rn(__fadd_rn(__fadd_rn(0.0f, xv.x), xv.y), xv.z), xv.w);
+      const float lo = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ps), 0x111, 0xf, 0xf, false));
+      ps = __fadd_rn(__fadd_rn(__fadd_rn(__fadd_rn(lo, xv.x), xv.y), xv.z), xv.w);
+      if (xt & 1) S.xs[(xt >> 3) * kXsRow + 32 + ((xt & 7) >> 1)] = ps * 0.125f;
+    }
     if (threadIdx.x == 64) {
       S.tag = tag;
       fill_banks(L, S.banks);
@@ -228,6 +238,11 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
   for (int i = 0; i < 8; i++) {
     const float4 f = *(const float4 *)&S.xs[lane * kXsRow + 4 * i];
     X.v[4 * i] = f.x, X.v[4 * i + 1] = f.y, X.v[4 * i + 2] = f.z, X.v[4 * i + 3] = f.w;
+  }
+  {  // the group sums staged with the activations
+    const float4 g = *(const float4 *)&S.xs[lane * kXsRow + 32];
+    X.gs8[0] = g.x, X.gs8[1] = g.y, X.gs8[2] = g.z, X.gs8[3] = g.w;
+    gs_ok = true;
   }
   if (item0 < n_items) issue(item0);
   for (int item = item0; item < n_items; item += nw) {
