@@ -159,7 +159,6 @@ __device__ __forceinline__ Row32 load_row32(const QMat &m, int cols, int r, int 
 
 struct X32 {
   float v[32];
-  float gs8[4];
 };
 
 template <int QT>
@@ -182,19 +181,19 @@ __device__ __forceinline__ float dot32(const Row32 &R, int q, const uint8_t *lds
     }
     return (a + b) * iq2_factor(R.v.z, R.v.w, q & 7);
   } else {
-    const uint4 *rows = (const uint4 *)(lds + TL.iq1h);
-    float a[2] = {0.0f, 0.0f}, b[2] = {0.0f, 0.0f}, ds[2] = {0.0f, 0.0f};
+    // the delta rows: index bits 0-10 pick the grid row, bit 11 (the nibble's delta
+    // sign) the half with -1/8 added instead of +1/8
+    const uint4 *rows = (const uint4 *)(lds + TL.iq1d);
+    float a[2] = {0.0f, 0.0f}, b[2] = {0.0f, 0.0f};
 #pragma unroll
     for (int g = 0; g < 4; g++) {
       const uint32_t ql8 = (R.v.x >> (8 * g)) & 0xFFu;
       const uint32_t nib = (R.v.y >> (4 * g)) & 15u;
-      const uint4 v = rows[ql8 | ((nib & 7u) << 8)];
-      ds[g >> 1] += (nib & 8u) ? -X.gs8[g] : X.gs8[g];
-      dot8(v, X.v + 8 * g, a[g >> 1], b[g >> 1]);
+      dot8(rows[ql8 | (nib << 8)], X.v + 8 * g, a[g >> 1], b[g >> 1]);
     }
     const uint64_t sd = ((uint64_t)R.v.w << 32) | R.v.z;
     const int sb = 2 * (q & 7);
-    return fmaf((a[1] + b[1]) + ds[1], iq1_factor(sd, sb + 1), ((a[0] + b[0]) + ds[0]) * iq1_factor(sd, sb));
+    return fmaf(a[1] + b[1], iq1_factor(sd, sb + 1), (a[0] + b[0]) * iq1_factor(sd, sb));
   }
 }
 
@@ -207,16 +206,6 @@ __device__ __forceinline__ void load_x32(const float *p, X32 &X) {
     X.v[4 * i + 1] = f.y;
     X.v[4 * i + 2] = f.z;
     X.v[4 * i + 3] = f.w;
-  }
-}
-
-__device__ __forceinline__ void group_sums32(X32 &X) {
-#pragma unroll
-  for (int g = 0; g < 4; g++) {
-    float s = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; j++) s += X.v[8 * g + j];
-    X.gs8[g] = s * 0.125f;
   }
 }
 
@@ -272,26 +261,16 @@ struct XSource {
   int tok_stride, lane_stride;
 };
 
-template <int QT, bool COHERENT = false, bool XGS = false>
-__device__ __forceinline__ void wide_run(const LayerArgs &L, WideItem &It, X32 &X, int &cur_tok, bool &gs_ok, int q,
-                                         int kprime, const XSource &xsrc, const int32_t *sorted_slot,
+template <int QT, bool COHERENT = false>
+__device__ __forceinline__ void wide_run(const LayerArgs &L, WideItem &It, X32 &X, int &cur_tok, int q, int kprime,
+                                         const XSource &xsrc, const int32_t *sorted_slot,
                                          const uint8_t *lds, const TableLayout &TL, void *h, uint32_t tag = 0) {
   const int I = L.inter;
   for (int p = It.W.p0; p < It.W.p1; p++) {
     const int tok = (p == It.W.p0 ? It.W.slot0 : sload(sorted_slot + p)) / kprime;
     if (tok != cur_tok) {
-      const float *xl = xsrc.x + (size_t)tok * xsrc.tok_stride + q * xsrc.lane_stride;
-      load_x32(xl, X);
-      if constexpr (XGS && QT == MOE_Q_IQ1M_LIKE) {  // the group sums follow the slice
-        const float4 g = *(const float4 *)(xl + 32);
-        X.gs8[0] = g.x, X.gs8[1] = g.y, X.gs8[2] = g.z, X.gs8[3] = g.w;
-      }
+      load_x32(xsrc.x + (size_t)tok * xsrc.tok_stride + q * xsrc.lane_stride, X);
       cur_tok = tok;
-      gs_ok = XGS;
-    }
-    if constexpr (QT == MOE_Q_IQ1M_LIKE && !XGS) {  // group sums of the current activations, once
-      if (!gs_ok) group_sums32(X);
-      gs_ok = true;
     }
     float vg[kWideRows], vu[kWideRows];
 #pragma unroll
@@ -329,7 +308,6 @@ __device__ __forceinline__ void wide_run(const LayerArgs &L, WideItem &It, X32 &
 template <int QT>
 __device__ __forceinline__ void wide_run_one(const WideItem &It, X32 &X, int q, int I, const uint8_t *lds,
                                              const TableLayout &TL, uint64_t *h, uint32_t tag) {
-  if constexpr (QT == MOE_Q_IQ1M_LIKE) group_sums32(X);
   float vg[kWideRows], vu[kWideRows];
 #pragma unroll
   for (int i = 0; i < kWideRows; i++) {

@@ -72,8 +72,7 @@ static_assert(sizeof(FusedSync) == 4352, "h follows the synchronisation words");
 static_assert(offsetof(FusedSync, error) == 128 && offsetof(FusedSync, group) == 256, "documented offsets");
 
 // Activations staged in LDS: lane l of a wave takes columns 32 l .. 32 l + 31 (hidden
-// 2048), stored at l * kXsRow floats (the padding spreads the lanes over the banks; in
-// k_layer_decode it holds the lane's four 8-column group sums).
+// 2048), stored at l * kXsRow floats (the padding spreads the lanes over the banks).
 constexpr int kXsRow = 36;
 
 // The expert at one sorted position: its id, slot and bank.
@@ -136,7 +135,16 @@ __device__ inline void stage_h_row(const uint64_t *src, uint32_t tag, float *hs,
   for (int i = 0; i < LPR; i++) hs[i * kChunkPad + lane] = __uint_as_float((uint32_t)v[i]);
 }
 
-template <int LPR>
+// True when a matrix of format qt is IQ2_XS-like, decided at compile time when the
+// kernel instance serves one format only.
+template <int FMT>
+__device__ __forceinline__ bool fmt_iq2(int qt) {
+  return FMT == MOE_Q_IQ2XS_LIKE || (FMT != MOE_Q_IQ1M_LIKE && qt == MOE_Q_IQ2XS_LIKE);
+}
+
+// FMT: the layer's formats (MOE_Q_* bits), a template parameter so that a layer of one
+// format runs an instance without the other format's code.
+template <int LPR, int FMT>
 __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, const float *__restrict__ logits,
                                                                     const float *__restrict__ x, int E, int k,
                                                                     int add_shared, int32_t *__restrict__ ids,
@@ -153,8 +161,8 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
   const int kprime = k + add_shared, n_ids = E + add_shared;
   const int H = L.hidden, I = L.inter;
   uint64_t *h = (uint64_t *)(sync + 1);
-  const int formats = layer_formats(L);
-  const TableLayout TL = table_layout(formats);
+  constexpr int formats = FMT;
+  const TableLayout TL = table_layout(formats, kTabIq1 | kTabIq1Delta);
   float *hs = (float *)(lds + TL.bytes) + wave * HS;
   // wave 0's logits are the first loads of the kernel; the table rows are loaded by
   // waves 1.. while wave 0 routes (vector loads complete in order)
@@ -198,16 +206,7 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
     }
   } else {
     tables_store(tr, formats, TL, lds, threadIdx.x - 64, blockDim.x - 64, false);
-    if (xt >= 0 && xt < 512) {
-      *(float4 *)&S.xs[(xt >> 3) * kXsRow + (xt & 7) * 4] = xv;
-      // the 8-column group sums (times 1/8) in column order, into the slice padding:
-      // the even thread of a pair sums the group's first four values, the odd one
-      // (its lane neighbour) adds the last four
-      float ps = __fadd_rn(__fadd_rn(__fadd_rn(__fadd_rn(0.0f, xv.x), xv.y), xv.z), xv.w);
-      const float lo = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ps), 0x111, 0xf, 0xf, false));
-      ps = __fadd_rn(__fadd_rn(__fadd_rn(__fadd_rn(lo, xv.x), xv.y), xv.z), xv.w);
-      if (xt & 1) S.xs[(xt >> 3) * kXsRow + 32 + ((xt & 7) >> 1)] = ps * 0.125f;
-    }
+    if (xt >= 0 && xt < 512) *(float4 *)&S.xs[(xt >> 3) * kXsRow + (xt & 7) * 4] = xv;
     if (threadIdx.x == 64) {
       S.tag = tag;
       fill_banks(L, S.banks);
@@ -225,13 +224,15 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
   const int item0 = blockIdx.x * kFusedWaves + wave;
   WideItem It;
   int cur_tok = 0;
-  bool gs_ok = false;
   auto issue = [&](int item) {
     const int p = item / ipe;
     const int e = uniform(S.pos[p].e), slot = uniform(S.pos[p].slot);
     const BankLds &B = S.banks[uniform(S.pos[p].bank)];
     It.W = WorkRec{e, p, p + 1, slot};
-    wide_issue_mats(It, bank_mat(B, e, kGate), bank_mat(B, e, kUp), uniform(B.qt), H, item - p * ipe, q);
+    if constexpr (FMT == MOE_Q_IQ2XS_LIKE || FMT == MOE_Q_IQ1M_LIKE)
+      wide_issue_fmt<FMT>(It, bank_mat(B, e, kGate), bank_mat(B, e, kUp), H, item - p * ipe, q);
+    else
+      wide_issue_mats(It, bank_mat(B, e, kGate), bank_mat(B, e, kUp), uniform(B.qt), H, item - p * ipe, q);
   };
   X32 X;
 #pragma unroll
@@ -239,18 +240,13 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
     const float4 f = *(const float4 *)&S.xs[lane * kXsRow + 4 * i];
     X.v[4 * i] = f.x, X.v[4 * i + 1] = f.y, X.v[4 * i + 2] = f.z, X.v[4 * i + 3] = f.w;
   }
-  {  // the group sums staged with the activations
-    const float4 g = *(const float4 *)&S.xs[lane * kXsRow + 32];
-    X.gs8[0] = g.x, X.gs8[1] = g.y, X.gs8[2] = g.z, X.gs8[3] = g.w;
-    gs_ok = true;
-  }
   if (item0 < n_items) issue(item0);
   for (int item = item0; item < n_items; item += nw) {
     if (item != item0) issue(item);
-    if (It.qt == MOE_Q_IQ2XS_LIKE)
-      wide_run<MOE_Q_IQ2XS_LIKE, true>(L, It, X, cur_tok, gs_ok, q, kprime, XSource{x, H, 32}, sorted_slot, lds, TL, h, tag);
+    if (fmt_iq2<FMT>(It.qt))
+      wide_run<MOE_Q_IQ2XS_LIKE, true>(L, It, X, cur_tok, q, kprime, XSource{x, H, 32}, sorted_slot, lds, TL, h, tag);
     else
-      wide_run<MOE_Q_IQ1M_LIKE, true>(L, It, X, cur_tok, gs_ok, q, kprime, XSource{x, H, 32}, sorted_slot, lds, TL, h, tag);
+      wide_run<MOE_Q_IQ1M_LIKE, true>(L, It, X, cur_tok, q, kprime, XSource{x, H, 32}, sorted_slot, lds, TL, h, tag);
   }
 
   // ---- 3. the down rows of the wave's first slot (slot = wave) in the workgroup's first
@@ -265,7 +261,7 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
     const BankLds &B = S.banks[uniform(P.bank)];
     const QMat Wd = bank_mat(B, uniform(P.e), kDown);
     dqt0 = uniform(B.qt);
-    Rd0 = dqt0 == MOE_Q_IQ2XS_LIKE ? load_row<MOE_Q_IQ2XS_LIKE>(Wd, I, tile * RPP + sub, lq)
+    Rd0 = fmt_iq2<FMT>(dqt0) ? load_row<MOE_Q_IQ2XS_LIKE>(Wd, I, tile * RPP + sub, lq)
                                    : load_row<MOE_Q_IQ1M_LIKE>(Wd, I, tile * RPP + sub, lq);
   }
   float acc_in = 0.0f;
@@ -288,14 +284,14 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
         const BankLds &B = S.banks[uniform(P.bank)];
         const QMat Wd = bank_mat(B, uniform(P.e), kDown);
         qt = uniform(B.qt);
-        R = qt == MOE_Q_IQ2XS_LIKE ? load_row<MOE_Q_IQ2XS_LIKE>(Wd, I, tile * RPP + sub, lq)
+        R = fmt_iq2<FMT>(qt) ? load_row<MOE_Q_IQ2XS_LIKE>(Wd, I, tile * RPP + sub, lq)
                                    : load_row<MOE_Q_IQ1M_LIKE>(Wd, I, tile * RPP + sub, lq);
       }
       // the slot's h row (written by other workgroups) into the wave's LDS area
       stage_h_row<LPR>(h + (size_t)S.pos_of[j] * I, tag, hs, sync);
       __builtin_amdgcn_wave_barrier();
       const float *hrow = hs + lq * kChunkPad;
-      const float v = qt == MOE_Q_IQ2XS_LIKE ? down_slot_dot<MOE_Q_IQ2XS_LIKE, LPR>(R, hrow, lq, lds, TL)
+      const float v = fmt_iq2<FMT>(qt) ? down_slot_dot<MOE_Q_IQ2XS_LIKE, LPR>(R, hrow, lq, lds, TL)
                                              : down_slot_dot<MOE_Q_IQ1M_LIKE, LPR>(R, hrow, lq, lds, TL);
       if (lq == 0) S.ydot[j][sub] = v;
       __builtin_amdgcn_wave_barrier();  // the staging area is reused by the next slot
@@ -430,7 +426,7 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_stack_decode(
   constexpr int ipe = I / kWideRows;
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
   const int kprime = k + add_shared;
-  const TableLayout TL = table_layout(formats);
+  const TableLayout TL = table_layout(formats, kTabIq1 | kTabIq1Delta);
   float *hs = (float *)(lds + TL.bytes) + wave * HS;
   const TableRegs tr = tables_load(grids, formats, threadIdx.x - 64, blockDim.x - 64);
   uint32_t tag = 0;
@@ -592,7 +588,7 @@ hipError_t launch_stack_decode(const LayerArgs *d_tab, int n_layers, int formats
   uint64_t *hp = (uint64_t *)((uint8_t *)ws + stack_pairs_offset(n_layers));
   uint64_t *rp = hp + (size_t)n_layers * kprime * inter;
   const dim3 grid((unsigned)(cus < kBarGroup * kBarGroups ? cus : kBarGroup * kBarGroups)), block(64 * kFusedWaves);
-  const size_t lds_bytes = table_layout(formats).bytes + fused_stage_floats(lpr) * sizeof(float);
+  const size_t lds_bytes = table_layout(formats, kTabIq1 | kTabIq1Delta).bytes + fused_stage_floats(lpr) * sizeof(float);
   const bool one_tile = grid.x >= (unsigned)(2048 / (64 / lpr));
   auto kern = lpr == 8 ? (one_tile ? k_stack_decode<8, true> : k_stack_decode<8, false>)
                        : (one_tile ? k_stack_decode<4, true> : k_stack_decode<4, false>);
@@ -604,7 +600,7 @@ hipError_t launch_stack_decode(const LayerArgs *d_tab, int n_layers, int formats
 size_t fused_sync_bytes() { return sizeof(FusedSync); }
 
 size_t fused_lds_bytes(const LayerArgs &L) {
-  return table_layout(L.formats).bytes + fused_stage_floats(L.inter / 64) * sizeof(float);
+  return table_layout(L.formats, kTabIq1 | kTabIq1Delta).bytes + fused_stage_floats(L.inter / 64) * sizeof(float);
 }
 
 hipError_t launch_layer_decode(const LayerArgs &L, const float *logits, const float *x, int E, int k, int add_shared,
@@ -620,12 +616,13 @@ hipError_t launch_layer_decode(const LayerArgs &L, const float *logits, const fl
   const int lpr = L.inter / 64;
   const dim3 grid((unsigned)(cus < kBarGroup * kBarGroups ? cus : kBarGroup * kBarGroups)), block(64 * kFusedWaves);
   FusedSync *sync = (FusedSync *)ws;
-  if (lpr == 8)
-    hipLaunchKernelGGL(k_layer_decode<8>, grid, block, fused_lds_bytes(L), s, L, logits, x, E, k, add_shared, ids, w,
-                       counts, offsets, sorted_slot, slot_pos, work, acc, sync);
-  else
-    hipLaunchKernelGGL(k_layer_decode<4>, grid, block, fused_lds_bytes(L), s, L, logits, x, E, k, add_shared, ids, w,
-                       counts, offsets, sorted_slot, slot_pos, work, acc, sync);
+  const bool both = L.formats == (MOE_Q_IQ2XS_LIKE | MOE_Q_IQ1M_LIKE), iq2 = L.formats == MOE_Q_IQ2XS_LIKE;
+  auto kern = lpr == 8 ? (both ? k_layer_decode<8, MOE_Q_IQ2XS_LIKE | MOE_Q_IQ1M_LIKE>
+                              : iq2 ? k_layer_decode<8, MOE_Q_IQ2XS_LIKE> : k_layer_decode<8, MOE_Q_IQ1M_LIKE>)
+                       : (both ? k_layer_decode<4, MOE_Q_IQ2XS_LIKE | MOE_Q_IQ1M_LIKE>
+                              : iq2 ? k_layer_decode<4, MOE_Q_IQ2XS_LIKE> : k_layer_decode<4, MOE_Q_IQ1M_LIKE>);
+  hipLaunchKernelGGL(kern, grid, block, fused_lds_bytes(L), s, L, logits, x, E, k, add_shared, ids, w, counts, offsets,
+                     sorted_slot, slot_pos, work, acc, sync);
   return hipGetLastError();
 }
 

@@ -135,7 +135,7 @@ constexpr int kWideWaves = 12;
 static_assert(64 * kWideWaves >= 2048 / 4 && 2 * 64 * kWideWaves >= MOE_MAX_IDS,
               "staging: one float4 of each token per thread; two work records per thread");
 constexpr int kXStageTokens = 8;
-constexpr int kXLaneRow = 36;                 // floats per lane slice in the staging (32 + 4 group sums)
+constexpr int kXLaneRow = 36;                 // floats per lane slice in the staging
 constexpr int kXTokRow = 64 * kXLaneRow;      // floats per staged token
 
 // LDS after the grid tables: the staged activations (room for kXStageTokens tokens,
@@ -154,7 +154,7 @@ __global__ void __launch_bounds__(64 * kWideWaves) k_gateup_wide(LayerArgs L, co
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ BankLds banks[MOE_MAX_BANKS];
   const int q = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
-  const TableLayout TL = table_layout(QT);
+  const TableLayout TL = table_layout(QT, kTabIq1Delta);
   const TableRegs tr = tables_load(L.grids, QT);
   const int ipe = L.inter / kWideRows, stride = gridDim.x * kWideWaves;
   const int n1 = sload(&work[0].e), total = n1 * ipe;
@@ -186,18 +186,6 @@ __global__ void __launch_bounds__(64 * kWideWaves) k_gateup_wide(LayerArgs L, co
   }
   if (threadIdx.x == 0) fill_banks(L, banks);
   tables_store(tr, QT, TL, lds);  // also publishes the records, the activations and the bank table
-  if constexpr (STAGED && QT == MOE_Q_IQ1M_LIKE) {
-    // the 8-column group sums (times 1/8) of every staged lane slice, in the slice's
-    // padding: thread i < 512 takes slice i % 64 of token i / 64, summing in column order
-    if (threadIdx.x < kXStageTokens * 64) {
-      float *sl = xs + (threadIdx.x >> 6) * kXTokRow + (threadIdx.x & 63) * kXLaneRow;
-      X32 Xs;
-      load_x32(sl, Xs);
-      group_sums32(Xs);
-      *(float4 *)(sl + 32) = make_float4(Xs.gs8[0], Xs.gs8[1], Xs.gs8[2], Xs.gs8[3]);
-    }
-    __syncthreads();
-  }
   // three items in flight per wave: A is computed while B and C load.  Items of the
   // other format are skipped (a layer with both formats runs this kernel once per format).
   // (items are passed by value: a by-reference hand-off put them in scratch memory, whose
@@ -217,10 +205,9 @@ __global__ void __launch_bounds__(64 * kWideWaves) k_gateup_wide(LayerArgs L, co
   const XSource xsrc = STAGED ? XSource{xs, kXTokRow, kXLaneRow} : XSource{x, L.hidden, 32};
   X32 X;
   int cur_tok = -1;
-  bool gs_ok = false;
   auto run = [&](WideItem &D) {
     if (D.qt == QT && D.W.p1 - D.W.p0 <= max_tokens)
-      wide_run<QT, false, STAGED>(L, D, X, cur_tok, gs_ok, q, kprime, xsrc, sorted_slot, lds, TL, h);
+      wide_run<QT>(L, D, X, cur_tok, q, kprime, xsrc, sorted_slot, lds, TL, h);
   };
   // unrolled by three so that each buffer keeps its registers (no copies between them)
   int it = blockIdx.x * kWideWaves + wave;
@@ -461,7 +448,7 @@ hipError_t launch_gateup_gemv(const LayerArgs &L, const float *x, int T, int kpr
     const dim3 g(grid < 1 ? 1 : grid), b(64 * kWideWaves);
     for (int qt : {MOE_Q_IQ2XS_LIKE, MOE_Q_IQ1M_LIKE}) {
       if (!(L.formats & qt)) continue;
-      const size_t bytes = table_layout(qt).bytes + wide_stage_bytes(T) + recs;
+      const size_t bytes = table_layout(qt, kTabIq1Delta).bytes + wide_stage_bytes(T) + recs;
       if (T <= kXStageTokens && qt == MOE_Q_IQ2XS_LIKE)
         hipLaunchKernelGGL((k_gateup_wide<true, MOE_Q_IQ2XS_LIKE>), g, b, bytes, s, L, x, T, kprime, sorted_slot, work,
                            max_tokens, n_ids, h);

@@ -23,22 +23,31 @@ __device__ __forceinline__ uint2 load_stream8(const uint8_t *p) {
 // ----------------------------------------------------------------------------- LDS tables
 // fp16 grid rows (8 values, 16 bytes per row) and the IQ2 sign-mask rows: entry s (the
 // 7 explicit sign bits) holds, per pair of weights, 0x8000 in each half whose weight is
-// negative, the 8th sign being the parity of the 7.
+// negative, the 8th sign being the parity of the 7.  IQ1 has two tables: the grid rows
+// (kTabIq1), and the rows with the group's delta already added (kTabIq1Delta): row
+// idx + 2048 s holds grid[idx][j] + 1/8 for s = 0 and grid[idx][j] - 1/8 for s = 1 (all
+// exact in fp16), so a dot product reads each weight's value up to its scale directly.
+constexpr int kTabIq1 = 1, kTabIq1Delta = 2;
+
 struct TableLayout {
-  int iq2h, iq2m, iq1h, bytes;  // byte offsets in dynamic LDS
+  int iq2h, iq2m, iq1h, iq1d, bytes;  // byte offsets in dynamic LDS (-1: not built)
 };
 
-__host__ __device__ inline TableLayout table_layout(int formats) {
-  TableLayout t{0, 0, 0, 0};
+__host__ __device__ inline TableLayout table_layout(int formats, int iq1_tables = kTabIq1) {
+  TableLayout t{-1, -1, -1, -1, 0};
   if (formats & MOE_Q_IQ2XS_LIKE) {
     t.iq2h = t.bytes;
     t.bytes += kIq2Rows * 16;
     t.iq2m = t.bytes;
     t.bytes += 128 * 16;
   }
-  if (formats & MOE_Q_IQ1M_LIKE) {
+  if ((formats & MOE_Q_IQ1M_LIKE) && (iq1_tables & kTabIq1)) {
     t.iq1h = t.bytes;
     t.bytes += kIq1Rows * 16;
+  }
+  if ((formats & MOE_Q_IQ1M_LIKE) && (iq1_tables & kTabIq1Delta)) {
+    t.iq1d = t.bytes;
+    t.bytes += 2 * kIq1Rows * 16;
   }
   return t;
 }
@@ -105,7 +114,7 @@ __device__ __forceinline__ void tables_store(const TableRegs &tr, int formats, c
       masks[s] = make_uint4(m[0], m[1], m[2], m[3]);
     }
   }
-  if (formats & MOE_Q_IQ1M_LIKE) {
+  if ((formats & MOE_Q_IQ1M_LIKE) && TL.iq1h >= 0) {
     const uint32_t h0 = f16_bits((float)kIq1SymVal[0]), h1 = f16_bits((float)kIq1SymVal[1]),
                    h2 = f16_bits((float)kIq1SymVal[2]);
     uint4 *rows = (uint4 *)(lds + TL.iq1h);
@@ -113,6 +122,22 @@ __device__ __forceinline__ void tables_store(const TableRegs &tr, int formats, c
     for (int i = 0; i < kTableRowsPerThread; i++) {
       const int r = t + i * n;
       if (t >= 0 && r < kIq1Rows) rows[r] = expand_row_f16(tr.c1[i], h0, h1, h2);
+    }
+  }
+  if ((formats & MOE_Q_IQ1M_LIKE) && TL.iq1d >= 0) {
+    const float d = 0.125f;
+    const uint32_t p0 = f16_bits((float)kIq1SymVal[0] + d), p1 = f16_bits((float)kIq1SymVal[1] + d),
+                   p2 = f16_bits((float)kIq1SymVal[2] + d);
+    const uint32_t m0 = f16_bits((float)kIq1SymVal[0] - d), m1 = f16_bits((float)kIq1SymVal[1] - d),
+                   m2 = f16_bits((float)kIq1SymVal[2] - d);
+    uint4 *rows = (uint4 *)(lds + TL.iq1d);
+#pragma unroll
+    for (int i = 0; i < kTableRowsPerThread; i++) {
+      const int r = t + i * n;
+      if (t >= 0 && r < kIq1Rows) {
+        rows[r] = expand_row_f16(tr.c1[i], p0, p1, p2);
+        rows[r + kIq1Rows] = expand_row_f16(tr.c1[i], m0, m1, m2);
+      }
     }
   }
   if (sync) __syncthreads();

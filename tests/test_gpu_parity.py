@@ -183,6 +183,9 @@ LAYER_CASES = {
     # accumulate holds more slots than it loads up front
     "top16_shared_t8": ([(IQ2, 32), (IQ1, 32)], 2048, 512, 64, 1, 8, 16, 0.0),
     "top13_t5": ([(IQ1, 24), (IQ2, 24)], 2048, 512, 48, 0, 5, 13, 0.0),
+    # one format at inter 256: the one-launch kernel's single-format instances, 4 lanes per row
+    "decode_iq1_i256": ([(IQ1, 16)], 2048, 256, 16, 1, 1, 4, 0.0),
+    "decode_iq2_i256": ([(IQ2, 16)], 2048, 256, 16, 0, 1, 5, 0.0),
 }
 
 
@@ -324,7 +327,7 @@ def call_counts(ws):
 
 
 FUSED_CASES = ["decode_iq2_top10_shared", "tiny16_top4_iq2", "mixed_h2048_t24_zipf", "decode_mixed_i256_shared",
-               "decode_iq1s_top10_shared"]
+               "decode_iq1s_top10_shared", "decode_iq1_i256", "decode_iq2_i256"]
 
 
 @pytest.mark.parametrize("name", FUSED_CASES)
