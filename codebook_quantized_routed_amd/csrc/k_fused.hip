@@ -181,7 +181,7 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
   // tables into LDS meanwhile
   if (wave == 0) {
     if (logits) {
-      topk_select<8>(tv, E, k, add_shared, blockIdx.x == 0 ? ids : nullptr, w, S.ids, S.w, S.topk);
+      topk_select<8, 1, 16>(tv, E, k, add_shared, blockIdx.x == 0 ? ids : nullptr, w, S.ids, S.w, S.topk);
     } else {
       if (lane < k) {
         S.ids[lane] = ids[lane];
