@@ -379,7 +379,7 @@ __device__ inline void route_wave(const float *logits, const LayerArgs &L, int E
                                   int32_t *ids_out, float *w_out, RouteLds &R, TopkLds &T) {
   const int lane = threadIdx.x & 63, kprime = k + add_shared;
   const TopkVals<8> tv = topk_load<8>(logits, E);
-  topk_select<8, 2>(tv, E, k, add_shared, ids_out, w_out, R.ids, R.w, T);
+  topk_select<8, 2, 16>(tv, E, k, add_shared, ids_out, w_out, R.ids, R.w, T);
   __builtin_amdgcn_wave_barrier();
   const int my = lane < kprime ? R.ids[lane] : 0x7FFFFFFF;
   const int rank = slot_rank(my, lane);

@@ -112,9 +112,8 @@ __device__ __forceinline__ TopkVals<VPL> topk_load(const float *__restrict__ l, 
 // ballot -> scalar count -> select, more ballots per step cost issue slots: one bit is
 // the faster where the wave has its SIMD mostly to itself, two where it shares it with
 // busy waves (the next layer's routing inside the stack kernel).  TAU_LOW: tau's bits
-// below this one are not searched (stay zero).  Measured: 16 is the faster in the
-// routing kernels and the one-layer decode kernel, 0 in the stack kernel's routing
-// wave; the selection is the same.
+// below this one are not searched (stay zero); every caller takes 16, measured the
+// faster (or as fast) in each kernel.  The selection is the same.
 template <int VPL, int TAU_BITS = 1, int TAU_LOW = 0>
 __device__ __forceinline__ void topk_select(const TopkVals<VPL> &tv, int E, int k, int add_shared,
                                             int32_t *__restrict__ ids, float *__restrict__ w, int32_t *ids_copy,
