@@ -7,8 +7,9 @@ and the weighted accumulation.  Default workload: the field-shape decode layer
 (hidden 2048, 512 experts + 1 shared, expert intermediate 512, IQ2_XS-like weights,
 1 token, top-10).  Inputs are resident in HBM before timing starts.  To keep the
 256 MB last-level cache from serving the weights, each step reads a different copy of
-the layer (--rotate copies, distinct device buffers with identical bytes) and a fresh
-batch (distinct seeded activations and logits per step).
+the layer (--rotate copies, distinct device buffers with identical bytes; by default
+enough copies that no byte is read again before at least 256 MB of other weights have
+been) and a fresh batch (distinct seeded activations and logits per step).
 
 One-token decode runs the whole layer in one launch (moe_layer_decode_q); the
 three-call path (route, gate/up, down fused with the accumulation) is timed beside it.
@@ -62,8 +63,68 @@ TRAFFIC_FILES = {"decode_iq2": "profiles/hbm_traffic_decode_iq2_t1.txt",
                  "stack48": "profiles/hbm_traffic_stack48_decode.txt"}
 
 
+# Bytes the last-level cache (256 MB) and the eight 4 MB L2s can hold together: a weight
+# read again only after more than this many bytes of other weights comes from HBM.
+LLC_REUSE_BYTES = 288 << 20
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def rotation_copies(layer, T, k, shared, max_copies=64):
+    """Copies of the layer to cycle through so that no weight is read again within
+    LLC_REUSE_BYTES of other steps' weights: a step reads at most min(E, T k) routed
+    experts plus the shared one; the smallest step is bounded below by k distinct experts
+    (one token) and the shared one."""
+    E = layer.n_experts
+    per_expert = min(layer.expert_bytes(e) for e in range(E + shared))
+    step_min = (min(E, k) + shared) * per_expert
+    return int(min(max_copies, max(2, -(-LLC_REUSE_BYTES // step_min) + 1)))
+
+
+def percentiles(samples_ms):
+    a = np.sort(np.asarray(samples_ms, dtype=np.float64)) * 1e3
+    return {"p10_us": round(float(np.percentile(a, 10)), 3), "p50_us": round(float(np.percentile(a, 50)), 3),
+            "p90_us": round(float(np.percentile(a, 90)), 3), "n": int(a.size)}
+
+
+def step_distribution(step, first, n):
+    """Per-step times of n consecutive steps (step(i) for i = first .. first+n-1), from an
+    event recorded between every two steps on the launch stream, with the steps queued
+    behind a GPU sleep so that the host does not starve the queue.  Each interval holds
+    one step plus one event record."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(50_000_000)
+    ev[0].record()
+    for j in range(n):
+        step(first + j)
+        ev[j + 1].record()
+    torch.cuda.synchronize()
+    return [ev[j].elapsed_time(ev[j + 1]) for j in range(n)]
+
+
+def cpu_info():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count(), "affinity": len(os.sched_getaffinity(0))}
+
+
+def oracle_threads():
+    """Threads for the oracle's all-core run: the cores this process may use, capped by
+    OMP_NUM_THREADS when it is set (the CPU share the machine gives this job)."""
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    return max(1, min(n, int(env))) if env.isdigit() else n
 
 
 def _code_only(src: str) -> str:
@@ -108,7 +169,11 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_iq2", choices=list(WORKLOADS))
-    ap.add_argument("--rotate", type=int, default=11, help="distinct copies of the layer cycled through")
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="distinct copies of the layer cycled through (0: enough that a copy is read again only "
+                         "after more than LLC_REUSE_BYTES of other weights)")
+    ap.add_argument("--dist-steps", type=int, default=256,
+                    help="steps timed one by one for the p10 / p50 / p90 of the step time")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a captured graph")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU-baseline sample")
     ap.add_argument("--no-cpu", action="store_true")
@@ -147,9 +212,11 @@ def main():
     grids = torch.empty(moe.grids_bytes(), dtype=torch.uint8, device=dev)
     moe.grids_expand(torch.from_numpy(c2.view(np.int16)).to(dev), torch.from_numpy(c1.view(np.int16)).to(dev), grids)
     layers = [moe.DeviceLayer(H, I, E, shared, layer.banks, grids)]
+    if args.rotate <= 0:  # a copy's bytes come back only after LLC_REUSE_BYTES of other steps' weights
+        args.rotate = rotation_copies(layer, T, k, shared)
     for _ in range(args.rotate - 1):  # distinct buffers, identical bytes
-        layers.append(moe.DeviceLayer(H, I, E, shared, layer.banks, grids))
-    n_in = args.steps + args.warmup
+        layers.append(layers[0].copy())
+    n_in = max(args.steps, args.dist_steps) + args.warmup
     xs = torch.from_numpy(synth.activations(n_in * T, H, tag="bench/x")).to(dev).view(n_in, T, H)
     lgs = torch.from_numpy(synth.logits(n_in * T, E, tag="bench/l", zipf_alpha=zipf)).to(dev).view(n_in, T, E)
     log(f"inputs ready in {time.time() - t0:.1f}s: {args.rotate} x {layers[0].bytes / 1e6:.1f} MB layers")
@@ -312,6 +379,14 @@ def main():
         torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
     tok_s = T / (ms * 1e-3)
+    # the same steps one by one (fresh inputs, the layer copies in rotation), for the
+    # spread of the step time
+    dist = percentiles(step_distribution(step, args.warmup, args.dist_steps))
+    status = 0
+    if fused:  # a timed-out wait in any of the one-launch calls above leaves its word set
+        status = moe.decode_error(ws)
+        if status:
+            log("one-launch decode reported a timed-out wait: its results are undefined")
 
     gu_b, dn_b, st_b = float(np.mean(gu_bytes)), float(np.mean(dn_bytes)), float(np.mean(step_bytes))
     if fused:  # the dominant (only) kernel: the whole layer in one launch
@@ -337,7 +412,10 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": desc, "tokens_per_step": T, "experts": E, "shared_experts": shared, "top_k": k,
-                   "hidden": H, "inter": I, "rotation_copies": args.rotate, "timing": mode},
+                   "hidden": H, "inter": I, "rotation_copies": args.rotate,
+                   "rotation_bytes": int(args.rotate * layers[0].bytes), "timing": mode},
+        "step_time": dict(dist, over="steps timed one by one, an event between every two (each interval holds "
+                                      "one step and one event record)"),
         "step_hbm_gbs": round(st_b / (ms * 1e-3) / 1e9, 1),
         "step_hbm_frac": round(st_b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": int(st_b),
@@ -356,6 +434,7 @@ def main():
                    "frac_of_hbm_peak": round(router_bytes / (kms["router"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                    "traffic": measured_traffic(args.workload, "k_router"), "parity": router_parity},
         "parity": parity,
+        "decode_status": status,
     }
     if path == "prefill":
         ffn_ms = kms["gateup"] + kms["down"]
@@ -367,6 +446,8 @@ def main():
         out["cpu_baseline"] = cpu_baseline(layer, c2, c1, xs.cpu().numpy(), lgs.cpu().numpy(), k, shared, T,
                                            args.cpu_seconds)
     print(json.dumps(out), flush=True)
+    if status or not parity["pass"]:
+        sys.exit(1)
 
 
 def check_router_parity(x, wr, wsg, lg_gpu, sw_gpu, bound=64 * 2.0 ** -24):
@@ -473,6 +554,11 @@ def run_stack(args, desc):
     hd = h_dec0.clone()
     chain_ms, mode = time_decode_steps(args, lambda s: st.step(hd[s], lg_dec[s]), ND)
     dec_ms, mode = time_decode_steps(args, lambda s: st.decode(h_dec0[s], hd_out[s], lg_dec[s]), ND)
+    dist = percentiles(step_distribution(lambda s: st.decode(h_dec0[s % ND], hd_out[s % ND], lg_dec[s % ND]), 0,
+                                         max(ND, args.dist_steps)))
+    status = max(st.stack_error(), st.decode_error(1))
+    if status:
+        log("one-launch decode reported a timed-out wait: its results are undefined")
     per_layer_tok_s = nl / (dec_ms * 1e-3)
     achieved = dec_bytes / (dec_ms * 1e-3) / 1e9
     out = {
@@ -495,7 +581,8 @@ def run_stack(args, desc):
                    "kernel": "k_stack_decode (one launch, 48 layers)",
                    "per_layer_chain_us_per_step": round(chain_ms * 1e3, 2),
                    "algorithmic_bytes_per_step": int(dec_bytes), "achieved_gbs": round(achieved, 1),
-                   "frac_of_hbm_peak": round(achieved / HBM_PEAK_GBS, 4)},
+                   "frac_of_hbm_peak": round(achieved / HBM_PEAK_GBS, 4),
+                   "step_time": dict(dist, over="decode steps timed one by one, an event between every two")},
         "prefill": {"ms": round(pre_ms, 3), "tokens_per_s_per_layer": round(TP * nl / (pre_ms * 1e-3), 1),
                     "stack_tokens_per_s": round(TP / (pre_ms * 1e-3), 1)},
         "roofline": {"bound": "hbm", "kernel": "k_stack_decode",
@@ -503,11 +590,14 @@ def run_stack(args, desc):
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic("stack48", "k_stack_decode"),
                      "bytes_per_launch": int(dec_bytes), "launch_us": round(dec_ms * 1e3, 3)},
         "parity": parity,
+        "decode_status": status,
     }
     if not args.no_cpu:
         out["cpu_baseline"] = stack_cpu_baseline(host, formats, c2, c1, h_dec0.cpu().numpy(), lg_host, k, shared,
                                                  args.cpu_seconds)
     print(json.dumps(out), flush=True)
+    if status or not parity["pass"]:
+        sys.exit(1)
 
 
 def time_decode_steps(args, step, n):
@@ -545,49 +635,60 @@ def time_decode_steps(args, step, n):
     return e0.elapsed_time(e1) / n, "eager"
 
 
-def check_stack_parity(host, formats, c2, c1, ins, outs, ids_gpu, lg, k, shared, bound=3e-5):
+def check_stack_parity(host, formats, c2, c1, ins, outs, ids_gpu, lg, k, shared, bound=2e-5, bound_delta=3e-5):
     """Each layer l of one decode step: the oracle's h + MoE_l(RMSNorm(h)) from the GPU's
-    input h to layer l, against the GPU's output, relative to the layer's MoE output."""
+    input h to layer l, against the GPU's output: max |error| within bound of the layer
+    output's L2 norm, and within bound_delta of the layer's MoE output (output - input)."""
     import oracle as O
-    O.set_threads(min(16, len(os.sched_getaffinity(0))))
     g = O.grids(c2, c1)
     tabs = {qt: O.ExpertTable(host[qt]) for qt in host}
-    worst, ok = 0.0, True
+    worst, worst_d, ok = 0.0, 0.0, True
     for l, (hin, hout) in enumerate(zip(ins, outs)):  # [1][H] each
         x = O.rmsnorm(hin)
-        r = O.moe_layer(tabs[formats[l]], g, x, k, shared, logits=lg[l], acc=hin)
+        r = O.moe_layer(tabs[formats[l]], g, x, k, shared, logits=lg[l], acc=hin, n_threads=oracle_threads())
         ok &= bool(np.array_equal(r["ids"][0], ids_gpu[l][0]))
+        err = float(np.abs(hout[0].astype(np.float64) - r["acc"][0]).max())
         delta = r["acc"][0].astype(np.float64) - hin[0]
-        worst = max(worst, float(np.abs(hout[0].astype(np.float64) - r["acc"][0]).max() / np.linalg.norm(delta)))
-    O.set_threads(1)
+        worst = max(worst, err / float(np.linalg.norm(r["acc"][0].astype(np.float64))))
+        worst_d = max(worst_d, err / float(np.linalg.norm(delta)))
     return {"layers_checked": len(ins), "ids_bit_exact": ok, "max_err_rel_l2": float(f"{worst:.3e}"),
-            "bound": bound, "pass": bool(ok and worst <= bound)}
+            "bound": bound, "max_err_rel_delta_l2": float(f"{worst_d:.3e}"), "bound_delta": bound_delta,
+            "pass": bool(ok and worst <= bound and worst_d <= bound_delta)}
 
 
 def stack_cpu_baseline(host, formats, c2, c1, h0, lg, k, shared, budget_s):
-    """The oracle's decode step through the whole stack (RMSNorm + layer per layer), on the
-    host cores, over a bounded number of steps."""
+    """The oracle's decode step through the whole stack (RMSNorm + layer per layer), on
+    all the cores this job may use, over a bounded number of steps; then one thread on
+    a sample of layers (every fourth layer of the first step, so both formats)."""
     import oracle as O
-    cores = min(16, len(os.sched_getaffinity(0)))
+    cores = oracle_threads()
     g = O.grids(c2, c1)
     tabs = {qt: O.ExpertTable(host[qt]) for qt in host}
-    t0 = time.time()
+    t0 = time.monotonic()
     n = 0
-    while n < 1 or time.time() - t0 < budget_s:
+    while n < 1 or time.monotonic() - t0 < budget_s:
         h = h0[n % len(h0)].astype(np.float32).reshape(1, -1).copy()
         for l in range(len(formats)):
             x = O.rmsnorm(h)
             h = O.moe_layer(tabs[formats[l]], g, x, k, shared, logits=lg[n % len(lg), l], acc=h,
                             n_threads=cores)["acc"]
         n += 1
-    dt = time.time() - t0
+    dt = time.monotonic() - t0
+    sample = list(range(0, len(formats), 4))
+    h = h0[0].astype(np.float32).reshape(1, -1).copy()
+    t1 = time.monotonic()
+    for l in sample:
+        O.moe_layer(tabs[formats[l]], g, O.rmsnorm(h), k, shared, logits=lg[0, l], acc=h, n_threads=1)
+    dt1 = time.monotonic() - t1
     return {"value": round(n * len(formats) / dt, 3), "unit": "tokens/s/layer", "cores": cores, "kind": "oracle",
-            "sample": f"{n} decode step(s) through {len(formats)} layers, {dt:.1f} s, OpenMP over output rows"}
+            "sample": f"{n} decode step(s) through {len(formats)} layers, {dt:.1f} s, OpenMP over output rows",
+            "single_thread": {"value": round(len(sample) / dt1, 3), "unit": "tokens/s/layer", "cores": 1,
+                              "sample": f"{len(sample)} layers (every fourth) of one decode step, {dt1:.1f} s"},
+            **cpu_info()}
 
 
 def check_parity(layer, c2, c1, x, lg, k, shared, acc_gpu, ids_gpu, max_tokens=4):
     import oracle as O
-    O.set_threads(min(16, len(os.sched_getaffinity(0))))
     g = O.grids(c2, c1)
     tab = O.ExpertTable(layer)
     T = x.shape[0]
@@ -595,29 +696,43 @@ def check_parity(layer, c2, c1, x, lg, k, shared, acc_gpu, ids_gpu, max_tokens=4
     worst = 0.0
     ok = True
     for t in toks:
-        r = O.moe_layer(tab, g, x[t:t + 1], k, shared, logits=lg[t:t + 1])
+        r = O.moe_layer(tab, g, x[t:t + 1], k, shared, logits=lg[t:t + 1], n_threads=oracle_threads())
         ok &= bool(np.array_equal(r["ids"][0], ids_gpu[t]))
         err = np.abs(acc_gpu[t].astype(np.float64) - r["acc"][0]).max() / np.linalg.norm(r["acc"][0])
         worst = max(worst, float(err))
-    O.set_threads(1)
     return {"tokens_checked": len(toks), "ids_bit_exact": ok, "max_err_rel_l2": float(f"{worst:.3e}"),
             "bound": 2e-5, "pass": bool(ok and worst <= 2e-5)}
 
 
+def time_oracle(run, n_threads, budget_s):
+    """Steps of run(i, n_threads) until budget_s has passed (at least one); returns
+    (steps, seconds).  Wall clock (CLOCK_MONOTONIC)."""
+    t0 = time.monotonic()
+    n = 0
+    while n < 1 or time.monotonic() - t0 < budget_s:
+        run(n, n_threads)
+        n += 1
+    return n, time.monotonic() - t0
+
+
 def cpu_baseline(layer, c2, c1, xs, lgs, k, shared, T, budget_s):
-    """The oracle as it stands, on the host cores, over a bounded sample of steps."""
+    """The oracle as it stands, on the host cores, over a bounded sample of steps: all
+    cores this job may use (the reported value), then one thread."""
     import oracle as O
-    cores = min(16, len(os.sched_getaffinity(0)))
+    cores = oracle_threads()
     g = O.grids(c2, c1)
     tab = O.ExpertTable(layer)
-    t0 = time.time()
-    n = 0
-    while n < 1 or time.time() - t0 < budget_s:  # cycles over the steps' inputs
-        O.moe_layer(tab, g, xs[n % len(xs)], k, shared, logits=lgs[n % len(lgs)], n_threads=cores)
-        n += 1
-    dt = time.time() - t0
+
+    def run(n, threads):  # cycles over the steps' inputs
+        O.moe_layer(tab, g, xs[n % len(xs)], k, shared, logits=lgs[n % len(lgs)], n_threads=threads)
+
+    n, dt = time_oracle(run, cores, budget_s)
+    n1, dt1 = time_oracle(run, 1, 0.5 * budget_s)
     return {"value": round(n * T / dt, 3), "unit": "tokens/s/layer", "cores": cores, "kind": "oracle",
-            "sample": f"{n} steps x {T} token(s) of the same workload, {dt:.1f} s, OpenMP over output rows"}
+            "sample": f"{n} steps x {T} token(s) of the same workload, {dt:.1f} s, OpenMP over output rows",
+            "single_thread": {"value": round(n1 * T / dt1, 3), "unit": "tokens/s/layer", "cores": 1,
+                              "sample": f"{n1} steps, {dt1:.1f} s"},
+            **cpu_info()}
 
 
 if __name__ == "__main__":

@@ -30,6 +30,7 @@ def matvec_max_tokens(T: int) -> int:
     return T if T <= SMALL_BATCH_TOKENS else MATVEC_MAX_TOKENS
 MFMA_TILE_TOKENS = 16  # tokens per matrix-core tile (MOE_MFMA_TILE_TOKENS)
 DECODE_SYNC_BYTES = 4352  # synchronisation words at the start of a decode workspace (MOE_DECODE_SYNC_BYTES)
+DECODE_ERROR_OFFSET = 128  # byte offset of the uint32 status word in it (MOE_DECODE_ERROR_OFFSET)
 MAX_STACK_LAYERS = 256  # MOE_MAX_STACK_LAYERS
 
 STATUS = {0: "MOE_OK", -1: "MOE_E_NULL", -2: "MOE_E_SHAPE", -3: "MOE_E_QTYPE", -4: "MOE_E_ALIGN",
@@ -188,6 +189,23 @@ def layer_decode_q(layer: Layer, logits, x, k, add_shared, ids, w, counts, offse
                                   _ptr(acc), _ptr(ws), nbytes, _stream(stream)))
 
 
+def decode_error(ws) -> int:
+    """The status word of a one-launch decode workspace (moe_layer_decode_q,
+    moe_stack_decode_q): nonzero when a wait of an earlier call timed out, which leaves
+    that call's results undefined.  Waits for the device to finish its queued work."""
+    import torch
+    torch.cuda.synchronize(ws.device)
+    return int(ws.view(torch.uint8)[DECODE_ERROR_OFFSET:DECODE_ERROR_OFFSET + 4].view(torch.int32).item())
+
+
+def check_decode(ws) -> None:
+    """Raises when the workspace's status word reports a timed-out wait."""
+    err = decode_error(ws)
+    if err:
+        raise RuntimeError(f"one-launch decode: a wait for another workgroup's values timed out (status {err}); "
+                           "the results are undefined and the workspace must be zeroed before reuse")
+
+
 def accumulate(y, w, ids, slot_pos, T, kprime, hidden, acc, stream=None):
     _check("moe_accumulate", lib.moe_accumulate(_ptr(y), _ptr(w), _ptr(ids), _ptr(slot_pos), T, kprime, hidden,
                                                 _ptr(acc), _stream(stream)))
@@ -300,6 +318,23 @@ class DeviceLayer:
                     self.bytes += t.numel()
                     arr[j] = t.data_ptr()
         self.desc = d
+
+    def copy(self) -> "DeviceLayer":
+        """Another resident copy of the same layer: the same bytes in new device buffers
+        (a device-to-device copy of every stream)."""
+        other = DeviceLayer.__new__(DeviceLayer)
+        other.grids, other.bytes = self.grids, self.bytes
+        other.tensors = [t.clone() for t in self.tensors]
+        d = Layer()
+        C.memmove(C.addressof(d), C.addressof(self.desc), C.sizeof(Layer))
+        remap = {t.data_ptr(): c.data_ptr() for t, c in zip(self.tensors, other.tensors)}
+        for i in range(d.n_banks):
+            for name in ("gate", "up", "down"):
+                arr = getattr(d.banks[i], name)
+                for j in range(3):
+                    arr[j] = remap[arr[j]]
+        other.desc = d
+        return other
 
     def __del__(self):
         self.tensors = []

@@ -335,9 +335,9 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
 // ============================================================================ stack
 // The decode step of a stack of layers for one token in a single launch:
 // h <- h + MoE_l(RMSNorm(h)) for l = 0 .. L-1 ("Red Lite dev16 — complete
-// full-attention parity", sections "Implemented path" and "Build and field validation":
-// the routed MoE follows the post-attention RMSNorm and feeds the residual stream;
-// cross-layer scheduling is the pages' next step).  Per layer, every workgroup:
+// full-attention parity", section "Pinned full-attention graph": the routed MoE follows
+// the post-attention RMSNorm and feeds the residual stream; section "Scope boundary":
+// the 48-layer scheduler is the next gate).  Per layer, every workgroup:
 //  1. stages the layer's input residual (layer 0: the caller's h; later layers: the
 //     previous layer's output rows, tagged pairs written by every workgroup) and
 //     computes RMSNorm with the arithmetic of k_rmsnorm;

@@ -5,14 +5,17 @@
 
 namespace moe {
 
-// Float -> u32 with the same order; every finite value maps above 0x007FFFFF, so 0 can
-// stand for "taken / no value".
+// Float -> u32 with the order of IEEE comparison: key = 2^31 + m for +m and 2^31 - m for
+// -m (m = the magnitude bits), so -0.0 and +0.0 share the key 2^31 and tie, as they
+// compare equal (the tie then goes to the lower id).  Every finite value maps above
+// 0x007FFFFF, so 0 can stand for "taken / no value".
 __device__ __forceinline__ uint32_t orderable(float f) {
-  uint32_t b = __float_as_uint(f);
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  const uint32_t b = __float_as_uint(f), m = b & 0x7FFFFFFFu;
+  return (b & 0x80000000u) ? 0x80000000u - m : 0x80000000u + m;
 }
+// The inverse (a zero key gives +0.0, which behaves as -0.0 in every use of it here).
 __device__ __forceinline__ float from_orderable(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+  return __uint_as_float(k >= 0x80000000u ? k - 0x80000000u : (0x80000000u - k) | 0x80000000u);
 }
 
 // Wave-wide max / min of a u32 through DPP row shifts and row broadcasts (lane 63 ends

@@ -1,9 +1,10 @@
 """A residual chain of routed layers: h <- h + MoE_l(RMSNorm(h)) for l = 0 .. L-1.
 
-"Red Lite dev16 — complete full-attention parity", sections "Implemented path" and
-"Build and field validation": in the field model the routed MoE (routed experts plus a
-shared expert) runs after the post-attention RMSNorm and its output is added to the
-residual stream; the model stacks 48 such layers.  Attention and the rest of the block
+"Red Lite dev16 — complete full-attention parity", section "Pinned full-attention graph"
+(the block composition: post-attention RMSNorm, the full-width top-10 routed MoE plus
+shared expert, then the residual) and section "Scope boundary" (the 48-layer scheduler
+is the next gate): in the field model the routed MoE runs after the post-attention
+RMSNorm and its output is added to the residual stream; the model stacks 48 layers.  Attention and the rest of the block
 are not part of this path, so the chain here is the MoE part of each block alone.
 
 This module only sequences calls of the C ABI (every step runs in the library's
@@ -17,9 +18,9 @@ of the path).
 """
 from __future__ import annotations
 
-from . import (DeviceLayer, accumulate, decode_workspace_bytes, expert_ffn_q, layer_decode_q, rmsnorm,
-               route_group, stack_decode_q, stack_layers, stack_prepare, stack_workspace_bytes, work_ints,
-               workspace_bytes)
+from . import (DeviceLayer, accumulate, check_decode, decode_error, decode_workspace_bytes, expert_ffn_q,
+               layer_decode_q, rmsnorm, route_group, stack_decode_q, stack_layers, stack_prepare,
+               stack_workspace_bytes, work_ints, workspace_bytes)
 
 RMS_EPS = 1e-6
 
@@ -118,6 +119,25 @@ class LayerStack:
         b = self.stack_buffers()
         stack_decode_q(b["layers"], logits_per_layer, h_in, h_out, self.k, self.shared, self.eps, b["ids"], b["w"],
                        b["ws"], stream)
+
+
+    def decode_error(self, T: int = 1) -> int:
+        """Status word of the one-launch per-layer decode's workspace (T = 1 calls of
+        ``layer``); nonzero after a timed-out wait.  Synchronises the device."""
+        b = self._bufs.get(T)
+        return 0 if b is None or T != 1 else decode_error(b["ws"])
+
+    def stack_error(self) -> int:
+        """Status word of the one-launch stack decode's workspace.  Synchronises."""
+        return 0 if self._stack is None else decode_error(self._stack["ws"])
+
+    def check(self) -> None:
+        """Raises if a one-launch call (per layer or whole stack) reported a timed-out
+        wait.  Call it after the stream has run the calls (it synchronises)."""
+        if self._stack is not None:
+            check_decode(self._stack["ws"])
+        if 1 in self._bufs:
+            check_decode(self._bufs[1]["ws"])
 
 
 def device_stack(formats, banks_by_format: dict, grids, hidden: int = 2048, inter: int = 512, n_experts: int = 512,

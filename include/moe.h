@@ -101,7 +101,9 @@ typedef struct {
 /* One routed layer ("Red Lite dev16 — complete full-attention parity": top-10 routed
  * MoE plus shared expert).  Routed experts have ids 0..E-1; with has_shared the shared
  * expert has id E.  The banks must cover ids 0..E-1+has_shared without overlap.
- * hidden and inter are multiples of 256.  Host memory; read during the call only. */
+ * hidden and inter are each one of 256, 512, 1024 or 2048 (MOE_E_SHAPE otherwise; the
+ * one-launch decode calls narrow this further).  Host memory; read during the call
+ * only. */
 typedef struct {
   int32_t hidden;
   int32_t inter;
@@ -145,6 +147,7 @@ size_t moe_workspace_bytes(int32_t T, int32_t kprime, int32_t hidden, int32_t in
  * to about one).  Per token t:
  *   - with d_logits ([T][E] fp32, finite): the k largest logits, ties to the lower id,
  *     in descending order, weights softmax(logits) renormalised over the selected set;
+ *     logits are compared as IEEE values, so -0.0 and +0.0 tie;
  *   - with d_logits == NULL: d_ids[t][0..k-1] and d_w[t][0..k-1] are inputs (k distinct
  *     ids in [0, E) per token) and only the shared slot and the grouping are written;
  *   - with add_shared: slot k is (E, 1.0).  kprime = k + add_shared.
@@ -207,6 +210,7 @@ moe_status moe_expert_down_accumulate_q(const moe_layer *layer, const float *d_h
 /* Workspace of moe_layer_decode_q: MOE_DECODE_SYNC_BYTES of synchronisation words, then h
  * [kprime][inter] as 64-bit (fp32 bits, call tag) pairs. */
 #define MOE_DECODE_SYNC_BYTES 4352
+#define MOE_DECODE_ERROR_OFFSET 128
 size_t moe_decode_workspace_bytes(int32_t kprime, int32_t inter);
 
 /* One decode step of a layer for one token, in one launch ("Red Metal dev8", steps 3-6:
@@ -217,13 +221,17 @@ size_t moe_decode_workspace_bytes(int32_t kprime, int32_t inter);
  * moe_route_group; d_acc [hidden] (in/out).  d_logits [E] or NULL (explicit d_ids /
  * d_w inputs, as in moe_route_group); d_x [hidden].  kprime = k + add_shared;
  * add_shared must equal the layer's has_shared.
- * d_ws: moe_decode_workspace_bytes(kprime, inter) bytes; its first MOE_DECODE_SYNC_BYTES
- * must be zero before the first call, and each call leaves them ready for the next,
- * whatever the layer (calls that share a workspace must not overlap, and a workspace
- * serves one device).  The uint32 at byte 128 becomes nonzero if a wait of the kernel
- * for another workgroup's h values ever timed out, which can only happen when other
- * kernels hold compute units while this one runs; the results of that call are then
- * undefined, and the whole workspace must be zeroed again before the next call.
+ * d_ws: moe_decode_workspace_bytes(kprime, inter) bytes, ALL zero before the first call
+ * (not only the synchronisation words: the h pairs carry call tags that restart at 1
+ * when the words are zeroed, so old pairs would read as fresh).  Each call leaves the
+ * workspace ready for the next, whatever the layer (calls that share a workspace must
+ * not overlap, and a workspace serves one device).  To reset a workspace, zero all of it.
+ * Status word: the uint32 at byte 128 (MOE_DECODE_ERROR_OFFSET) becomes nonzero if a
+ * wait of the kernel for another workgroup's h values ever timed out, which can only
+ * happen when other kernels hold compute units while this one runs; the results of that
+ * call are then undefined and the whole workspace must be zeroed before the next call.
+ * The call cannot report this in its return value (it returns before the kernel runs):
+ * read the word after the stream has finished the call.
  * Limits: hidden == 2048, inter == 256 or 512, E <= 512. */
 moe_status moe_layer_decode_q(const moe_layer *layer, const float *d_logits, const float *d_x, int32_t k,
                               int32_t add_shared, int32_t *d_ids, float *d_w, int32_t *d_counts, int32_t *d_offsets,
@@ -231,22 +239,24 @@ moe_status moe_layer_decode_q(const moe_layer *layer, const float *d_logits, con
                               size_t ws_bytes, hipStream_t stream);
 
 /* ---- Decode of a residual chain of layers in one launch ("Red Lite dev16 -- complete
- * full-attention parity", sections "Implemented path" and "Build and field validation":
- * in the field model each block's routed MoE reads the post-attention RMSNorm of the
- * hidden state and its output is added back to it; 48 such blocks are stacked).  For
+ * full-attention parity", section "Pinned full-attention graph": in the field model each
+ * block's routed MoE reads the post-attention RMSNorm of the hidden state and its output
+ * is added back to it; section "Scope boundary": the 48-layer scheduler is the next
+ * gate).  For
  * one token, l = 0 .. n_layers-1:
  *     h_{l+1} = h_l + MoE_l(RMSNorm(h_l)),
  * with MoE_l routed by its own logits row.  The attention part of the blocks is not
  * part of this call.
  *
  * Workspace, moe_stack_workspace_bytes(n_layers, kprime, hidden, inter) bytes:
- *   [0, MOE_DECODE_SYNC_BYTES)   synchronisation words, zero before the first call;
+ *   [0, MOE_DECODE_SYNC_BYTES)   synchronisation words;
  *   [MOE_DECODE_SYNC_BYTES, +moe_stack_table_bytes(n_layers))   the layer table, copied
  *                                there by the caller from the host buffer that
  *                                moe_stack_table filled;
- *   the rest                     per-layer exchange buffers (any contents).
- * To set up: zero the workspace, then copy the table in.  A table stays valid while
- * the layers' device buffers do. */
+ *   the rest                     per-layer exchange buffers (tagged pairs).
+ * To set up: zero the WHOLE workspace (the exchange buffers too: their tags restart
+ * with the synchronisation words), then copy the table in.  To reset it later, do the
+ * same.  A table stays valid while the layers' device buffers do. */
 #define MOE_MAX_STACK_LAYERS 256
 size_t moe_stack_workspace_bytes(int32_t n_layers, int32_t kprime, int32_t hidden, int32_t inter);
 size_t moe_stack_table_bytes(int32_t n_layers);
@@ -270,8 +280,9 @@ moe_status moe_stack_table(const moe_layer *layers, int32_t n_layers, void *h_ta
  *   d_ids / d_w [n_layers][kprime]: each layer's selection as moe_route_group writes
  *     it, or both NULL.
  *   eps: RMSNorm epsilon (>= 0).
- * The synchronisation rules of moe_layer_decode_q apply to the workspace (the error
- * word at byte 128; after an error zero the workspace and copy the table in again).
+ * The synchronisation rules of moe_layer_decode_q apply to the workspace (the status
+ * word at MOE_DECODE_ERROR_OFFSET, read after the call has run; after an error, zero
+ * the whole workspace and copy the table in again).
  * Limits: 1 <= n_layers <= MOE_MAX_STACK_LAYERS. */
 moe_status moe_stack_decode_q(const moe_layer *layers, int32_t n_layers, const float *d_logits, const float *d_h_in,
                               float *d_h_out, int32_t k, int32_t add_shared, float eps, int32_t *d_ids, float *d_w,

@@ -251,6 +251,28 @@ def logits(T: int, E: int, seed: int = SEED_INPUT, tag: str = "logits", zipf_alp
     return np.ascontiguousarray(z)
 
 
+def tie_logits(kind: str, T: int, E: int, seed: int = SEED_INPUT, tag: str = "ties") -> np.ndarray:
+    """Router logits [T][E] full of ties, for the selection's tie rule:
+    few_values: N(0,1)/2 rounded to integers -- long runs of equal logits; rounding the
+      small negatives leaves -0.0 next to +0.0;
+    signed_zeros: every logit <= -0.5 except 12 per token, set to +0.0 or -0.0 at seeded
+      positions, so the selection is decided among zeros of both signs;
+    all_zero: every logit +0.0 or -0.0 (seeded signs)."""
+    z = normal(seed, tag, T * E).reshape(T, E)
+    neg = (u64(seed, tag + "/sign", T * E).reshape(T, E) & np.uint64(1)).astype(bool)
+    if kind == "few_values":
+        return np.round(z * 0.5).astype(np.float32)
+    if kind == "all_zero":
+        return np.where(neg, np.float32(-0.0), np.float32(0.0)).astype(np.float32)
+    if kind == "signed_zeros":
+        out = (-np.abs(z) - 0.5).astype(np.float32)
+        for t in range(T):
+            pos = np.argsort(u64(seed, f"{tag}/zpos/{t}", E), kind="stable")[:12]
+            out[t, pos] = np.where(neg[t, pos], np.float32(-0.0), np.float32(0.0))
+        return out
+    raise ValueError(kind)
+
+
 def router_weights(E: int, H: int, seed: int = SEED_BANK, tag: str = "router") -> np.ndarray:
     """fp32 router matrix [E][H] with entries N(0, 1/H): for activations ~N(0, 1) the
     logits are then about N(0, 1), the distribution the routed-layer workloads use."""

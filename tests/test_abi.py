@@ -45,6 +45,7 @@ def test_binding_constants_match_header():
     assert int(defs["MOE_SMALL_BATCH_TOKENS"]) == moe.SMALL_BATCH_TOKENS
     assert int(defs["MOE_MFMA_TILE_TOKENS"]) == moe.MFMA_TILE_TOKENS
     assert int(defs["MOE_DECODE_SYNC_BYTES"]) == moe.DECODE_SYNC_BYTES
+    assert int(defs["MOE_DECODE_ERROR_OFFSET"]) == moe.DECODE_ERROR_OFFSET
     assert int(defs["MOE_MAX_STACK_LAYERS"]) == moe.MAX_STACK_LAYERS
     assert int(defs["MOE_Q_IQ1S_LIKE"]) == moe.IQ1S_LIKE
     assert moe.decode_workspace_bytes(11, 512) - 11 * 512 * 8 == moe.DECODE_SYNC_BYTES
@@ -118,6 +119,9 @@ def test_expert_ffn_rejects():
     assert ffn(layer(), x=None) == -1
     assert ffn(layer(grids=None)) == -1
     assert ffn(layer(hidden=300)) == -2
+    for bad in (768, 1536, 4096, 128):              # widths other than 256, 512, 1024, 2048
+        assert ffn(layer(hidden=bad)) == -2
+        assert ffn(layer(inter=bad)) == -2
     assert ffn(layer(inter=4096)) == -2
     assert ffn(layer(n_banks=0)) == -2
     assert ffn(layer(n_experts=600)) == -2          # banks no longer cover E + shared

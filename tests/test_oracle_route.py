@@ -85,3 +85,25 @@ def test_group_is_stable_sort(T, E, k, shared):
     np.testing.assert_array_equal(ss, np.argsort(flat, kind="stable"))
     np.testing.assert_array_equal(sp[ss], np.arange(len(flat)))
     assert offsets[-1] == T * (k + int(shared))
+
+
+@pytest.mark.parametrize("kind", ["few_values", "signed_zeros", "all_zero"])
+@pytest.mark.parametrize("E,k", [(512, 10), (1023, 16), (16, 4)])
+def test_route_signed_zero_and_heavy_ties(kind, E, k):
+    """-0.0 and +0.0 compare equal, so they tie and the lower id goes first; long runs of
+    equal logits select the lowest ids of the run.  Checked against the brute-force sort
+    (numpy orders -0.0 and +0.0 as equal), and the weights of tied experts are equal."""
+    T = 24
+    lg = synth.tie_logits(kind, T, E, tag=f"edge/{kind}/{E}")
+    assert np.signbit(lg).any() and (lg == 0).any()
+    ids, w = O.route(lg, k, add_shared=False)
+    for t in range(T):
+        np.testing.assert_array_equal(ids[t], brute_topk(lg[t], k))
+        sel = lg[t, ids[t]]
+        for a in range(k):
+            for b in range(k):
+                if sel[a] == sel[b]:
+                    assert w[t, a] == w[t, b]
+    if kind == "all_zero":
+        np.testing.assert_array_equal(ids, np.tile(np.arange(k), (T, 1)))
+        assert np.all(w == np.float32(1.0) / np.float32(k))
