@@ -147,9 +147,11 @@ moe_status check_ffn_common(const moe_layer *layer, LayerArgs *L, int32_t T, int
 }
 
 // Both kernels of a projection: the mat-vec kernel takes the experts of the first work
-// list, the matrix-core kernel those of the second.
+// list, the matrix-core kernel those of the second.  Gate / up of 2 .. kDecMaxTokens
+// tokens runs on one decode kernel instead (k_dec.hip).
 hipError_t launch_gateup(const LayerArgs &L, const float *x, int T, int kprime, const int32_t *sorted_slot,
                          const WorkRec *work, int n_ids, float *h, hipStream_t s) {
+  if (dec_path_ok(L, T)) return launch_gateup_dec(L, x, T, kprime, sorted_slot, work, n_ids, h, s);
   hipError_t err = launch_gateup_gemv(L, x, T, kprime, sorted_slot, work, n_ids, matvec_max_tokens(T), h, s);
   if (err != hipSuccess) return err;
   return launch_gateup_mfma(L, x, T, kprime, sorted_slot, work, n_ids, h, s);

@@ -202,6 +202,12 @@ hipError_t launch_stack_decode(const LayerArgs *d_tab, int n_layers, int formats
 hipError_t launch_layer_decode(const LayerArgs &L, const float *logits, const float *x, int E, int k, int add_shared,
                                int32_t *ids, float *w, int32_t *counts, int32_t *offsets, int32_t *sorted_slot,
                                int32_t *slot_pos, WorkRec *work, float *acc, void *ws, hipStream_t s);
+// Calls of 2 .. kDecMaxTokens tokens with inter <= 512 run gate / up on the matrix-core
+// decode kernel (k_dec.hip).
+constexpr int kDecMaxTokens = 8;
+bool dec_path_ok(const LayerArgs &L, int T);
+hipError_t launch_gateup_dec(const LayerArgs &L, const float *x, int T, int kprime, const int32_t *sorted_slot,
+                             const WorkRec *work, int n_ids, float *h, hipStream_t s);
 hipError_t launch_accumulate(const float *y, const float *w, const int32_t *ids, const int32_t *slot_pos, int T,
                              int kprime, int H, float *acc, hipStream_t s);
 hipError_t launch_rmsnorm(const float *h, int T, int H, float eps, float *x, hipStream_t s);

@@ -63,12 +63,15 @@ extern "C" {
 #define MOE_MAX_K 16        /* routed experts per token */
 #define MOE_MAX_IDS 1024    /* E + has_shared */
 /* Which experts run where.  In a call of T tokens, experts with at most m(T) tokens
- * run on the mat-vec kernels (each weight decoded once per token, the work spread over
- * the expert's rows); experts with more run on the matrix-core grouped GEMM in tiles of
- * up to MOE_MFMA_TILE_TOKENS tokens (each weight decoded once per tile).  m(T) = T for
- * small batches, T <= MOE_SMALL_BATCH_TOKENS (every expert on the mat-vec kernels: too
- * few tiles would leave most of the GPU idle), else MOE_MATVEC_MAX_TOKENS.  The work
- * list written by moe_route_group keeps the two sets apart. */
+ * form the work list's first set and run on the mat-vec kernels (each weight decoded
+ * once per token, the work spread over the expert's rows); experts with more run on the
+ * matrix-core grouped GEMM in tiles of up to MOE_MFMA_TILE_TOKENS tokens (each weight
+ * decoded once per tile).  m(T) = T for small batches, T <= MOE_SMALL_BATCH_TOKENS
+ * (every expert in the first set: too few tiles would leave most of the GPU idle), else
+ * MOE_MATVEC_MAX_TOKENS.  For 2 to 8 tokens and inter <= 512, gate / up of the first set
+ * runs instead on a matrix-core decode kernel that decodes each weight once per call
+ * into fragments the expert's tokens share.  The work list written by moe_route_group
+ * keeps the two sets apart. */
 #define MOE_MATVEC_MAX_TOKENS 1
 #define MOE_SMALL_BATCH_TOKENS 16
 #define MOE_MFMA_TILE_TOKENS 16

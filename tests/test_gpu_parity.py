@@ -216,6 +216,14 @@ LAYER_CASES = {
     # one format at inter 256: the one-launch kernel's single-format instances, 4 lanes per row
     "decode_iq1_i256": ([(IQ1, 16)], 2048, 256, 16, 1, 1, 4, 0.0),
     "decode_iq2_i256": ([(IQ2, 16)], 2048, 256, 16, 0, 1, 5, 0.0),
+    # 2 to 8 tokens: gate / up on the matrix-core decode kernel (one part of one or two
+    # super-blocks per wave at hidden 256 / 512, two parts at 1024)
+    "decode2_iq2_top10_shared": ([(IQ2, 512)], 2048, 512, 512, 1, 2, 10, 0.0),
+    "dec_h256_i256_mixed_t7": ([(IQ2, 12), (IQ1, 12)], 256, 256, 24, 1, 7, 3, 0.0),
+    "dec_h512_iq2_t3": ([(IQ2, 16)], 512, 512, 16, 0, 3, 4, 0.0),
+    "dec_h1024_iq1_t4_zipf": ([(IQ1, 16)], 1024, 512, 16, 0, 4, 4, 1.0),
+    # every expert takes all 8 tokens: the 16-row A operand full
+    "dec_every_expert_all_tokens": ([(IQ2, 4)], 2048, 512, 4, 1, 8, 4, 0.0),
 }
 
 
