@@ -30,6 +30,7 @@ def matvec_max_tokens(T: int) -> int:
     return T if T <= SMALL_BATCH_TOKENS else MATVEC_MAX_TOKENS
 MFMA_TILE_TOKENS = 16  # tokens per matrix-core tile (MOE_MFMA_TILE_TOKENS)
 DECODE_SYNC_BYTES = 4352  # synchronisation words at the start of a decode workspace (MOE_DECODE_SYNC_BYTES)
+DECODE_STATIC_BYTES = 73984  # the static per-device workspace of layer_decode_q_static
 DECODE_ERROR_OFFSET = 128  # byte offset of the uint32 status word in it (MOE_DECODE_ERROR_OFFSET)
 MAX_STACK_LAYERS = 256  # MOE_MAX_STACK_LAYERS
 
@@ -38,7 +39,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_E_NULL", -2: "MOE_E_SHAPE", -3: "MOE_E_QTYPE", -
 
 EXPORTS = ["moe_abi_version", "moe_status_string", "moe_last_hip_error", "moe_last_hip_error_string", "moe_grids_bytes", "moe_grids_expand", "moe_work_ints", "moe_workspace_bytes",
            "moe_route_group", "moe_expert_ffn_q", "moe_expert_gateup_q", "moe_expert_down_q",
-           "moe_expert_down_accumulate_q", "moe_decode_workspace_bytes", "moe_layer_decode_q", "moe_accumulate",
+           "moe_expert_down_accumulate_q", "moe_decode_workspace_bytes", "moe_layer_decode_q", "moe_layer_decode_q_static", "moe_accumulate",
            "moe_dequant_f32", "moe_rmsnorm", "moe_stack_workspace_bytes", "moe_stack_table_bytes", "moe_stack_table",
            "moe_stack_decode_q", "moe_router_logits", "moe_shared_weight", "moe_repack_iq1s"]
 
@@ -85,6 +86,7 @@ def _load():
         "moe_expert_down_accumulate_q": (C.c_int, [P, P, i32, i32, P, P, P, P, P]),
         "moe_decode_workspace_bytes": (sz, [i32, i32]),
         "moe_layer_decode_q": (C.c_int, [P, P, P, i32, i32, P, P, P, P, P, P, P, P, P, sz, P]),
+        "moe_layer_decode_q_static": (C.c_int, [P, P, P, i32, i32, P, P, P, P, P, P, P, P, P, P]),
         "moe_accumulate": (C.c_int, [P, P, P, P, i32, i32, i32, P, P]),
         "moe_dequant_f32": (C.c_int, [i32, i32, i32, P, P, P, P, P, P]),
         "moe_rmsnorm": (C.c_int, [P, i32, i32, C.c_float, P, P]),
@@ -187,6 +189,17 @@ def layer_decode_q(layer: Layer, logits, x, k, add_shared, ids, w, counts, offse
            lib.moe_layer_decode_q(C.byref(layer), _ptr(logits), _ptr(x), k, add_shared, _ptr(ids), _ptr(w),
                                   _ptr(counts), _ptr(offsets), _ptr(sorted_slot), _ptr(slot_pos), _ptr(work),
                                   _ptr(acc), _ptr(ws), nbytes, _stream(stream)))
+
+
+def layer_decode_q_static(layer: Layer, logits, x, k, add_shared, ids, w, counts, offsets, sorted_slot, slot_pos, work,
+                          acc, status, stream=None):
+    """layer_decode_q with the library's static per-device workspace: the call allocates
+    no device memory.  status: one 32-bit word (device) that receives the call's status
+    word (nonzero: a wait timed out and the results are undefined)."""
+    _check("moe_layer_decode_q_static",
+           lib.moe_layer_decode_q_static(C.byref(layer), _ptr(logits), _ptr(x), k, add_shared, _ptr(ids), _ptr(w),
+                                         _ptr(counts), _ptr(offsets), _ptr(sorted_slot), _ptr(slot_pos), _ptr(work),
+                                         _ptr(acc), _ptr(status), _stream(stream)))
 
 
 def decode_error(ws) -> int:

@@ -2,6 +2,7 @@
 // caller's stream.  No allocation, no host<->device copies, no synchronization.
 #include <cstring>
 #include <initializer_list>
+#include <mutex>
 
 #include "common.hpp"
 #include "repack.hpp"
@@ -233,6 +234,79 @@ moe_status moe_layer_decode_q(const moe_layer *layer, const float *d_logits, con
   clear_pending();
   return from_hip(launch_layer_decode(L, d_logits, d_x, E, k, add_shared, d_ids, d_w, d_counts, d_offsets,
                                       d_sorted_slot, d_slot_pos, (WorkRec *)d_work, d_acc, d_ws, stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+// The workspace of moe_layer_decode_q_static: one array per device (each device's copy
+// of the code object holds its own), held until the process ends.  Host code never
+// passes the array's name to a kernel: it stands for a host-side shadow, not a device
+// address; the device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) uint8_t scratch[MOE_DECODE_STATIC_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t *g_scratch_ptr[kMaxScratchDevices];  // per device: the array's address, null until the first call
+
+// With status: its word gets the decode's status word first.  Then the whole array is
+// zeroed (16-byte stores; MOE_DECODE_STATIC_BYTES is a multiple of 16).
+__global__ void __launch_bounds__(1024) k_scratch_reset(uint8_t *ws, uint32_t *status) {
+  if (status && threadIdx.x == 0) *status = *(const volatile uint32_t *)(ws + MOE_DECODE_ERROR_OFFSET);
+  __syncthreads();
+  uint4 *p = (uint4 *)ws;
+  for (int i = threadIdx.x; i < MOE_DECODE_STATIC_BYTES / 16; i += blockDim.x) p[i] = make_uint4(0, 0, 0, 0);
+}
+
+// The current device's array (device address), zeroed on the stream on first use.
+moe_status scratch_for_current_device(hipStream_t stream, uint8_t **out) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return from_hip(err);
+  if (dev < 0 || dev >= kMaxScratchDevices) return from_hip(hipErrorInvalidDevice);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return from_hip(err);
+    if (!p || ((uintptr_t)p & 255)) return from_hip(hipErrorInvalidSymbol);
+    hipLaunchKernelGGL(k_scratch_reset, dim3(1), dim3(1024), 0, stream, (uint8_t *)p, (uint32_t *)nullptr);
+    err = hipGetLastError();
+    if (err != hipSuccess) return from_hip(err);
+    g_scratch_ptr[dev] = (uint8_t *)p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_layer_decode_q_static(const moe_layer *layer, const float *d_logits, const float *d_x, int32_t k,
+                                     int32_t add_shared, int32_t *d_ids, float *d_w, int32_t *d_counts,
+                                     int32_t *d_offsets, int32_t *d_sorted_slot, int32_t *d_slot_pos, int32_t *d_work,
+                                     float *d_acc, uint32_t *d_status, hipStream_t stream) {
+  LayerArgs L;
+  moe_status st = check_ffn_common(layer, &L, 1, k + add_shared,
+                                   {d_x, d_ids, d_w, d_counts, d_offsets, d_sorted_slot, d_slot_pos, d_work, d_acc});
+  if (st != MOE_OK) return st;
+  if (!d_status) return MOE_E_NULL;
+  if (!aligned16(d_status) || (d_logits && !aligned16(d_logits))) return MOE_E_ALIGN;
+  const int E = layer->n_experts;
+  if (k < 1 || k > MOE_MAX_K || k > E || add_shared != layer->has_shared || E > 512) return MOE_E_SHAPE;
+  if (L.hidden != 2048 || (L.inter != 256 && L.inter != 512)) return MOE_E_SHAPE;
+  if (moe_decode_workspace_bytes(k + add_shared, L.inter) > MOE_DECODE_STATIC_BYTES) return MOE_E_WORKSPACE;
+  clear_pending();
+  uint8_t *ws = nullptr;
+  st = scratch_for_current_device(stream, &ws);
+  if (st != MOE_OK) return st;
+  hipError_t err = launch_layer_decode(L, d_logits, d_x, E, k, add_shared, d_ids, d_w, d_counts, d_offsets,
+                                       d_sorted_slot, d_slot_pos, (WorkRec *)d_work, d_acc, ws, stream);
+  if (err != hipSuccess) return from_hip(err);
+  hipLaunchKernelGGL(k_scratch_reset, dim3(1), dim3(1024), 0, stream, ws, d_status);
+  return from_hip(hipGetLastError());
 }
 
 size_t moe_stack_table_bytes(int32_t n_layers) {

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 8
+#define MOE_ABI_VERSION 9
 #define MOE_MAX_BANKS 4
 #define MOE_MAX_K 16        /* routed experts per token */
 #define MOE_MAX_IDS 1024    /* E + has_shared */
@@ -240,6 +240,26 @@ moe_status moe_layer_decode_q(const moe_layer *layer, const float *d_logits, con
                               int32_t add_shared, int32_t *d_ids, float *d_w, int32_t *d_counts, int32_t *d_offsets,
                               int32_t *d_sorted_slot, int32_t *d_slot_pos, int32_t *d_work, float *d_acc, void *d_ws,
                               size_t ws_bytes, hipStream_t stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, serving
+ * loops that allow no hipMalloc): moe_layer_decode_q with its workspace in the library's
+ * own static device array of MOE_DECODE_STATIC_BYTES per device, which each device holds
+ * until the process ends.  The call allocates nothing; it computes and writes exactly
+ * what moe_layer_decode_q does, with the same arguments and limits, except:
+ *   d_status: one uint32 (device, output), set after the decode to its status word:
+ *     nonzero if a wait for another workgroup's values timed out (the call's results
+ *     are then undefined).
+ * The first call on a device looks the array up and zeroes it on the stream; every call
+ * zeroes it again after its decode, so each call starts from a zeroed workspace.  Every
+ * call on a device shares that device's array: calls that overlap on one device (other
+ * streams, other host threads) race and give undefined results.  A call whose kprime
+ * and inter would need more than MOE_DECODE_STATIC_BYTES returns MOE_E_WORKSPACE (the
+ * limits of moe_layer_decode_q keep every valid call within it). */
+#define MOE_DECODE_STATIC_BYTES 73984 /* MOE_DECODE_SYNC_BYTES + (MOE_MAX_K + 1) * 512 * 8 */
+moe_status moe_layer_decode_q_static(const moe_layer *layer, const float *d_logits, const float *d_x, int32_t k,
+                                     int32_t add_shared, int32_t *d_ids, float *d_w, int32_t *d_counts,
+                                     int32_t *d_offsets, int32_t *d_sorted_slot, int32_t *d_slot_pos, int32_t *d_work,
+                                     float *d_acc, uint32_t *d_status, hipStream_t stream);
 
 /* ---- Decode of a residual chain of layers in one launch ("Red Lite dev16 -- complete
  * full-attention parity", section "Pinned full-attention graph": in the field model each

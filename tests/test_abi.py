@@ -46,13 +46,17 @@ def test_binding_constants_match_header():
     assert int(defs["MOE_MFMA_TILE_TOKENS"]) == moe.MFMA_TILE_TOKENS
     assert int(defs["MOE_DECODE_SYNC_BYTES"]) == moe.DECODE_SYNC_BYTES
     assert int(defs["MOE_DECODE_ERROR_OFFSET"]) == moe.DECODE_ERROR_OFFSET
+    assert int(defs["MOE_DECODE_STATIC_BYTES"]) == moe.DECODE_STATIC_BYTES
+    # the static workspace holds the largest valid call: 16 routed + 1 shared slots at inter 512
+    assert moe.decode_workspace_bytes(17, 512) == moe.DECODE_STATIC_BYTES
+    assert moe.DECODE_STATIC_BYTES % 16 == 0
     assert int(defs["MOE_MAX_STACK_LAYERS"]) == moe.MAX_STACK_LAYERS
     assert int(defs["MOE_Q_IQ1S_LIKE"]) == moe.IQ1S_LIKE
     assert moe.decode_workspace_bytes(11, 512) - 11 * 512 * 8 == moe.DECODE_SYNC_BYTES
 
 
 def test_version_strings_sizes():
-    assert moe.abi_version() == 8
+    assert moe.abi_version() == 9
     for st in moe.STATUS:
         assert lib.moe_status_string(st)
     assert moe.grids_bytes() >= 512 * 8 + 2048 * 8
@@ -180,6 +184,26 @@ def test_layer_decode_rejects():
     assert call(d=layer(hidden=1024, n_experts=512)) == -2
     assert call(d=layer(inter=1024)) == -2
     assert call(ws_bytes=ws_need - 4) == -5
+
+
+def test_layer_decode_static_rejects():
+    """The no-allocation variant validates its arguments before any HIP call."""
+    d = layer()
+
+    def call(d=d, logits=A, x=A, k=10, add_shared=1, acc=A, status=A):
+        return lib.moe_layer_decode_q_static(C.byref(d), logits, x, k, add_shared, A, A, A, A, A, A, A, acc, status,
+                                             None)
+    assert lib.moe_layer_decode_q_static(None, A, A, 10, 1, A, A, A, A, A, A, A, A, A, None) == -1
+    assert call(x=None) == -1
+    assert call(status=None) == -1
+    assert call(status=MIS) == -4
+    assert call(logits=MIS) == -4
+    assert call(acc=MIS) == -4
+    assert call(k=0) == -2
+    assert call(k=17) == -2
+    assert call(add_shared=0) == -2
+    assert call(d=layer(hidden=1024, n_experts=512)) == -2
+    assert call(d=layer(inter=1024)) == -2
 
 
 def test_stack_table_and_rejects():
