@@ -78,7 +78,9 @@ k_gateup_dec(LayerArgs L, const float *__restrict__ x, int T, int kprime, const 
   const int H = L.hidden, I = L.inter, tid = threadIdx.x;
   constexpr int SB = NSB;                  // super-blocks per wave
   const int KP = (H >> 8) / SB, UPR = kDecWaves / KP, rbs = I / 8;
-  const int wave = tid >> 6, lane = tid & 63, q = lane >> 4, n = lane & 15;
+  // wave-uniform in scalar registers: the first unit's record then comes through the
+  // scalar cache and its bank through scalar loads of the kernel arguments
+  const int wave = uniform(tid >> 6), lane = tid & 63, q = lane >> 4, n = lane & 15;
   const int us = wave / KP, kp = wave - us * KP, stride = gridDim.x * UPR;
   const int nslots = T * kprime, nrec = min(nslots, n_ids) + 1;
   // the small inputs first, one load per thread (clamped: no load behind a branch)

@@ -180,8 +180,9 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
   // ---- 1. routing, in every workgroup, by wave 0; the other waves expand the grid
   // tables into LDS meanwhile
   if (wave == 0) {
+    int sel = 0x7FFFFFFF;
     if (logits) {
-      topk_select<8, 1, 16>(tv, E, k, add_shared, blockIdx.x == 0 ? ids : nullptr, w, S.ids, S.w, S.topk);
+      sel = topk_select<8, 1, 16>(tv, E, k, add_shared, blockIdx.x == 0 ? ids : nullptr, w, S.ids, S.w, S.topk);
     } else {
       if (lane < k) {
         S.ids[lane] = ids[lane];
@@ -197,7 +198,8 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
       }
     }
     __builtin_amdgcn_wave_barrier();
-    const int my = lane < kprime ? S.ids[lane] : 0x7FFFFFFF;
+    // routed: the ids are still in the lanes; explicit: as copied to LDS above
+    const int my = logits ? sel : (lane < kprime ? S.ids[lane] : 0x7FFFFFFF);
     const int rank = slot_rank(my, lane);
     if (lane < kprime) {
       S.pos_of[lane] = rank;
@@ -234,13 +236,15 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
     else
       wide_issue_mats(It, bank_mat(B, e, kGate), bank_mat(B, e, kUp), uniform(B.qt), H, item - p * ipe, q);
   };
+  // the first item's loads leave before the activations are read from LDS (its
+  // addresses need only the routing records)
+  if (item0 < n_items) issue(item0);
   X32 X;
 #pragma unroll
   for (int i = 0; i < 8; i++) {
     const float4 f = *(const float4 *)&S.xs[lane * kXsRow + 4 * i];
     X.v[4 * i] = f.x, X.v[4 * i + 1] = f.y, X.v[4 * i + 2] = f.z, X.v[4 * i + 3] = f.w;
   }
-  if (item0 < n_items) issue(item0);
   for (int item = item0; item < n_items; item += nw) {
     if (item != item0) issue(item);
     if (fmt_iq2<FMT>(It.qt))
@@ -379,9 +383,7 @@ __device__ inline void route_wave(const float *logits, const LayerArgs &L, int E
                                   int32_t *ids_out, float *w_out, RouteLds &R, TopkLds &T) {
   const int lane = threadIdx.x & 63, kprime = k + add_shared;
   const TopkVals<8> tv = topk_load<8>(logits, E);
-  topk_select<8, 2, 16>(tv, E, k, add_shared, ids_out, w_out, R.ids, R.w, T);
-  __builtin_amdgcn_wave_barrier();
-  const int my = lane < kprime ? R.ids[lane] : 0x7FFFFFFF;
+  const int my = topk_select<8, 2, 16>(tv, E, k, add_shared, ids_out, w_out, R.ids, R.w, T);
   const int rank = slot_rank(my, lane);
   if (lane < kprime) {
     R.pos_of[lane] = rank;

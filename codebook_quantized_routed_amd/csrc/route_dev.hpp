@@ -50,7 +50,8 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
 // others by (key descending, id ascending) from broadcast LDS reads; rank < k is selected.
 // If more than 64 keys reach tau (heavy ties), the selection falls back to k rounds of
 // a wave-wide arg-max.  Both give the same result.
-// Outputs: ids / w (global, skipped when ids is null) and the optional copies.
+// Outputs: ids / w (global, skipped when ids is null) and the optional copies; returns
+// the lane's slot id.
 constexpr int kCand = 64;
 
 struct TopkLds {
@@ -118,7 +119,7 @@ __device__ __forceinline__ TopkVals<VPL> topk_load(const float *__restrict__ l, 
 // below this one are not searched (stay zero); every caller takes 16, measured the
 // faster (or as fast) in each kernel.  The selection is the same.
 template <int VPL, int TAU_BITS = 1, int TAU_LOW = 0>
-__device__ __forceinline__ void topk_select(const TopkVals<VPL> &tv, int E, int k, int add_shared,
+__device__ __forceinline__ int topk_select(const TopkVals<VPL> &tv, int E, int k, int add_shared,
                                             int32_t *__restrict__ ids, float *__restrict__ w, int32_t *ids_copy,
                                             float *w_copy, TopkLds &S) {
   int lane = threadIdx.x & 63;
@@ -161,13 +162,21 @@ __device__ __forceinline__ void topk_select(const TopkVals<VPL> &tv, int E, int 
       if (key[i] >= tau) S.cand[pos[i]] = ((uint64_t)key[i] << 32) | (uint32_t)~(uint32_t)(i * 64 + lane);
     __builtin_amdgcn_wave_barrier();
     // each lane ranks its candidate against all of them, two per 16-byte read (every
-    // lane reads the same address: one broadcast read)
+    // lane reads the same address: one broadcast read), four reads issued back to back
+    // per trip (j0 <= 56, so j0 + 7 stays within the 64 entries; entries at or past
+    // total are not counted)
     const uint64_t mine = lane < total ? S.cand[lane] : 0u;
     int rank = 0;
-    for (int j = 0; j < total; j += 2) {
-      const uint4 pr = *(const uint4 *)&S.cand[j];
-      rank += (((uint64_t)pr.y << 32) | pr.x) > mine ? 1 : 0;
-      rank += (j + 1 < total && (((uint64_t)pr.w << 32) | pr.z) > mine) ? 1 : 0;
+    for (int j0 = 0; j0 < total; j0 += 8) {
+      uint4 pr[4];
+#pragma unroll
+      for (int u = 0; u < 4; u++) pr[u] = *(const uint4 *)&S.cand[j0 + 2 * u];
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        const int j = j0 + 2 * u;
+        rank += (j < total && (((uint64_t)pr[u].y << 32) | pr[u].x) > mine) ? 1 : 0;
+        rank += (j + 1 < total && (((uint64_t)pr[u].w << 32) | pr[u].z) > mine) ? 1 : 0;
+      }
     }
     if (lane < total && rank < k) {
       S.sel_key[rank] = (uint32_t)(mine >> 32);
@@ -207,6 +216,9 @@ __device__ __forceinline__ void topk_select(const TopkVals<VPL> &tv, int E, int 
     if (ids_copy) ids_copy[k] = E;
     if (w_copy) w_copy[k] = 1.0f;
   }
+  // the lane's slot id (lane j < k: selection j; lane k: the shared expert), else
+  // 0x7FFFFFFF
+  return lane < k ? myid : (add_shared && lane == k ? E : 0x7FFFFFFF);
 }
 
 template <int VPL>
