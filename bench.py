@@ -106,6 +106,38 @@ def step_distribution(step, first, n):
     return [ev[j].elapsed_time(ev[j + 1]) for j in range(n)]
 
 
+def stream_probe(gb, dev, reps=20):
+    """Plain streaming kernels over gb GB of fp32, timed with events over reps passes after
+    a warm one: a read-only pass (a sum reduction) and a device-to-device copy (read and
+    write).  Their rates are what simple streaming code reaches on this GPU, the
+    practical ceiling under the 8 TB/s peak."""
+    import torch
+    n = int(gb * 1e9) // 4
+    x = torch.ones(n, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize(dev)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize(dev)
+        return e0.elapsed_time(e1) / reps
+
+    ms_sum = timed(lambda: x.sum())
+    ms_copy = timed(lambda: y.copy_(x))
+    assert float(y[-1].item()) == 1.0
+    out = {"bytes": n * 4, "passes": reps, "peak_gbs": HBM_PEAK_GBS}
+    for name, ms, moved in (("sum", ms_sum, n * 4), ("copy", ms_copy, 2 * n * 4)):
+        gbs = moved / (ms * 1e-3) / 1e9
+        out[name] = {"ms_per_pass": round(ms, 4), "bytes_moved": moved, "achieved_gbs": round(gbs, 1),
+                     "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    return out
+
+
 def cpu_info():
     model = "unknown"
     try:
@@ -179,6 +211,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run three device-to-device copies of this size first (counter calibration)")
+    ap.add_argument("--stream-probe-gb", type=float, default=0.0,
+                    help="only time one read-only pass over this many GB (the reachable HBM read rate) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the layer is data-parallel and needs no exchange between GPUs, "
@@ -193,6 +227,9 @@ def main():
     banks, T, k, shared, zipf, path, desc = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.stream_probe_gb > 0:
+        print(json.dumps(stream_probe(args.stream_probe_gb, dev)))
+        return
     if args.calib_copy_mb:
         src = torch.ones(args.calib_copy_mb << 18, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)

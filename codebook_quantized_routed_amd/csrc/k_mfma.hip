@@ -43,7 +43,10 @@ __host__ __device__ inline size_t mfma_lds_bytes(int formats) {
 // The lane's codes of one tile row for one super-block.  IQ2: c = 8 codes (u16), s = the
 // scale word, d = the binary16 d.  IQ1: c.xy = 8 index bytes, c.z = 8 nibbles, (s:c.w)
 // = the sd word (d in its low half).  Offsets are 32-bit from the matrix bases, so the
-// loads take a scalar base and a vector offset.
+// loads take a scalar base and a vector offset.  A super-block reads a quarter (IQ1) or
+// a half (IQ2) of each 128-byte line of a row's index stream and the next super-blocks
+// read the rest, so these are ordinary loads: as non-temporal loads the line left L2
+// sooner and was fetched again for more of its parts.
 struct TileCodes {
   uint4 c;
   uint32_t s, d;
@@ -54,12 +57,12 @@ __device__ __forceinline__ TileCodes load_tile_codes(const QMat &m, int cols, in
   const uint32_t ng = cols >> 3, nb = cols >> 8, g0 = sb * 32 + 8 * qd, blk = row * nb + sb;
   TileCodes t;
   if constexpr (QT == MOE_Q_IQ2XS_LIKE) {
-    t.c = load_stream16(m.s0 + (uint32_t)((row * ng + g0) * 2));
+    t.c = *(const uint4 *)(m.s0 + (uint32_t)((row * ng + g0) * 2));
     t.s = *(const uint32_t *)(m.s1 + (uint32_t)(blk * 4));
     t.d = *(const uint16_t *)(m.s2 + (uint32_t)(blk * 2));
   } else {
-    const uint2 ql = load_stream8(m.s0 + (uint32_t)(row * ng + g0));
-    const uint32_t qh = __builtin_nontemporal_load((const uint32_t *)(m.s1 + (uint32_t)(row * (ng / 2) + g0 / 2)));
+    const uint2 ql = *(const uint2 *)(m.s0 + (uint32_t)(row * ng + g0));
+    const uint32_t qh = *(const uint32_t *)(m.s1 + (uint32_t)(row * (ng / 2) + g0 / 2));
     const uint2 sd = *(const uint2 *)(m.s2 + (uint32_t)(blk * 8));
     t.c = make_uint4(ql.x, ql.y, qh, sd.x);
     t.s = sd.y;

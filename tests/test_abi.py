@@ -280,3 +280,60 @@ def test_repack_rejects():
     assert call(cols=300) == -2
     assert call(cols=0) == -2
     assert call(rows=1 << 30, cols=2048) == -2        # 2^33 super-blocks
+
+
+# The HIP runtime functions the library may call: kernel registration and launch, error
+# queries, the device id and attributes, and the static workspace's symbol lookup.
+# Nothing that copies, synchronises with the host, allocates, frees or sets memory.
+ALLOWED_HIP_IMPORTS = {
+    "__hipPopCallConfiguration", "__hipPushCallConfiguration", "__hipRegisterFatBinary",
+    "__hipRegisterFunction", "__hipRegisterVar", "__hipUnregisterFatBinary",
+    "hipLaunchKernel", "hipGetLastError", "hipGetErrorString", "hipGetDevice",
+    "hipDeviceGetAttribute", "hipGetSymbolAddress",
+}
+
+
+def test_library_imports_no_copy_sync_or_alloc():
+    """Every entry point only enqueues kernels: the library's dynamic imports hold no
+    memcpy, memset, synchronisation, allocation or host-registration function, so no
+    call can copy to or from the host, wait for the device or allocate (the analogue
+    of the pages' zero-bytes-read check during the routed layer)."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm (binutils) not installed")
+    out = subprocess.run([nm, "-D", "--undefined-only", moe.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    hip = {line.split()[-1].split("@")[0] for line in out.splitlines() if "hip" in line.lower()}
+    assert "hipLaunchKernel" in hip
+    assert hip <= ALLOWED_HIP_IMPORTS, sorted(hip - ALLOWED_HIP_IMPORTS)
+    for bad in ("Memcpy", "Memset", "Malloc", "Free", "Synchronize", "HostRegister", "HostAlloc"):
+        assert not any(bad.lower() in s.lower() for s in hip), bad
+
+
+def test_forced_hip_error_reports_moe_e_hip():
+    """A launch the runtime refuses returns MOE_E_HIP, and the thread's last HIP error
+    and its text are readable.  Forced from the host: a child process in which no GPU
+    is visible, so the launch fails before any kernel could touch the (fake) pointers.
+    Skipped where this process sees a GPU."""
+    import subprocess
+    import sys
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible; the forced error runs on CPU-only machines")
+    code = (
+        "import ctypes as C\n"
+        "import codebook_quantized_routed_amd as moe\n"
+        "A = C.c_void_p(1 << 20)\n"
+        "st = moe.lib.moe_accumulate(A, A, A, A, 1, 11, 2048, A, None)\n"
+        "print(st, moe.lib.moe_last_hip_error(), moe.lib.moe_last_hip_error_string().decode())\n"
+    )
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1", CUDA_VISIBLE_DEVICES="-1",
+               PYTHONPATH=ROOT + os.pathsep + os.environ.get("PYTHONPATH", ""))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    st, err, msg = r.stdout.strip().splitlines()[-1].split(" ", 2)
+    assert int(st) == -6                                   # MOE_E_HIP
+    assert int(err) != 0 and msg                           # the hipError_t and its text
+    assert lib.moe_status_string(-6)

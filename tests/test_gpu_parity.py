@@ -94,8 +94,10 @@ ROUTE_CASES = [  # T, E, k, shared, zipf
     (1, 512, 10, True, 0.0), (8, 512, 10, True, 0.0), (256, 512, 10, False, 0.0), (256, 512, 10, False, 1.1),
     (1024, 512, 10, True, 0.0), (1, 16, 4, False, 0.0), (33, 16, 16, True, 0.0), (5, 1023, 16, True, 0.0),
     (3, 64, 1, False, 0.0), (2000, 100, 7, True, 0.0),
-    # 65 .. 128 slots in one workgroup (two slots per lane): duplicates, wide experts
+    # 65 .. 272 slots in one workgroup (the counting sort): duplicates, every expert in the
+    # first set up to 16 tokens, wide experts at T = 20
     (20, 16, 5, True, 0.0), (12, 64, 9, True, 0.0), (11, 512, 10, True, 1.1), (13, 40, 4, True, 0.0),
+    (16, 512, 16, True, 0.0), (16, 64, 16, True, 0.0), (9, 16, 8, False, 0.0), (16, 512, 15, True, 1.1),
 ]
 
 
