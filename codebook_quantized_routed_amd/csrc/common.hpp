@@ -24,7 +24,13 @@ constexpr size_t kGridIq2Off = 0;
 constexpr size_t kGridIq1Off = kIq2Rows * 8;
 constexpr size_t kGridIq2CompactOff = kGridIq1Off + kIq1Rows * 8;
 constexpr size_t kGridIq1CompactOff = kGridIq2CompactOff + kIq2Rows * 2;
-constexpr size_t kGridBytes = kGridIq1CompactOff + kIq1Rows * 2;
+// then the matrix-core decode tables, expanded once by moe_grids_expand in the layout the
+// decode kernels keep in LDS for a layer of both formats: IQ2 fp16 grid rows [512][8],
+// IQ2 signed-scale rows [128 sign patterns][16 scales][8], IQ1 rows with the delta
+// added [2][2048][8] (+1/8, then -1/8)
+constexpr size_t kGridDecOff = (kGridIq1CompactOff + kIq1Rows * 2 + 255) & ~(size_t)255;
+constexpr size_t kGridDecBytes = kIq2Rows * 16 + 128 * 16 * 16 + 2 * kIq1Rows * 16;
+constexpr size_t kGridBytes = kGridDecOff + kGridDecBytes;
 
 // Work record of one active expert, written by the grouping: expert id, its first and
 // one-past-last sorted positions, and the slot at its first position.

@@ -90,6 +90,10 @@ k_gateup_dec(LayerArgs L, const float *__restrict__ x, int T, int kprime, const 
   float4 v[8];
 #pragma unroll
   for (int t = 0; t < 8; t++) v[t] = ((const float4 *)(x + (size_t)min(t, T - 1) * H))[ic];
+  // the decode tables next: issued before the first unit's weight loads, so waiting for
+  // them (vector loads complete in order) does not also wait for the weights
+  const DecTables D = dec_tables(QT);
+  const DecTableCopy tc = dec_tables_copy_load<QT>(L.grids, tid, blockDim.x);
   // the first unit's record through the scalar cache (its index does not depend on the
   // record count), so its weight loads leave without waiting for the copy
   int u = blockIdx.x * UPR + us;
@@ -97,14 +101,16 @@ k_gateup_dec(LayerArgs L, const float *__restrict__ x, int T, int kprime, const 
   if ((int)blockIdx.x * UPR >= total) return;  // no unit for this workgroup (uniform)
   const int a0 = min(u / rbs, n_ids - 1);
   GuUnit<NSB> cur = gu_issue<QT, NSB>(L, load_work(work, 1 + a0), u - a0 * rbs, u < total, kp);
-  const DecTables D = dec_tables(QT);
-  const DecTableRegs tr = dec_tables_load(L.grids, QT, tid, blockDim.x);
   const int XR = stage_row_halves(H);
   _Float16 *xs = (_Float16 *)(lds + D.bytes);
   float *red = (float *)(xs + (size_t)2 * T * XR);  // [UPR][KP][8 tokens][16 columns]
-  if (tid < nrec) recs[tid] = rec;
-  if (tid < nslots) tok_of[tid] = slot / kprime;
-  dec_tables_store(tr, QT, D, lds, tid, blockDim.x);
+  // unconditional stores (a conditional one lets the compiler move the load into the
+  // branch, where it waits for every older load): threads past the counts write
+  // entries never read, or at the clamped last index the value that entry holds
+  // (their loads were clamped to the last record / slot)
+  recs[min(tid, kDecMaxSlots)] = rec;
+  tok_of[min(tid, kDecMaxSlots - 1)] = slot / kprime;
+  dec_tables_copy_store<QT>(tc, lds, tid, blockDim.x);
   // activations: per token the largest magnitude (wave max, then the 16 wave maxima),
   // then the hi / lo rows
   const bool mine = 4 * tid < H;

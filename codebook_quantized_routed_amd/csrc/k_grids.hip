@@ -1,5 +1,6 @@
 // Grid expansion and bit-exact dequantization to fp32.
 #include "decode.hpp"
+#include "mfma_dec.hpp"
 
 namespace moe {
 
@@ -16,6 +17,15 @@ __global__ void __launch_bounds__(256) k_grids_expand(const uint16_t *c2, const 
   }
   for (int i = threadIdx.x; i < kIq2Rows; i += blockDim.x) ((uint16_t *)(grids + kGridIq2CompactOff))[i] = c2[i];
   for (int i = threadIdx.x; i < kIq1Rows; i += blockDim.x) ((uint16_t *)(grids + kGridIq1CompactOff))[i] = c1[i];
+  // the matrix-core decode tables, from the compact rows, in their LDS layout
+  DecTableRegs r;
+  const int t = threadIdx.x, n = blockDim.x;
+#pragma unroll
+  for (int i = 0; i < 2; i++) r.c2[i] = t + i * n < kIq2Rows ? c2[t + i * n] : 0u;
+#pragma unroll
+  for (int i = 0; i < 8; i++) r.c1[i] = t + i * n < kIq1Rows ? c1[t + i * n] : 0u;
+  dec_tables_store(r, MOE_Q_IQ2XS_LIKE | MOE_Q_IQ1M_LIKE, dec_tables(MOE_Q_IQ2XS_LIKE | MOE_Q_IQ1M_LIKE),
+                   grids + kGridDecOff, t, n);
 }
 
 hipError_t launch_grids_expand(const uint16_t *c2, const uint16_t *c1, uint8_t *grids, hipStream_t s) {

@@ -46,7 +46,7 @@ struct DecTables {
   int iq2h, iq2ss, iq1d, bytes;
 };
 
-__host__ __device__ inline DecTables dec_tables(int formats) {
+__host__ __device__ constexpr DecTables dec_tables(int formats) {
   DecTables t{-1, -1, -1, 0};
   if (formats & MOE_Q_IQ2XS_LIKE) {
     t.iq2h = t.bytes;
@@ -59,6 +59,37 @@ __host__ __device__ inline DecTables dec_tables(int formats) {
     t.bytes += 2 * kIq1Rows * 16;
   }
   return t;
+}
+
+static_assert(kGridDecBytes == (size_t)dec_tables(MOE_Q_IQ2XS_LIKE | MOE_Q_IQ1M_LIKE).bytes,
+              "the grid buffer holds the decode tables of both formats");
+
+// Copy of the decode tables of format(s) QT from the grid buffer (written there once by
+// moe_grids_expand) into LDS at dec_tables(QT): thread t of n (n >= 256) takes the
+// 16-byte words t, t + n, ...  The loads are issued unconditionally (clamped) so they
+// leave together; call dec_tables_copy_store after whatever else should travel with them.
+struct DecTableCopy {
+  uint4 w[4];
+};
+template <int QT>
+__device__ __forceinline__ DecTableCopy dec_tables_copy_load(const uint8_t *grids, int t, int n) {
+  // the IQ1 rows follow the IQ2 tables in the grid buffer
+  constexpr size_t src_off = QT == MOE_Q_IQ1M_LIKE ? kIq2Rows * 16 + 128 * 16 * 16 : 0;
+  constexpr int words = (int)(dec_tables(QT).bytes / 16);
+  static_assert(words <= 4 * 1024, "at most four words per thread of a 1024-thread block");
+  const uint4 *src = (const uint4 *)(grids + kGridDecOff + src_off);
+  DecTableCopy c;
+#pragma unroll
+  for (int k = 0; k < 4; k++) c.w[k] = src[min(t + k * n, words - 1)];
+  return c;
+}
+template <int QT>
+__device__ __forceinline__ void dec_tables_copy_store(const DecTableCopy &c, uint8_t *lds, int t, int n) {
+  constexpr int words = (int)(dec_tables(QT).bytes / 16);
+  uint4 *dst = (uint4 *)lds;
+#pragma unroll
+  for (int k = 0; k < 4; k++)
+    if (t + k * n < words) dst[t + k * n] = c.w[k];
 }
 
 // The compact rows a loader thread expands (issued early: the loads of the table build).

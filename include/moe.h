@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 9
+#define MOE_ABI_VERSION 10
 #define MOE_MAX_BANKS 4
 #define MOE_MAX_K 16        /* routed experts per token */
 #define MOE_MAX_IDS 1024    /* E + has_shared */
@@ -127,8 +127,9 @@ const char *moe_status_string(moe_status s);
 int32_t moe_last_hip_error(void);
 const char *moe_last_hip_error_string(void);
 
-/* Size of the expanded-grid buffer (the grid values of both formats, plus derived
- * tables the kernels read). */
+/* Size of the expanded-grid buffer: the grid values of both formats, the compact rows,
+ * and the fp16 tables the matrix-core decode kernels copy into LDS (written once here
+ * instead of built by every workgroup). */
 size_t moe_grids_bytes(void);
 
 /* Expands the compact grids once ("Red Lite dev10", section "Quant grids": the runtime

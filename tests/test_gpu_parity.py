@@ -49,7 +49,24 @@ def test_grids_expand_bit_exact(grids, ogrids, grids_compact):
     c2, c1 = grids_compact
     np.testing.assert_array_equal(g[20480:21504].view(np.uint16), c2)
     np.testing.assert_array_equal(g[21504:25600].view(np.uint16), c1)
-    assert g.size == moe.grids_bytes() == 25600
+    assert g.size == moe.grids_bytes() == 25600 + 8192 + 32768 + 65536
+    # the matrix-core decode tables, from the oracle's grid values and the pages' sign
+    # and scale mapping: fp16 IQ2 rows; per (7 explicit signs, 4-bit scale) the eight
+    # values +-(2s + 1), the eighth sign being the parity of the seven; IQ1 rows with
+    # +1/8, then with -1/8 added
+    dec = g[25600:]
+    np.testing.assert_array_equal(dec[:8192].view(np.float16).reshape(512, 8),
+                                  ogrids.iq2_array().astype(np.float16))
+    e = np.arange(128 * 16)
+    s7, sc = e >> 4, e & 15
+    parity = np.array([bin(v).count("1") & 1 for v in range(128)])[s7]
+    bits = (s7 | (parity << 7))[:, None] >> np.arange(8)[None, :] & 1
+    ss = np.where(bits == 1, -(2 * sc + 1)[:, None], (2 * sc + 1)[:, None]).astype(np.float16)
+    np.testing.assert_array_equal(dec[8192:40960].view(np.float16).reshape(2048, 8), ss)
+    G1 = ogrids.iq1_array().astype(np.float64)
+    d1 = dec[40960:].view(np.float16).reshape(2, 2048, 8)
+    np.testing.assert_array_equal(d1[0], (G1 + 0.125).astype(np.float16))
+    np.testing.assert_array_equal(d1[1], (G1 - 0.125).astype(np.float16))
 
 
 def _dequant_gpu(qt, rows, cols, streams, grids):
