@@ -219,22 +219,15 @@ __device__ __forceinline__ WorkRec mfma_tile(const WorkRec *work, int n_ids, int
   return load_work(work, n_ids + 1 + i);
 }
 
-// gate + up + SiLU * up.  Workgroup = (tile, block of 128 rows of inter); wave
-// w takes gate and up rows r0 .. r0 + 31, r0 = 128 * block + 32 w.  One instance per
-// format: a workgroup whose expert has the other format returns at once.
+// gate + up + SiLU * up of one tile for a workgroup = (tile W, block rb of 128 rows of
+// inter); wave w takes gate and up rows r0 .. r0 + 31, r0 = 128 rb + 32 w.  TL: the table
+// layout of the launch's formats; only this tile's format is built.
 template <int QT>
-__global__ void __launch_bounds__(256) k_gateup_mfma(LayerArgs L, const float *__restrict__ x, int kprime,
-                                                     const int32_t *__restrict__ sorted_slot,
-                                                     const WorkRec *__restrict__ work, int n_ids,
-                                                     float *__restrict__ h) {
-  extern __shared__ __align__(16) uint8_t lds[];
-  const int H = L.hidden, I = L.inter, RB = I / 128;
-  const int a = blockIdx.x / RB, rb = blockIdx.x - a * RB;
-  if (a >= sload(&work[0].slot0)) return;  // record 0 = (matvec experts, slots, MFMA experts, tiles)
-  const WorkRec W = mfma_tile(work, n_ids, a);
-  const BankArgs &B = bank_of(L, W.e);
-  if (B.qtype != QT) return;
-  const TableLayout TL = table_layout(QT);
+__device__ __forceinline__ void gateup_tile(const LayerArgs &L, const float *__restrict__ x, int kprime,
+                                            const int32_t *__restrict__ sorted_slot, const WorkRec &W,
+                                            const BankArgs &B, int rb, const TableLayout &TL, uint8_t *lds,
+                                            float *__restrict__ h) {
+  const int H = L.hidden, I = L.inter;
   _Float16 *xbuf = (_Float16 *)(lds + TL.bytes);
   int *src_row = (int *)(xbuf + 4 * kXHalves);
   build_tables(L.grids, QT, TL, lds);
@@ -263,21 +256,37 @@ __global__ void __launch_bounds__(256) k_gateup_mfma(LayerArgs L, const float *_
   }
 }
 
-// down: y[p] = Wd h[p].  Workgroup = (tile, block of 256 rows of hidden); wave w
-// takes rows r0 .. r0 + 63, r0 = 256 * block + 64 w.  h rows are contiguous per expert.
-// One instance per format, as above.
-template <int QT>
-__global__ void __launch_bounds__(256) k_down_mfma(LayerArgs L, const float *__restrict__ h,
-                                                   const WorkRec *__restrict__ work, int n_ids,
-                                                   float *__restrict__ y) {
+// One launch for the layer's formats FMT (MOE_Q_* bits): a workgroup runs the format of
+// its tile's expert, so a layer with both formats has one launch and one tail.
+template <int FMT>
+__global__ void __launch_bounds__(256) k_gateup_mfma(LayerArgs L, const float *__restrict__ x, int kprime,
+                                                     const int32_t *__restrict__ sorted_slot,
+                                                     const WorkRec *__restrict__ work, int n_ids,
+                                                     float *__restrict__ h) {
   extern __shared__ __align__(16) uint8_t lds[];
-  const int H = L.hidden, I = L.inter, RB = H / 256;
+  const int RB = L.inter / 128;
   const int a = blockIdx.x / RB, rb = blockIdx.x - a * RB;
-  if (a >= sload(&work[0].slot0)) return;
+  if (a >= sload(&work[0].slot0)) return;  // record 0 = (matvec experts, slots, MFMA experts, tiles)
   const WorkRec W = mfma_tile(work, n_ids, a);
   const BankArgs &B = bank_of(L, W.e);
-  if (B.qtype != QT) return;
-  const TableLayout TL = table_layout(QT);
+  const TableLayout TL = table_layout(FMT);
+  if constexpr (FMT == MOE_Q_IQ2XS_LIKE || FMT == MOE_Q_IQ1M_LIKE) {
+    gateup_tile<FMT>(L, x, kprime, sorted_slot, W, B, rb, TL, lds, h);
+  } else if (B.qtype == MOE_Q_IQ2XS_LIKE) {
+    gateup_tile<MOE_Q_IQ2XS_LIKE>(L, x, kprime, sorted_slot, W, B, rb, TL, lds, h);
+  } else {
+    gateup_tile<MOE_Q_IQ1M_LIKE>(L, x, kprime, sorted_slot, W, B, rb, TL, lds, h);
+  }
+}
+
+// down: y[p] = Wd h[p] of one tile for a workgroup = (tile, block rb of 256 rows of
+// hidden); wave w takes rows r0 .. r0 + 63, r0 = 256 rb + 64 w.  h rows are contiguous per
+// expert.
+template <int QT>
+__device__ __forceinline__ void down_tile(const LayerArgs &L, const float *__restrict__ h, const WorkRec &W,
+                                          const BankArgs &B, int rb, const TableLayout &TL, uint8_t *lds,
+                                          float *__restrict__ y) {
+  const int H = L.hidden, I = L.inter;
   _Float16 *xbuf = (_Float16 *)(lds + TL.bytes);
   int *src_row = (int *)(xbuf + 4 * kXHalves);
   build_tables(L.grids, QT, TL, lds);
@@ -300,20 +309,43 @@ __global__ void __launch_bounds__(256) k_down_mfma(LayerArgs L, const float *__r
   }
 }
 
+template <int FMT>
+__global__ void __launch_bounds__(256) k_down_mfma(LayerArgs L, const float *__restrict__ h,
+                                                   const WorkRec *__restrict__ work, int n_ids,
+                                                   float *__restrict__ y) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int RB = L.hidden / 256;
+  const int a = blockIdx.x / RB, rb = blockIdx.x - a * RB;
+  if (a >= sload(&work[0].slot0)) return;
+  const WorkRec W = mfma_tile(work, n_ids, a);
+  const BankArgs &B = bank_of(L, W.e);
+  const TableLayout TL = table_layout(FMT);
+  if constexpr (FMT == MOE_Q_IQ2XS_LIKE || FMT == MOE_Q_IQ1M_LIKE) {
+    down_tile<FMT>(L, h, W, B, rb, TL, lds, y);
+  } else if (B.qtype == MOE_Q_IQ2XS_LIKE) {
+    down_tile<MOE_Q_IQ2XS_LIKE>(L, h, W, B, rb, TL, lds, y);
+  } else {
+    down_tile<MOE_Q_IQ1M_LIKE>(L, h, W, B, rb, TL, lds, y);
+  }
+}
+
+#define MOE_MFMA_FMT(KERNEL, ...)                                                                          \
+  do {                                                                                                      \
+    if (L.formats == MOE_Q_IQ2XS_LIKE)                                                                      \
+      hipLaunchKernelGGL(KERNEL<MOE_Q_IQ2XS_LIKE>, grid, dim3(256), mfma_lds_bytes(L.formats), s, __VA_ARGS__); \
+    else if (L.formats == MOE_Q_IQ1M_LIKE)                                                                  \
+      hipLaunchKernelGGL(KERNEL<MOE_Q_IQ1M_LIKE>, grid, dim3(256), mfma_lds_bytes(L.formats), s, __VA_ARGS__); \
+    else                                                                                                    \
+      hipLaunchKernelGGL(KERNEL<MOE_Q_IQ2XS_LIKE | MOE_Q_IQ1M_LIKE>, grid, dim3(256), mfma_lds_bytes(L.formats), s, \
+                         __VA_ARGS__);                                                                      \
+  } while (0)
+
 hipError_t launch_gateup_mfma(const LayerArgs &L, const float *x, int T, int kprime, const int32_t *sorted_slot,
                               const WorkRec *work, int n_ids, float *h, hipStream_t s) {
   const long n = max_mfma_tiles(T, kprime, n_ids);
   if (n == 0) return hipSuccess;
   const dim3 grid((unsigned)(n * (L.inter / 128)));
-  if (L.formats & MOE_Q_IQ2XS_LIKE) {
-    hipLaunchKernelGGL(k_gateup_mfma<MOE_Q_IQ2XS_LIKE>, grid, dim3(256), mfma_lds_bytes(MOE_Q_IQ2XS_LIKE), s, L, x,
-                       kprime, sorted_slot, work, n_ids, h);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-  }
-  if (L.formats & MOE_Q_IQ1M_LIKE)
-    hipLaunchKernelGGL(k_gateup_mfma<MOE_Q_IQ1M_LIKE>, grid, dim3(256), mfma_lds_bytes(MOE_Q_IQ1M_LIKE), s, L, x,
-                       kprime, sorted_slot, work, n_ids, h);
+  MOE_MFMA_FMT(k_gateup_mfma, L, x, kprime, sorted_slot, work, n_ids, h);
   return hipGetLastError();
 }
 
@@ -322,16 +354,9 @@ hipError_t launch_down_mfma(const LayerArgs &L, const float *h, int T, int kprim
   const long n = max_mfma_tiles(T, kprime, n_ids);
   if (n == 0) return hipSuccess;
   const dim3 grid((unsigned)(n * (L.hidden / 256)));
-  if (L.formats & MOE_Q_IQ2XS_LIKE) {
-    hipLaunchKernelGGL(k_down_mfma<MOE_Q_IQ2XS_LIKE>, grid, dim3(256), mfma_lds_bytes(MOE_Q_IQ2XS_LIKE), s, L, h,
-                       work, n_ids, y);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-  }
-  if (L.formats & MOE_Q_IQ1M_LIKE)
-    hipLaunchKernelGGL(k_down_mfma<MOE_Q_IQ1M_LIKE>, grid, dim3(256), mfma_lds_bytes(MOE_Q_IQ1M_LIKE), s, L, h, work,
-                       n_ids, y);
+  MOE_MFMA_FMT(k_down_mfma, L, h, work, n_ids, y);
   return hipGetLastError();
 }
+#undef MOE_MFMA_FMT
 
 }  // namespace moe
