@@ -9,7 +9,7 @@
 // (16 B columns); the hidden dimension is split into parts of two super-blocks, one
 // wave each; the parts' partials are added in part order, then scaled back by 2^-e of
 // the token.  The down projection of these calls stays on the vector kernels
-// (k_matvec.hip): with about one token per selected expert a 16-row A operand is
+// (k_gemv.hip): with about one token per selected expert a 16-row A operand is
 // mostly empty, and the decode through LDS tables measured slower there.
 #include "mfma_dec.hpp"
 #include "route_dev.hpp"
