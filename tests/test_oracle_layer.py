@@ -141,3 +141,29 @@ def test_residual_chain_is_stable(ogrids):
     assert np.all(np.isfinite(h))
     for t in range(2):
         assert np.abs(h[t] - h64[t]).max() <= 1e-5 * np.linalg.norm(h64[t])
+
+
+@pytest.mark.parametrize("banks", [[(synth.QTYPE_IQ2XS, 2), (synth.QTYPE_IQ1M, 2)]])
+def test_fp64_shadow_brute_force_numpy(ogrids, banks):
+    """The fp64 shadow of the layer against the same numpy float64 brute force, at the
+    bound of float64 summation order (measured ~1e-16 of the norm; fp32 sits near 1e-7), not
+    the fp32 one: pins the shadow independently of its fp32 twin."""
+    layer = synth.make_layer(banks, hidden=256, inter=256, n_experts=4, has_shared=1, tag="tiny64")
+    tab = O.ExpertTable(layer)
+    T, k = 4, 3
+    x = synth.activations(T, 256, tag="tiny64/x")
+    lg = synth.logits(T, 4, tag="tiny64/l")
+    acc0 = synth.activations(T, 256, tag="tiny64/acc")
+    r = O.moe_layer_f64(tab, ogrids, x, k, True, logits=lg, acc=acc0)
+    ref = acc0.astype(np.float64).copy()
+    for t in range(T):
+        sel = np.lexsort((np.arange(4), -lg[t].astype(np.float64)))[:k]
+        p = softmax(lg[t].astype(np.float64))[sel]
+        p = p / p.sum()
+        for e, wt in list(zip(sel, p)) + [(4, 1.0)]:
+            Wg, Wu, Wd = (O.dequant(tab.qmat(e, n), ogrids).astype(np.float64) for n in ("gate", "up", "down"))
+            g = Wg @ x[t].astype(np.float64)
+            h = g * expit(g) * (Wu @ x[t].astype(np.float64))
+            ref[t] += wt * (Wd @ h)
+    for t in range(T):
+        assert np.abs(r["acc"][t] - ref[t]).max() <= 1e-13 * np.linalg.norm(ref[t])

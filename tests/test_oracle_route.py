@@ -107,3 +107,40 @@ def test_route_signed_zero_and_heavy_ties(kind, E, k):
     if kind == "all_zero":
         np.testing.assert_array_equal(ids, np.tile(np.arange(k), (T, 1)))
         assert np.all(w == np.float32(1.0) / np.float32(k))
+
+
+def test_route_fp64_against_full_sort_and_scipy():
+    """The fp64 shadow of the router top-k against a full float64 sort (ties to the lower
+    id) and scipy's softmax renormalised over the selection, to float64 rounding: pins
+    the shadow independently of its fp32 twin."""
+    from scipy.special import softmax
+    lg = synth.logits(16, 512, tag="r64/sort")
+    ids64, w64 = O.route_f64(lg, 10, True)
+    for t in range(16):
+        sel = np.lexsort((np.arange(512), -lg[t].astype(np.float64)))[:10]
+        p = softmax(lg[t].astype(np.float64))[sel]
+        np.testing.assert_array_equal(ids64[t, :10], sel)
+        np.testing.assert_allclose(w64[t, :10], p / p.sum(), rtol=1e-14, atol=0)
+        assert ids64[t, 10] == 512 and w64[t, 10] == 1.0
+
+
+def test_accumulate_fp64_exact_on_dyadic_values():
+    """acc + sum of w * y over the slots in ascending id, on values whose products and
+    partial sums are exact in float64 (small dyadic rationals): the shadow must return
+    the exact rational sum, and the order of the slots in the list must not matter."""
+    from fractions import Fraction
+    rng = np.random.default_rng(7)
+    T, kp, H = 3, 5, 16
+    ids = np.stack([rng.permutation(9)[:kp] for _ in range(T)]).astype(np.int32)
+    w = rng.integers(-8, 9, size=(T, kp)) / 16.0
+    y = rng.integers(-1000, 1001, size=(T * kp, H)) / 64.0
+    acc = rng.integers(-50, 51, size=(T, H)) / 4.0
+    got = O.accumulate_f64(y, w, ids, acc)
+    for t in range(T):
+        for c in range(H):
+            exact = Fraction(acc[t, c]) + sum(Fraction(w[t, j]) * Fraction(y[t * kp + j, c]) for j in range(kp))
+            assert Fraction(got[t, c]) == exact
+    perm = rng.permutation(kp)
+    rows = (np.arange(T)[:, None] * kp + perm[None, :]).reshape(-1)
+    again = O.accumulate_f64(y[rows], w[:, perm], ids[:, perm], acc)
+    np.testing.assert_array_equal(again, got)
