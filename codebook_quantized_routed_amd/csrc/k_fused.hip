@@ -88,7 +88,8 @@ struct FusedLds {
   float w[kFusedMaxSlots];             // slot j -> router weight
   int32_t slot_at[kFusedMaxSlots];     // sorted position p -> slot
   int32_t pos_of[kFusedMaxSlots];      // slot j -> sorted position
-  float ydot[kFusedMaxSlots][16];      // down outputs of the block's rows, per slot
+  float wpos[kFusedMaxSlots];          // sorted position p -> router weight
+  float ydot[kFusedMaxSlots][16];      // down outputs of the block's rows, per sorted position
   float xs[64 * kXsRow];               // the token's activations, lane l's 32 at l * kXsRow
   uint32_t tag;                        // the call's tag
 };
@@ -172,7 +173,8 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
   uint32_t tag = 0;
   if (threadIdx.x == 64) tag = call_tag(sync);
   // waves 1..: the activations, one float4 per thread (hidden 2048), staged in LDS with
-  // the tables
+  // the tables (loading each wave's slice from global memory instead was measured 0.6 us
+  // slower)
   const int xt = threadIdx.x - 64;
   float4 xv;
   if (xt >= 0 && xt < 512) xv = ((const float4 *)x)[xt];
@@ -180,9 +182,9 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
   // ---- 1. routing, in every workgroup, by wave 0; the other waves expand the grid
   // tables into LDS meanwhile
   if (wave == 0) {
-    int sel = 0x7FFFFFFF;
+    TopkSlot ts{0x7FFFFFFF, -1, 0.0f};
     if (logits) {
-      sel = topk_select<8, 1, 16>(tv, E, k, add_shared, blockIdx.x == 0 ? ids : nullptr, w, S.ids, S.w, S.topk);
+      ts = topk_select<8, 1, 16>(tv, E, k, add_shared, blockIdx.x == 0 ? ids : nullptr, w, S.ids, S.w, S.topk);
     } else {
       if (lane < k) {
         S.ids[lane] = ids[lane];
@@ -198,13 +200,16 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
       }
     }
     __builtin_amdgcn_wave_barrier();
-    // routed: the ids are still in the lanes; explicit: as copied to LDS above
-    const int my = logits ? sel : (lane < kprime ? S.ids[lane] : 0x7FFFFFFF);
-    const int rank = slot_rank(my, lane);
+    // routed: the slot, its position and weight are still in the lanes; explicit: as
+    // copied to LDS above, positions by counting
+    const int my = logits ? ts.id : (lane < kprime ? S.ids[lane] : 0x7FFFFFFF);
+    const int rank = logits ? ts.pos : slot_rank(my, lane);
+    const float wt = logits ? ts.w : (lane < kprime ? S.w[lane] : 0.0f);
     if (lane < kprime) {
       S.pos_of[lane] = rank;
       S.slot_at[rank] = lane;
       S.pos[rank] = PosRec{my, lane, bank_index(L, my), 0};
+      S.wpos[rank] = wt;
     }
   } else {
     tables_store(tr, formats, TL, lds, threadIdx.x - 64, blockDim.x - 64, false);
@@ -278,13 +283,14 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
     for (int i = 0; i < kFusedSlotsPerWave; i++) {
       const int j = wave + kDownWaves * i;
       if (!down_wave || j >= kprime) break;
+      const int pj = uniform(S.pos_of[j]);
       RowRaw R;
       int qt;
       if (first && i == 0) {
         R = Rd0;
         qt = dqt0;
       } else {
-        const PosRec &P = S.pos[uniform(S.pos_of[j])];
+        const PosRec &P = S.pos[pj];
         const BankLds &B = S.banks[uniform(P.bank)];
         const QMat Wd = bank_mat(B, uniform(P.e), kDown);
         qt = uniform(B.qt);
@@ -292,22 +298,30 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
                                    : load_row<MOE_Q_IQ1M_LIKE>(Wd, I, tile * RPP + sub, lq);
       }
       // the slot's h row (written by other workgroups) into the wave's LDS area
-      stage_h_row<LPR>(h + (size_t)S.pos_of[j] * I, tag, hs, sync);
+      stage_h_row<LPR>(h + (size_t)pj * I, tag, hs, sync);
       __builtin_amdgcn_wave_barrier();
       const float *hrow = hs + lq * kChunkPad;
       const float v = fmt_iq2<FMT>(qt) ? down_slot_dot<MOE_Q_IQ2XS_LIKE, LPR>(R, hrow, lq, lds, TL)
                                              : down_slot_dot<MOE_Q_IQ1M_LIKE, LPR>(R, hrow, lq, lds, TL);
-      if (lq == 0) S.ydot[j][sub] = v;
+      if (lq == 0) S.ydot[pj][sub] = v;
       __builtin_amdgcn_wave_barrier();  // the staging area is reused by the next slot
     }
     __syncthreads();
     if (threadIdx.x < RPP) {
+      // acc += w * y over the sorted positions, i.e. in ascending expert id; every
+      // operand is read before the first add (positions past the last slot are read and
+      // not used), so the reads overlap instead of forming a chain
       const int r = tile * RPP + threadIdx.x;
-      float a = first ? acc_in : acc[r];
-      for (int p = 0; p < kprime; p++) {
-        const int j = S.slot_at[p];
-        a = __fadd_rn(a, __fmul_rn(S.w[j], S.ydot[j][threadIdx.x]));
+      float wv[kFusedMaxSlots], yv[kFusedMaxSlots];
+#pragma unroll
+      for (int p = 0; p < kFusedMaxSlots; p++) {
+        wv[p] = S.wpos[p];
+        yv[p] = S.ydot[p][threadIdx.x];
       }
+      float a = first ? acc_in : acc[r];
+#pragma unroll
+      for (int p = 0; p < kFusedMaxSlots; p++)
+        if (p < kprime) a = __fadd_rn(a, __fmul_rn(wv[p], yv[p]));
       acc[r] = a;
     }
     __syncthreads();
@@ -383,7 +397,9 @@ __device__ inline void route_wave(const float *logits, const LayerArgs &L, int E
                                   int32_t *ids_out, float *w_out, RouteLds &R, TopkLds &T) {
   const int lane = threadIdx.x & 63, kprime = k + add_shared;
   const TopkVals<8> tv = topk_load<8>(logits, E);
-  const int my = topk_select<8, 2, 16>(tv, E, k, add_shared, ids_out, w_out, R.ids, R.w, T);
+  // positions by counting, not the ones the top-k returns: with those, this kernel (at
+  // its register limit) was scheduled 8 % slower
+  const int my = topk_select<8, 2, 16>(tv, E, k, add_shared, ids_out, w_out, R.ids, R.w, T).id;
   const int rank = slot_rank(my, lane);
   if (lane < kprime) {
     R.pos_of[lane] = rank;
@@ -524,13 +540,14 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_stack_decode(
       for (int i = 0; i < kFusedSlotsPerWave; i++) {
         const int j = wave + kDownWaves * i;
         if (!item_wave || j >= kprime) break;
-        const PosRec &P = R.pos[uniform(R.pos_of[j])];
+        const int pj = uniform(R.pos_of[j]);
+        const PosRec &P = R.pos[pj];
         const BankLds &B = Bk[uniform(P.bank)];
         const QMat Wd = bank_mat(B, uniform(P.e), kDown);
         const int qt = uniform(B.qt);
         const RowRaw Rw = qt == MOE_Q_IQ2XS_LIKE ? load_row<MOE_Q_IQ2XS_LIKE>(Wd, I, tile * RPP + sub, lq)
                                                  : load_row<MOE_Q_IQ1M_LIKE>(Wd, I, tile * RPP + sub, lq);
-        stage_h_row<LPR>(hpl + (size_t)R.pos_of[j] * I, tag, hs, sync);
+        stage_h_row<LPR>(hpl + (size_t)pj * I, tag, hs, sync);
         __builtin_amdgcn_wave_barrier();
         const float *hrow = hs + lq * kChunkPad;
         const float v = qt == MOE_Q_IQ2XS_LIKE ? down_slot_dot<MOE_Q_IQ2XS_LIKE, LPR>(Rw, hrow, lq, lds, TL)

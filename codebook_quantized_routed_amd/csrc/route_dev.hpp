@@ -51,7 +51,7 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
 // If more than 64 keys reach tau (heavy ties), the selection falls back to k rounds of
 // a wave-wide arg-max.  Both give the same result.
 // Outputs: ids / w (global, skipped when ids is null) and the optional copies; returns
-// the lane's slot id.
+// the lane's slot (TopkSlot).
 constexpr int kCand = 64;
 
 struct TopkLds {
@@ -60,6 +60,16 @@ struct TopkLds {
   alignas(16) uint64_t cand[kCand];
   uint32_t sel_key[MOE_MAX_K];
   int sel_id[MOE_MAX_K];
+  int sel_pos[MOE_MAX_K];
+};
+
+// A lane's slot after the top-k.  Lane j < k: selection j, with its expert id, its
+// position among the token's slots in ascending expert id, and its router weight; lane k
+// with a shared expert: id E, position k (E is above every routed id), weight 1; other
+// lanes: id 0x7FFFFFFF, position -1.
+struct TopkSlot {
+  int id, pos;
+  float w;
 };
 
 // k rounds of: the largest remaining key, ties to the lowest expert id; the winner is
@@ -119,7 +129,7 @@ __device__ __forceinline__ TopkVals<VPL> topk_load(const float *__restrict__ l, 
 // below this one are not searched (stay zero); every caller takes 16, measured the
 // faster (or as fast) in each kernel.  The selection is the same.
 template <int VPL, int TAU_BITS = 1, int TAU_LOW = 0>
-__device__ __forceinline__ int topk_select(const TopkVals<VPL> &tv, int E, int k, int add_shared,
+__device__ __forceinline__ TopkSlot topk_select(const TopkVals<VPL> &tv, int E, int k, int add_shared,
                                             int32_t *__restrict__ ids, float *__restrict__ w, int32_t *ids_copy,
                                             float *w_copy, TopkLds &S) {
   int lane = threadIdx.x & 63;
@@ -178,19 +188,31 @@ __device__ __forceinline__ int topk_select(const TopkVals<VPL> &tv, int E, int k
         rank += (j + 1 < total && (((uint64_t)pr[u].w << 32) | pr[u].z) > mine) ? 1 : 0;
       }
     }
-    if (lane < total && rank < k) {
+    // the candidates are packed in ascending expert id, so a selected candidate's
+    // position among the selected ids is the count of selected candidates before it
+    const bool chosen = lane < total && rank < k;
+    const int pos = lanes_below(__ballot(chosen));
+    if (chosen) {
       S.sel_key[rank] = (uint32_t)(mine >> 32);
       S.sel_id[rank] = (int)~(uint32_t)mine;
+      S.sel_pos[rank] = pos;
     }
   } else {
     topk_select_rounds<VPL>(key, k, S);
+    __builtin_amdgcn_wave_barrier();
+    // positions in ascending expert id by counting (the ids are distinct)
+    const int sid = lane < k ? S.sel_id[lane] : 0x7FFFFFFF;
+    int pos = 0;
+    for (int j = 0; j < k; j++) pos += __builtin_amdgcn_readlane(sid, j) < sid ? 1 : 0;
+    if (lane < k) S.sel_pos[lane] = pos;
   }
   __builtin_amdgcn_wave_barrier();
   // weights: lane j exponentiates selection j; the sum runs over j in order
   float ex = 0.0f, top = 0.0f;
-  int myid = 0;
+  int myid = 0, mypos = -1;
   if (lane < k) {
     myid = S.sel_id[lane];
+    mypos = S.sel_pos[lane];
     top = from_orderable(S.sel_key[0]);
     ex = expf(__fsub_rn(from_orderable(S.sel_key[lane]), top));
   }
@@ -199,8 +221,9 @@ __device__ __forceinline__ int topk_select(const TopkVals<VPL> &tv, int E, int k
   float sum = 0.0f;
 #pragma unroll
   for (int j = 0; j < MOE_MAX_K; j++) sum = __fadd_rn(sum, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j)));
+  float wl = 0.0f;
   if (lane < k) {
-    const float wl = __fdiv_rn(ex, sum);
+    wl = __fdiv_rn(ex, sum);
     if (ids) {
       ids[lane] = myid;
       w[lane] = wl;
@@ -216,9 +239,9 @@ __device__ __forceinline__ int topk_select(const TopkVals<VPL> &tv, int E, int k
     if (ids_copy) ids_copy[k] = E;
     if (w_copy) w_copy[k] = 1.0f;
   }
-  // the lane's slot id (lane j < k: selection j; lane k: the shared expert), else
-  // 0x7FFFFFFF
-  return lane < k ? myid : (add_shared && lane == k ? E : 0x7FFFFFFF);
+  if (lane < k) return TopkSlot{myid, mypos, wl};
+  if (add_shared && lane == k) return TopkSlot{E, k, 1.0f};
+  return TopkSlot{0x7FFFFFFF, -1, 0.0f};
 }
 
 template <int VPL>
