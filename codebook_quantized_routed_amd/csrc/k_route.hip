@@ -24,7 +24,8 @@ __global__ void __launch_bounds__(256) k_topk(const float *__restrict__ logits, 
 // 16 waves.  Wave w owns a contiguous range of slots.  Pass 1 builds a histogram per
 // wave in LDS; an exclusive scan over (expert, wave) in expert-major order gives every
 // wave its starting cursor per expert; pass 2 walks the wave's slots 64 at a time and
-// ranks each lane among the earlier lanes holding the same expert.  Integer-only and
+// ranks each lane among the earlier lanes holding the same expert (found by ballots
+// over the bits of the id).  Integer-only and
 // order-defined, so the output is unique and identical run to run.
 
 constexpr int kGroupWaves = 16;
@@ -78,6 +79,7 @@ __device__ void group_block(const int32_t *ids, int n, int n_ids, int max_narrow
                             int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_slot,
                             int32_t *__restrict__ slot_pos, WorkRec *__restrict__ work, GroupLds &S) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int id_bits = n_ids > 1 ? 32 - __builtin_clz((unsigned)(n_ids - 1)) : 0;
   const int per = (((n + kGroupWaves - 1) / kGroupWaves) + 63) / 64 * 64;
   const int lo = wave * per, hi = min(n, lo + per);
   const int nw = min(kGroupWaves, (n + per - 1) / per);  // the waves that hold slots
@@ -136,14 +138,15 @@ __device__ void group_block(const int32_t *ids, int n, int n_ids, int max_narrow
       int v = ids[s];
       my = (v >= 0 && v < n_ids) ? v : -1;
     }
-    int rank = 0, tot = 0;
-    for (int j = 0; j < 64; j++) {
-      int ej = __builtin_amdgcn_readlane(my, j);
-      if (ej == my) {
-        tot++;
-        rank += j < lane ? 1 : 0;
-      }
+    // the lanes holding the same expert: one ballot per bit of the id (ids < 2^id_bits),
+    // intersected, among the lanes that hold a slot; rank = those below this lane
+    uint64_t peers = __ballot(my >= 0);
+    for (int b = 0; b < id_bits; b++) {
+      const bool bit = (my >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      peers &= bit ? m : ~m;
     }
+    const int rank = lanes_below(peers), tot = (int)__popcll(peers);
     if (my >= 0) {
       int pos = S.hist[wave][my] + rank;
       sorted_slot[pos] = s;
