@@ -34,10 +34,9 @@ constexpr int kMfTiles = 4;              // 16-row tiles per wave
 constexpr int kXRow = 256 + 8;           // halves per staged column (16 bytes of padding)
 constexpr int kXHalves = kMfPass * kXRow;  // one of hi / lo, one buffer
 
-// LDS: grid tables, then two buffers of staged activations (hi, lo), then the pass's
-// source rows.
+// LDS: grid tables, then two buffers of staged activations (hi, lo).
 __host__ __device__ inline size_t mfma_lds_bytes(int formats) {
-  return table_layout(formats).bytes + 4 * kXHalves * sizeof(_Float16) + kMfPass * sizeof(int);
+  return table_layout(formats).bytes + 4 * kXHalves * sizeof(_Float16);
 }
 
 // The lane's codes of one tile row for one super-block.  IQ2: c = 8 codes (u16), s = the
@@ -119,16 +118,16 @@ __device__ __forceinline__ h8 decode_a(const TileCodes &t, int ks, int qd, const
   return __builtin_bit_cast(h8, v);
 }
 
-// Staging of 256 columns of the pass's kMfPass activation rows: thread t takes row
-// t / 16, floats 16 (t % 16) .. + 15.  stage_load issues the global loads (src_row[c]
-// < 0: zeros), stage_store splits each value into fp16 hi / lo halves in LDS.
+// Staging of 256 columns of the pass's kMfPass activation rows: thread t takes column
+// c = t / 16 of the pass (source row r, from the caller), floats 16 (t % 16) .. + 15.
+// stage_load issues the global loads (r < 0: zeros), stage_store splits each value into
+// fp16 hi / lo halves in LDS.
 struct XRegs {
   u32x4 v[4];
 };
 
-__device__ __forceinline__ XRegs stage_load(const float *base, int row_stride, const int *src_row, int col0) {
-  const int c = threadIdx.x >> 4, part = threadIdx.x & 15;
-  const int r = src_row[c];
+__device__ __forceinline__ XRegs stage_load(const float *base, int row_stride, int r, int col0) {
+  const int part = threadIdx.x & 15;
   XRegs x;
   const u32x4 *p = (const u32x4 *)(base + (size_t)(r < 0 ? 0 : r) * row_stride + col0 + 16 * part);
 #pragma unroll
@@ -158,11 +157,15 @@ __device__ __forceinline__ void stage_store(const XRegs &x, _Float16 *xhi, _Floa
 // over the K range [0, cols) in super-blocks.  Super-block sb + 1's activations, codes
 // and scales are loaded while sb is computed; the staged activations alternate
 // between two LDS buffers, with one workgroup barrier per super-block.  Ct[t]: the
-// fp32 result of tile t.  The caller has built the grid tables and set src_row.
+// fp32 result of tile t.  my_row: the source row of the thread's staging column.  With
+// store_tables, the grid tables (whose compact rows tr the caller loaded first) are
+// expanded into LDS after the first super-block's codes and activations are requested,
+// so the three loads travel together.
 template <int QT>
 __device__ __forceinline__ void mfma_pass(const QMat (&mats)[kMfTiles], const int (&trow)[kMfTiles], int cols,
-                                          const float *xbase, int x_stride, const int *src_row, const uint8_t *lds,
-                                          const TableLayout &TL, _Float16 *xbuf, f4 (&Ct)[kMfTiles]) {
+                                          const float *xbase, int x_stride, int my_row, const TableRegs &tr,
+                                          bool store_tables, uint8_t *lds, const TableLayout &TL, _Float16 *xbuf,
+                                          f4 (&Ct)[kMfTiles]) {
   const int lane = threadIdx.x & 63, qd = lane >> 4, lr = lane & 15;
   const int nsb = cols >> 8;
 #pragma unroll
@@ -170,7 +173,9 @@ __device__ __forceinline__ void mfma_pass(const QMat (&mats)[kMfTiles], const in
   TileCodes tc[kMfTiles];
 #pragma unroll
   for (int t = 0; t < kMfTiles; t++) tc[t] = load_tile_codes<QT>(mats[t], cols, trow[t] + lr, 0, qd);
-  stage_store(stage_load(xbase, x_stride, src_row, 0), xbuf, xbuf + kXHalves);
+  const XRegs x0 = stage_load(xbase, x_stride, my_row, 0);
+  if (store_tables) tables_store(tr, QT, TL, lds, threadIdx.x, blockDim.x, false);
+  stage_store(x0, xbuf, xbuf + kXHalves);
   __syncthreads();
   for (int sb = 0; sb < nsb; sb++) {
     const _Float16 *xhi = xbuf + (sb & 1) * 2 * kXHalves, *xlo = xhi + kXHalves;
@@ -178,7 +183,7 @@ __device__ __forceinline__ void mfma_pass(const QMat (&mats)[kMfTiles], const in
     XRegs xn;
     TileCodes nx[kMfTiles];
     if (more) {
-      xn = stage_load(xbase, x_stride, src_row, (sb + 1) * 256);
+      xn = stage_load(xbase, x_stride, my_row, (sb + 1) * 256);
 #pragma unroll
       for (int t = 0; t < kMfTiles; t++) nx[t] = load_tile_codes<QT>(mats[t], cols, trow[t] + lr, sb + 1, qd);
     }
@@ -222,6 +227,18 @@ __device__ __forceinline__ WorkRec mfma_tile(const WorkRec *work, int n_ids, int
 // gate + up + SiLU * up of one tile for a workgroup = (tile W, block rb of 128 rows of
 // inter); wave w takes gate and up rows r0 .. r0 + 31, r0 = 128 rb + 32 w.  TL: the table
 // layout of the launch's formats; only this tile's format is built.
+// The source row (token) of the thread's staging column t / 16 of the pass at sorted
+// position pp with n columns: the wave's four columns come through scalar loads of the
+// sorted slots (clamped; columns past n stage zeros).
+__device__ __forceinline__ int pass_token_row(const int32_t *sorted_slot, int pp, int n, int kprime) {
+  const int cb = uniform((int)(threadIdx.x >> 6) * 4);
+  int r[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) r[i] = cb + i < n ? sload(sorted_slot + pp + min(cb + i, n - 1)) / kprime : -1;
+  const int j = (threadIdx.x >> 4) & 3;
+  return j == 0 ? r[0] : (j == 1 ? r[1] : (j == 2 ? r[2] : r[3]));
+}
+
 template <int QT>
 __device__ __forceinline__ void gateup_tile(const LayerArgs &L, const float *__restrict__ x, int kprime,
                                             const int32_t *__restrict__ sorted_slot, const WorkRec &W,
@@ -229,8 +246,8 @@ __device__ __forceinline__ void gateup_tile(const LayerArgs &L, const float *__r
                                             float *__restrict__ h) {
   const int H = L.hidden, I = L.inter;
   _Float16 *xbuf = (_Float16 *)(lds + TL.bytes);
-  int *src_row = (int *)(xbuf + 4 * kXHalves);
-  build_tables(L.grids, QT, TL, lds);
+  // the compact grid rows are the first loads; the tables are expanded in the pass
+  const TableRegs tr = tables_load(L.grids, QT);
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6), qd = lane >> 4, lr = lane & 15;
   const QMat Wg = expert_mat(B, W.e, kGate, I, H), Wu = expert_mat(B, W.e, kUp, I, H);
   const int r0 = rb * 128 + wave * 32;
@@ -238,10 +255,9 @@ __device__ __forceinline__ void gateup_tile(const LayerArgs &L, const float *__r
   const int trow[kMfTiles] = {r0, r0 + 16, r0, r0 + 16};
   for (int pp = W.p0; pp < W.p1; pp += kMfPass) {
     const int n = min(kMfPass, W.p1 - pp);
-    if (threadIdx.x < kMfPass) src_row[threadIdx.x] = threadIdx.x < n ? sorted_slot[pp + threadIdx.x] / kprime : -1;
-    __syncthreads();
     f4 Ct[kMfTiles];
-    mfma_pass<QT>(mats, trow, H, x, H, src_row, lds, TL, xbuf, Ct);
+    mfma_pass<QT>(mats, trow, H, x, H, pass_token_row(sorted_slot, pp, n, kprime), tr, pp == W.p0, lds, TL, xbuf,
+                  Ct);
     if (lr < n) {
 #pragma unroll
       for (int j = 0; j < 2; j++) {
@@ -288,8 +304,7 @@ __device__ __forceinline__ void down_tile(const LayerArgs &L, const float *__res
                                           float *__restrict__ y) {
   const int H = L.hidden, I = L.inter;
   _Float16 *xbuf = (_Float16 *)(lds + TL.bytes);
-  int *src_row = (int *)(xbuf + 4 * kXHalves);
-  build_tables(L.grids, QT, TL, lds);
+  const TableRegs tr = tables_load(L.grids, QT);
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6), qd = lane >> 4, lr = lane & 15;
   const QMat Wd = expert_mat(B, W.e, kDown, H, I);
   const int r0 = rb * 256 + wave * 64;
@@ -297,10 +312,9 @@ __device__ __forceinline__ void down_tile(const LayerArgs &L, const float *__res
   const int trow[kMfTiles] = {r0, r0 + 16, r0 + 32, r0 + 48};
   for (int pp = W.p0; pp < W.p1; pp += kMfPass) {
     const int n = min(kMfPass, W.p1 - pp);
-    if (threadIdx.x < kMfPass) src_row[threadIdx.x] = threadIdx.x < n ? pp + (int)threadIdx.x : -1;
-    __syncthreads();
+    const int c = threadIdx.x >> 4;
     f4 Ct[kMfTiles];
-    mfma_pass<QT>(mats, trow, I, h, I, src_row, lds, TL, xbuf, Ct);
+    mfma_pass<QT>(mats, trow, I, h, I, c < n ? pp + c : -1, tr, pp == W.p0, lds, TL, xbuf, Ct);
     if (lr < n) {
 #pragma unroll
       for (int t = 0; t < kMfTiles; t++)
