@@ -20,7 +20,7 @@ IQ1S_LIKE = 4  # repacked into IQ1M_LIKE banks when a layer is loaded
 MAX_BANKS = 4
 MAX_K = 16
 MAX_IDS = 1024
-MATVEC_MAX_TOKENS = 1  # above SMALL_BATCH_TOKENS: experts with more tokens run on the matrix cores
+MATVEC_MAX_TOKENS = 0  # above SMALL_BATCH_TOKENS: every expert with a token runs on the matrix cores
 SMALL_BATCH_TOKENS = 16  # calls of at most this many tokens run every expert on the mat-vec kernels
 
 

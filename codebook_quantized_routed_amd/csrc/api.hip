@@ -153,15 +153,20 @@ moe_status check_ffn_common(const moe_layer *layer, LayerArgs *L, int32_t T, int
 hipError_t launch_gateup(const LayerArgs &L, const float *x, int T, int kprime, const int32_t *sorted_slot,
                          const WorkRec *work, int n_ids, float *h, hipStream_t s) {
   if (dec_path_ok(L, T)) return launch_gateup_dec(L, x, T, kprime, sorted_slot, work, n_ids, h, s);
-  hipError_t err = launch_gateup_gemv(L, x, T, kprime, sorted_slot, work, n_ids, matvec_max_tokens(T), h, s);
-  if (err != hipSuccess) return err;
+  // m(T) = 0: the first set is empty, its kernels are not launched
+  if (matvec_max_tokens(T) > 0) {
+    hipError_t err = launch_gateup_gemv(L, x, T, kprime, sorted_slot, work, n_ids, matvec_max_tokens(T), h, s);
+    if (err != hipSuccess) return err;
+  }
   return launch_gateup_mfma(L, x, T, kprime, sorted_slot, work, n_ids, h, s);
 }
 
 hipError_t launch_down(const LayerArgs &L, const float *h, int T, int kprime, const WorkRec *work, int n_ids, float *y,
                        hipStream_t s) {
-  hipError_t err = launch_down_gemv(L, h, T, kprime, work, n_ids, matvec_max_tokens(T), y, s);
-  if (err != hipSuccess) return err;
+  if (matvec_max_tokens(T) > 0) {
+    hipError_t err = launch_down_gemv(L, h, T, kprime, work, n_ids, matvec_max_tokens(T), y, s);
+    if (err != hipSuccess) return err;
+  }
   return launch_down_mfma(L, h, T, kprime, work, n_ids, y, s);
 }
 

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 10
+#define MOE_ABI_VERSION 11
 #define MOE_MAX_BANKS 4
 #define MOE_MAX_K 16        /* routed experts per token */
 #define MOE_MAX_IDS 1024    /* E + has_shared */
@@ -68,11 +68,12 @@ extern "C" {
  * matrix-core grouped GEMM in tiles of up to MOE_MFMA_TILE_TOKENS tokens (each weight
  * decoded once per tile).  m(T) = T for small batches, T <= MOE_SMALL_BATCH_TOKENS
  * (every expert in the first set: too few tiles would leave most of the GPU idle), else
- * MOE_MATVEC_MAX_TOKENS.  For 2 to 8 tokens and inter <= 512, gate / up of the first set
- * runs instead on a matrix-core decode kernel that decodes each weight once per call
- * into fragments the expert's tokens share.  The work list written by moe_route_group
- * keeps the two sets apart. */
-#define MOE_MATVEC_MAX_TOKENS 1
+ * MOE_MATVEC_MAX_TOKENS = 0: above it every expert with a token runs on the matrix
+ * cores, and the mat-vec kernels are not launched.  For 2 to 8 tokens and inter <= 512,
+ * gate / up of the first set runs instead on a matrix-core decode kernel that decodes
+ * each weight once per call into fragments the expert's tokens share.  The work list
+ * written by moe_route_group keeps the two sets apart. */
+#define MOE_MATVEC_MAX_TOKENS 0
 #define MOE_SMALL_BATCH_TOKENS 16
 #define MOE_MFMA_TILE_TOKENS 16
 

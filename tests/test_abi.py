@@ -56,7 +56,7 @@ def test_binding_constants_match_header():
 
 
 def test_version_strings_sizes():
-    assert moe.abi_version() == 10
+    assert moe.abi_version() == 11
     for st in moe.STATUS:
         assert lib.moe_status_string(st)
     assert moe.grids_bytes() >= 512 * 8 + 2048 * 8
