@@ -29,6 +29,7 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMfPass = 16;              // token columns per pass (one 16-column tile)
+constexpr int kDownGroupsPerCu = 1;      // down workgroups per compute unit, at least, when blocks are merged
 static_assert(kMfPass == MOE_MFMA_TILE_TOKENS, "a tile of the work list is one pass");
 constexpr int kMfTiles = 4;              // 16-row tiles per wave
 constexpr int kXRow = 256 + 8;           // halves per staged column (16 bytes of padding)
@@ -153,6 +154,36 @@ __device__ __forceinline__ void stage_store(const XRegs &x, _Float16 *xhi, _Floa
   dl[1] = u32x4{lo[4], lo[5], lo[6], lo[7]};
 }
 
+// One super-block step of the wave's kMfTiles row tiles (codes tc) against the staged
+// activations (xhi, xlo): 8 k-steps of two MFMAs per tile (hi and lo halves), the
+// super-block's sums scaled by the rows' d / 8 and added into Ct.
+template <int QT>
+__device__ __forceinline__ void mfma_step(const TileCodes (&tc)[kMfTiles], const _Float16 *xhi, const _Float16 *xlo,
+                                          const uint8_t *lds, const TableLayout &TL, int qd, int lr,
+                                          f4 (&Ct)[kMfTiles]) {
+  f4 Cs[kMfTiles];
+#pragma unroll
+  for (int t = 0; t < kMfTiles; t++) Cs[t] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int ks = 0; ks < 8; ks++) {
+    const int koff = lr * kXRow + (8 * qd + ks) * 8;
+    const h8 bh = *(const h8 *)(xhi + koff), bl = *(const h8 *)(xlo + koff);
+#pragma unroll
+    for (int t = 0; t < kMfTiles; t++) {
+      const h8 A = decode_a<QT>(tc[t], ks, qd, lds, TL);
+      Cs[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bh, Cs[t], 0, 0, 0);
+      Cs[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bl, Cs[t], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < kMfTiles; t++) {
+    float df[4];
+    c_row_factors(tc[t], qd, df);
+#pragma unroll
+    for (int i = 0; i < 4; i++) Ct[t][i] = fmaf(Cs[t][i], df[i], Ct[t][i]);
+  }
+}
+
 // One pass: the wave's kMfTiles row tiles times the pass's (up to) 16 staged columns,
 // over the K range [0, cols) in super-blocks.  Super-block sb + 1's activations, codes
 // and scales are loaded while sb is computed; the staged activations alternate
@@ -187,27 +218,7 @@ __device__ __forceinline__ void mfma_pass(const QMat (&mats)[kMfTiles], const in
 #pragma unroll
       for (int t = 0; t < kMfTiles; t++) nx[t] = load_tile_codes<QT>(mats[t], cols, trow[t] + lr, sb + 1, qd);
     }
-    f4 Cs[kMfTiles];
-#pragma unroll
-    for (int t = 0; t < kMfTiles; t++) Cs[t] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int ks = 0; ks < 8; ks++) {
-      const int koff = lr * kXRow + (8 * qd + ks) * 8;
-      const h8 bh = *(const h8 *)(xhi + koff), bl = *(const h8 *)(xlo + koff);
-#pragma unroll
-      for (int t = 0; t < kMfTiles; t++) {
-        const h8 A = decode_a<QT>(tc[t], ks, qd, lds, TL);
-        Cs[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bh, Cs[t], 0, 0, 0);
-        Cs[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bl, Cs[t], 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < kMfTiles; t++) {
-      float df[4];
-      c_row_factors(tc[t], qd, df);
-#pragma unroll
-      for (int i = 0; i < 4; i++) Ct[t][i] = fmaf(Cs[t][i], df[i], Ct[t][i]);
-    }
+    mfma_step<QT>(tc, xhi, xlo, lds, TL, qd, lr, Ct);
     if (more) {
       _Float16 *nh = xbuf + ((sb + 1) & 1) * 2 * kXHalves;
       stage_store(xn, nh, nh + kXHalves);
@@ -323,23 +334,102 @@ __device__ __forceinline__ void down_tile(const LayerArgs &L, const float *__res
   }
 }
 
+// down for inter <= 512 (at most two super-blocks, which the two staging buffers hold
+// at once): a workgroup = (tile W, row blocks rb0 .. rb0 + nrb - 1 of 256 rows of
+// hidden).  The tile's h is staged once, with the grid tables; then the row blocks run
+// one after the other with no barrier (the staged h is only read), each step's codes
+// loaded during the previous step, the first block's with the staging.
+template <int QT>
+__device__ __forceinline__ void down_tile_resident(const LayerArgs &L, const float *__restrict__ h, const WorkRec &W,
+                                                   const BankArgs &B, int rb0, int nrb, const TableLayout &TL,
+                                                   uint8_t *lds, float *__restrict__ y) {
+  const int H = L.hidden, I = L.inter, nsb = I >> 8;
+  _Float16 *xbuf = (_Float16 *)(lds + TL.bytes);
+  const TableRegs tr = tables_load(L.grids, QT);
+  const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6), qd = lane >> 4, lr = lane & 15;
+  const QMat Wd = expert_mat(B, W.e, kDown, H, I);
+  const QMat mats[kMfTiles] = {Wd, Wd, Wd, Wd};
+  const int n = min(kMfPass, W.p1 - W.p0), c = threadIdx.x >> 4;
+  const int my_row = c < n ? W.p0 + c : -1;
+  TileCodes tc[kMfTiles];
+#pragma unroll
+  for (int t = 0; t < kMfTiles; t++) tc[t] = load_tile_codes<QT>(Wd, I, rb0 * 256 + wave * 64 + 16 * t + lr, 0, qd);
+  const XRegs x0 = stage_load(h, I, my_row, 0);
+  XRegs x1;
+  if (nsb > 1) x1 = stage_load(h, I, my_row, 256);
+  tables_store(tr, QT, TL, lds, threadIdx.x, blockDim.x, false);
+  stage_store(x0, xbuf, xbuf + kXHalves);
+  if (nsb > 1) stage_store(x1, xbuf + 2 * kXHalves, xbuf + 3 * kXHalves);
+  __syncthreads();
+  for (int r = 0; r < nrb; r++) {
+    const int r0 = (rb0 + r) * 256 + wave * 64;
+    f4 Ct[kMfTiles];
+#pragma unroll
+    for (int t = 0; t < kMfTiles; t++) Ct[t] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int sb = 0; sb < nsb; sb++) {
+      // the next step: super-block sb + 1 of this block, else super-block 0 of the next
+      const bool more = sb + 1 < nsb || r + 1 < nrb;
+      const int nsbi = sb + 1 < nsb ? sb + 1 : 0, nr0 = sb + 1 < nsb ? r0 : r0 + 256;
+      TileCodes nx[kMfTiles];
+      if (more) {
+#pragma unroll
+        for (int t = 0; t < kMfTiles; t++) nx[t] = load_tile_codes<QT>(mats[t], I, nr0 + 16 * t + lr, nsbi, qd);
+      }
+      const _Float16 *xhi = xbuf + sb * 2 * kXHalves, *xlo = xhi + kXHalves;
+      mfma_step<QT>(tc, xhi, xlo, lds, TL, qd, lr, Ct);
+      if (more) {
+#pragma unroll
+        for (int t = 0; t < kMfTiles; t++) tc[t] = nx[t];
+      }
+    }
+    if (lr < n) {
+#pragma unroll
+      for (int t = 0; t < kMfTiles; t++)
+        *(float4 *)(y + (size_t)(W.p0 + lr) * H + r0 + 16 * t + 4 * qd) =
+            make_float4(Ct[t][0], Ct[t][1], Ct[t][2], Ct[t][3]);
+    }
+  }
+}
+
+// Row blocks per workgroup (inter <= 512; else 1, one block per workgroup with h staged
+// super-block by super-block): the most, down to 1, that still give at least
+// min_groups workgroups for the call's tiles (read from the work list, so the choice
+// follows the routing: many small tiles take whole columns of blocks, a few large
+// experts keep the grid filled).  The grid has one workgroup per (tile bound, block);
+// the workgroups past the chosen layout return at once.
 template <int FMT>
 __global__ void __launch_bounds__(256) k_down_mfma(LayerArgs L, const float *__restrict__ h,
-                                                   const WorkRec *__restrict__ work, int n_ids,
+                                                   const WorkRec *__restrict__ work, int n_ids, int min_groups,
                                                    float *__restrict__ y) {
   extern __shared__ __align__(16) uint8_t lds[];
-  const int RB = L.hidden / 256;
-  const int a = blockIdx.x / RB, rb = blockIdx.x - a * RB;
-  if (a >= sload(&work[0].slot0)) return;
+  const int rbs = L.hidden / 256, n_tiles = sload(&work[0].slot0);
+  int nrb = 1;
+  if (L.inter <= 512) {
+    nrb = rbs;
+    while (nrb > 1 && n_tiles * (rbs / nrb) < min_groups) nrb >>= 1;
+  }
+  const int RB = rbs / nrb;
+  const int a = blockIdx.x / RB, rb = (blockIdx.x - a * RB) * nrb;
+  if (a >= n_tiles) return;
   const WorkRec W = mfma_tile(work, n_ids, a);
   const BankArgs &B = bank_of(L, W.e);
   const TableLayout TL = table_layout(FMT);
+  const bool resident = L.inter <= 512;
   if constexpr (FMT == MOE_Q_IQ2XS_LIKE || FMT == MOE_Q_IQ1M_LIKE) {
-    down_tile<FMT>(L, h, W, B, rb, TL, lds, y);
+    if (resident)
+      down_tile_resident<FMT>(L, h, W, B, rb, nrb, TL, lds, y);
+    else
+      down_tile<FMT>(L, h, W, B, rb, TL, lds, y);
   } else if (B.qtype == MOE_Q_IQ2XS_LIKE) {
-    down_tile<MOE_Q_IQ2XS_LIKE>(L, h, W, B, rb, TL, lds, y);
+    if (resident)
+      down_tile_resident<MOE_Q_IQ2XS_LIKE>(L, h, W, B, rb, nrb, TL, lds, y);
+    else
+      down_tile<MOE_Q_IQ2XS_LIKE>(L, h, W, B, rb, TL, lds, y);
   } else {
-    down_tile<MOE_Q_IQ1M_LIKE>(L, h, W, B, rb, TL, lds, y);
+    if (resident)
+      down_tile_resident<MOE_Q_IQ1M_LIKE>(L, h, W, B, rb, nrb, TL, lds, y);
+    else
+      down_tile<MOE_Q_IQ1M_LIKE>(L, h, W, B, rb, TL, lds, y);
   }
 }
 
@@ -367,8 +457,12 @@ hipError_t launch_down_mfma(const LayerArgs &L, const float *h, int T, int kprim
                             float *y, hipStream_t s) {
   const long n = max_mfma_tiles(T, kprime, n_ids);
   if (n == 0) return hipSuccess;
+  int dev = 0, cus = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (err != hipSuccess) return err;
   const dim3 grid((unsigned)(n * (L.hidden / 256)));
-  MOE_MFMA_FMT(k_down_mfma, L, h, work, n_ids, y);
+  MOE_MFMA_FMT(k_down_mfma, L, h, work, n_ids, kDownGroupsPerCu * cus, y);
   return hipGetLastError();
 }
 #undef MOE_MFMA_FMT
