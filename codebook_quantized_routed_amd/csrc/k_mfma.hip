@@ -349,45 +349,48 @@ __device__ __forceinline__ void down_tile_resident(const LayerArgs &L, const flo
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6), qd = lane >> 4, lr = lane & 15;
   const QMat Wd = expert_mat(B, W.e, kDown, H, I);
   const QMat mats[kMfTiles] = {Wd, Wd, Wd, Wd};
-  const int n = min(kMfPass, W.p1 - W.p0), c = threadIdx.x >> 4;
-  const int my_row = c < n ? W.p0 + c : -1;
-  TileCodes tc[kMfTiles];
+  for (int pp = W.p0; pp < W.p1; pp += kMfPass) {
+    const int n = min(kMfPass, W.p1 - pp), c = threadIdx.x >> 4;
+    const int my_row = c < n ? pp + c : -1;
+    TileCodes tc[kMfTiles];
 #pragma unroll
-  for (int t = 0; t < kMfTiles; t++) tc[t] = load_tile_codes<QT>(Wd, I, rb0 * 256 + wave * 64 + 16 * t + lr, 0, qd);
-  const XRegs x0 = stage_load(h, I, my_row, 0);
-  XRegs x1;
-  if (nsb > 1) x1 = stage_load(h, I, my_row, 256);
-  tables_store(tr, QT, TL, lds, threadIdx.x, blockDim.x, false);
-  stage_store(x0, xbuf, xbuf + kXHalves);
-  if (nsb > 1) stage_store(x1, xbuf + 2 * kXHalves, xbuf + 3 * kXHalves);
-  __syncthreads();
-  for (int r = 0; r < nrb; r++) {
-    const int r0 = (rb0 + r) * 256 + wave * 64;
-    f4 Ct[kMfTiles];
+    for (int t = 0; t < kMfTiles; t++) tc[t] = load_tile_codes<QT>(Wd, I, rb0 * 256 + wave * 64 + 16 * t + lr, 0, qd);
+    const XRegs x0 = stage_load(h, I, my_row, 0);
+    XRegs x1;
+    if (nsb > 1) x1 = stage_load(h, I, my_row, 256);
+    if (pp == W.p0) tables_store(tr, QT, TL, lds, threadIdx.x, blockDim.x, false);
+    stage_store(x0, xbuf, xbuf + kXHalves);
+    if (nsb > 1) stage_store(x1, xbuf + 2 * kXHalves, xbuf + 3 * kXHalves);
+    __syncthreads();
+    for (int r = 0; r < nrb; r++) {
+      const int r0 = (rb0 + r) * 256 + wave * 64;
+      f4 Ct[kMfTiles];
 #pragma unroll
-    for (int t = 0; t < kMfTiles; t++) Ct[t] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int sb = 0; sb < nsb; sb++) {
-      // the next step: super-block sb + 1 of this block, else super-block 0 of the next
-      const bool more = sb + 1 < nsb || r + 1 < nrb;
-      const int nsbi = sb + 1 < nsb ? sb + 1 : 0, nr0 = sb + 1 < nsb ? r0 : r0 + 256;
-      TileCodes nx[kMfTiles];
-      if (more) {
+      for (int t = 0; t < kMfTiles; t++) Ct[t] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int sb = 0; sb < nsb; sb++) {
+        // the next step: super-block sb + 1 of this block, else super-block 0 of the next
+        const bool more = sb + 1 < nsb || r + 1 < nrb;
+        const int nsbi = sb + 1 < nsb ? sb + 1 : 0, nr0 = sb + 1 < nsb ? r0 : r0 + 256;
+        TileCodes nx[kMfTiles];
+        if (more) {
 #pragma unroll
-        for (int t = 0; t < kMfTiles; t++) nx[t] = load_tile_codes<QT>(mats[t], I, nr0 + 16 * t + lr, nsbi, qd);
+          for (int t = 0; t < kMfTiles; t++) nx[t] = load_tile_codes<QT>(mats[t], I, nr0 + 16 * t + lr, nsbi, qd);
+        }
+        const _Float16 *xhi = xbuf + sb * 2 * kXHalves, *xlo = xhi + kXHalves;
+        mfma_step<QT>(tc, xhi, xlo, lds, TL, qd, lr, Ct);
+        if (more) {
+#pragma unroll
+          for (int t = 0; t < kMfTiles; t++) tc[t] = nx[t];
+        }
       }
-      const _Float16 *xhi = xbuf + sb * 2 * kXHalves, *xlo = xhi + kXHalves;
-      mfma_step<QT>(tc, xhi, xlo, lds, TL, qd, lr, Ct);
-      if (more) {
+      if (lr < n) {
 #pragma unroll
-        for (int t = 0; t < kMfTiles; t++) tc[t] = nx[t];
+        for (int t = 0; t < kMfTiles; t++)
+          *(float4 *)(y + (size_t)(pp + lr) * H + r0 + 16 * t + 4 * qd) =
+              make_float4(Ct[t][0], Ct[t][1], Ct[t][2], Ct[t][3]);
       }
     }
-    if (lr < n) {
-#pragma unroll
-      for (int t = 0; t < kMfTiles; t++)
-        *(float4 *)(y + (size_t)(W.p0 + lr) * H + r0 + 16 * t + 4 * qd) =
-            make_float4(Ct[t][0], Ct[t][1], Ct[t][2], Ct[t][3]);
-    }
+    __syncthreads();  // the next pass restages h
   }
 }
 
