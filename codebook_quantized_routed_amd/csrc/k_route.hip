@@ -59,14 +59,12 @@ __device__ __forceinline__ int4 block_exclusive_scan4(int4 v, GroupLds &S) {
                              wave_inclusive_scan(v.w));
   if (lane == 63) S.wave_tot[wave] = inc;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int4 run = make_int4(0, 0, 0, 0);
-    for (int i = 0; i < kGroupWaves; i++) {
-      const int4 c = S.wave_tot[i];
-      S.wave_tot[i] = run;
-      run.x += c.x, run.y += c.y, run.z += c.z, run.w += c.w;
-    }
-    S.total = run;
+  if (threadIdx.x < 64) {  // the wave totals scanned by wave 0, lane i holding wave i's
+    const int4 c = lane < kGroupWaves ? S.wave_tot[lane] : make_int4(0, 0, 0, 0);
+    const int4 ic = make_int4(wave_inclusive_scan(c.x), wave_inclusive_scan(c.y), wave_inclusive_scan(c.z),
+                              wave_inclusive_scan(c.w));
+    if (lane < kGroupWaves) S.wave_tot[lane] = make_int4(ic.x - c.x, ic.y - c.y, ic.z - c.z, ic.w - c.w);
+    if (lane == kGroupWaves - 1) S.total = ic;
   }
   __syncthreads();
   const int4 b = S.wave_tot[wave];
@@ -92,14 +90,13 @@ __device__ void group_block(const int32_t *ids, int n, int n_ids, int max_narrow
   }
   __syncthreads();
   const int e = threadIdx.x;  // n_ids <= MOE_MAX_IDS == blockDim.x
-  int c = 0;
-  if (e < n_ids) {
-    for (int w = 0; w < nw; w++) {
-      int h = S.hist[w][e];
-      S.hist[w][e] = c;
-      c += h;
-    }
-  }
+  // the expert's count per wave (rows past nw were not cleared: not counted), all read
+  // before any is used
+  int hv[kGroupWaves], c = 0;
+#pragma unroll
+  for (int w = 0; w < kGroupWaves; w++) hv[w] = S.hist[w][e];
+#pragma unroll
+  for (int w = 0; w < kGroupWaves; w++) c += (w < nw && e < n_ids) ? hv[w] : 0;
   const bool wide = c > max_narrow;
   const int tiles = wide ? (c + MOE_MFMA_TILE_TOKENS - 1) / MOE_MFMA_TILE_TOKENS : 0;
   // slots, mat-vec experts, matrix-core experts, tiles
@@ -126,9 +123,16 @@ __device__ void group_block(const int32_t *ids, int n, int n_ids, int max_narrow
     offsets[n_ids] = n_total;
     work[0] = WorkRec{n_narrow, n_total, n_wide, n_tiles};
   }
-  __syncthreads();
-  if (e < n_ids)
-    for (int w = 0; w < nw; w++) S.hist[w][e] += S.offs[e];
+  if (e < n_ids) {  // each wave's first position for the expert
+    int run = excl;
+#pragma unroll
+    for (int w = 0; w < kGroupWaves; w++) {
+      if (w < nw) {
+        S.hist[w][e] = run;
+        run += hv[w];
+      }
+    }
+  }
   __syncthreads();
 
   for (int base = lo; base < hi; base += 64) {
