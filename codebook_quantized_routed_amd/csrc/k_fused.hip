@@ -378,13 +378,14 @@ struct RouteLds {
   float w[kFusedMaxSlots];
   int32_t slot_at[kFusedMaxSlots];
   int32_t pos_of[kFusedMaxSlots];
+  float wpos[kFusedMaxSlots];  // sorted position -> router weight
 };
 
 struct StackLds {
   BankLds banks[2][MOE_MAX_BANKS];  // this layer's and the next layer's
   RouteLds route[2];
   TopkLds topk;
-  float ydot[kFusedMaxSlots][16];
+  float ydot[kFusedMaxSlots][16];   // down outputs of the block's rows, per sorted position
   float hres[2048];                 // the layer's input residual
   float xs[64 * kXsRow];            // the same values, lane l's 32 at l * kXsRow (no bank conflicts)
   float part[8];
@@ -399,12 +400,14 @@ __device__ inline void route_wave(const float *logits, const LayerArgs &L, int E
   const TopkVals<8> tv = topk_load<8>(logits, E);
   // positions by counting, not the ones the top-k returns: with those, this kernel (at
   // its register limit) was scheduled 8 % slower
-  const int my = topk_select<8, 2, 16>(tv, E, k, add_shared, ids_out, w_out, R.ids, R.w, T).id;
+  const TopkSlot ts = topk_select<8, 2, 16>(tv, E, k, add_shared, ids_out, w_out, R.ids, R.w, T);
+  const int my = ts.id;
   const int rank = slot_rank(my, lane);
   if (lane < kprime) {
     R.pos_of[lane] = rank;
     R.slot_at[rank] = lane;
     R.pos[rank] = PosRec{my, lane, bank_index(L, my), 0};
+    R.wpos[rank] = ts.w;
   }
 }
 
@@ -552,7 +555,7 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_stack_decode(
         const float *hrow = hs + lq * kChunkPad;
         const float v = qt == MOE_Q_IQ2XS_LIKE ? down_slot_dot<MOE_Q_IQ2XS_LIKE, LPR>(Rw, hrow, lq, lds, TL)
                                                : down_slot_dot<MOE_Q_IQ1M_LIKE, LPR>(Rw, hrow, lq, lds, TL);
-        if (lq == 0) S.ydot[j][sub] = v;
+        if (lq == 0) S.ydot[pj][sub] = v;
         __builtin_amdgcn_wave_barrier();  // the staging area is reused by the next slot
       }
       __syncthreads();
@@ -561,10 +564,7 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_stack_decode(
       if (tid < RPP) {
         const int r = tile * RPP + tid;
         float a = S.hres[r];
-        for (int p = 0; p < kprime; p++) {
-          const int j = R.slot_at[p];
-          a = __fadd_rn(a, __fmul_rn(R.w[j], S.ydot[j][tid]));
-        }
+        for (int p = 0; p < kprime; p++) a = __fadd_rn(a, __fmul_rn(R.wpos[p], S.ydot[p][tid]));
         if (l + 1 < n_layers)
           __hip_atomic_store(rp + (size_t)l * H + r, ((uint64_t)tag << 32) | __float_as_uint(a), __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
