@@ -525,3 +525,30 @@ def test_rmsnorm_matches_oracle():
     hd = dev(h)
     moe.rmsnorm(hd, 33, 2048, 1e-6, hd)  # in place
     np.testing.assert_array_equal(hd.cpu().numpy(), out.cpu().numpy())
+
+
+@pytest.mark.parametrize("qt", [IQ2, IQ1])
+def test_tile_longer_than_one_pass(grids, ogrids, qt):
+    """A caller's work list may hold a matrix-core tile of more than 16 tokens (the
+    grouping never writes one): both tile kernels then run it in passes of 16.  One tile
+    of 40 tokens of expert 3, built by hand; every token's y against the oracle's FFN."""
+    T, E, H, I, e = 40, 8, 2048, 512, 3
+    log(f"tile of {T} tokens, format {qt}")
+    sl = synth.make_layer([(qt, E)], hidden=H, inter=I, n_experts=E, has_shared=0, tag=f"L/longtile/{qt}")
+    dl = device_layer(sl, grids)
+    tab = O.ExpertTable(sl)
+    x = synth.activations(T, H, tag=f"longtile/{qt}/x")
+    n_ids = E
+    work = np.zeros(moe.work_ints(T, 1, n_ids), np.int32).reshape(-1, 4)
+    work[0] = [0, T, 1, 1]               # no mat-vec expert, T slots, one expert, one tile
+    work[n_ids + 1] = [e, 0, T, 0]       # the tile: expert e, sorted positions 0 .. T
+    ss = dev(np.arange(T, dtype=np.int32))  # one slot per token, already in order
+    h = torch.zeros((T, I), dtype=torch.float32, device="cuda")
+    y = torch.zeros((T, H), dtype=torch.float32, device="cuda")
+    wk = dev(work.reshape(-1))
+    xd = dev(x)
+    moe.expert_gateup_q(dl.desc, xd, T, 1, ss, wk, h)
+    moe.expert_down_q(dl.desc, h, T, 1, wk, y)
+    torch.cuda.synchronize()
+    ref = np.stack([O.expert_ffn(tab, e, ogrids, x[t]) for t in range(T)])
+    assert_rows_close(y.cpu().numpy(), ref, f"tile of {T} tokens, format {qt}")
