@@ -71,6 +71,64 @@ __device__ __forceinline__ TileCodes load_tile_codes(const QMat &m, int cols, in
   return t;
 }
 
+// The small per-super-block words of the lane's row for the super-block pair p0, p0 + 1
+// (p0 = 2 qd, clamped to the row's last pair): IQ2 x, y = the two scale words, z = the
+// two d halves; IQ1 x, y and z, w = the two sd words.  Loaded once per pass (whole pair
+// per lane, so the lines of these streams are read once instead of once per step); step
+// sb takes its words from lane lr + 16 (sb / 2) with two lane shuffles.  Needs at least
+// two super-blocks per row.
+template <int QT>
+__device__ __forceinline__ uint4 load_tile_small(const QMat &m, int cols, int row, int qd) {
+  const uint32_t nb = cols >> 8, p0 = min(2 * qd, (int)nb - 2), blk = row * nb + p0;
+  uint4 v;
+  if constexpr (QT == MOE_Q_IQ2XS_LIKE) {
+    const uint2 sc = *(const uint2 *)(m.s1 + (uint32_t)(blk * 4));
+    v = make_uint4(sc.x, sc.y, *(const uint32_t *)(m.s2 + (uint32_t)(blk * 2)), 0u);
+  } else {
+    v = *(const uint4 *)(m.s2 + (uint32_t)(blk * 8));
+  }
+  return v;
+}
+
+// The codes of one step without the small words (filled by fill_tile_small).
+template <int QT>
+__device__ __forceinline__ TileCodes load_tile_codes_only(const QMat &m, int cols, int row, int sb, int qd) {
+  const uint32_t ng = cols >> 3, g0 = sb * 32 + 8 * qd;
+  TileCodes t;
+  if constexpr (QT == MOE_Q_IQ2XS_LIKE) {
+    t.c = *(const uint4 *)(m.s0 + (uint32_t)((row * ng + g0) * 2));
+  } else {
+    const uint2 ql = *(const uint2 *)(m.s0 + (uint32_t)(row * ng + g0));
+    const uint32_t qh = *(const uint32_t *)(m.s1 + (uint32_t)(row * (ng / 2) + g0 / 2));
+    t.c = make_uint4(ql.x, ql.y, qh, 0u);
+  }
+  t.s = 0u;
+  t.d = 0u;
+  return t;
+}
+
+// Step sb's small words of the lane's row, from the lane holding that super-block's pair.
+// The word of the pair is picked arithmetically (a select on sb & 1 was compiled into an
+// indexed access to a stack copy of the words).
+__device__ __forceinline__ uint32_t pick(uint32_t a, uint32_t b, uint32_t odd) { return a ^ ((a ^ b) & (0u - odd)); }
+
+template <int QT>
+__device__ __forceinline__ void fill_tile_small(TileCodes &t, const uint4 &sm, int sb, int lr) {
+  const int src = lr + 16 * (sb >> 1);
+  const uint32_t odd = (uint32_t)sb & 1u;
+  if constexpr (QT == MOE_Q_IQ2XS_LIKE) {
+    t.s = (uint32_t)__shfl((int)pick(sm.x, sm.y, odd), src, 64);
+    const uint32_t dd = (uint32_t)__shfl((int)sm.z, src, 64);
+    t.d = (dd >> (16u * odd)) & 0xFFFFu;
+  } else {
+    const uint32_t lo = (uint32_t)__shfl((int)pick(sm.x, sm.z, odd), src, 64);
+    const uint32_t hi = (uint32_t)__shfl((int)pick(sm.y, sm.w, odd), src, 64);
+    t.c.w = lo;
+    t.s = hi;
+    t.d = lo & 0xFFFFu;
+  }
+}
+
 // d / 8 of the lane's four C rows 4 qd + i of a tile, taken from the lanes that hold
 // those rows' codes (lane j holds row j % 16).
 __device__ __forceinline__ void c_row_factors(const TileCodes &t, int qd, float (&df)[4]) {
@@ -192,7 +250,7 @@ __device__ __forceinline__ void mfma_step(const TileCodes (&tc)[kMfTiles], const
 // store_tables, the grid tables (whose compact rows tr the caller loaded first) are
 // expanded into LDS after the first super-block's codes and activations are requested,
 // so the three loads travel together.
-template <int QT>
+template <int QT, bool SMALL = false>
 __device__ __forceinline__ void mfma_pass(const QMat (&mats)[kMfTiles], const int (&trow)[kMfTiles], int cols,
                                           const float *xbase, int x_stride, int my_row, const TableRegs &tr,
                                           bool store_tables, uint8_t *lds, const TableLayout &TL, _Float16 *xbuf,
@@ -201,9 +259,18 @@ __device__ __forceinline__ void mfma_pass(const QMat (&mats)[kMfTiles], const in
   const int nsb = cols >> 8;
 #pragma unroll
   for (int t = 0; t < kMfTiles; t++) Ct[t] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+  // SMALL: the rows' small words once for the pass, the steps load only the codes
+  uint4 sm[kMfTiles];
   TileCodes tc[kMfTiles];
 #pragma unroll
-  for (int t = 0; t < kMfTiles; t++) tc[t] = load_tile_codes<QT>(mats[t], cols, trow[t] + lr, 0, qd);
+  for (int t = 0; t < kMfTiles; t++) {
+    if constexpr (SMALL) {
+      sm[t] = load_tile_small<QT>(mats[t], cols, trow[t] + lr, qd);
+      tc[t] = load_tile_codes_only<QT>(mats[t], cols, trow[t] + lr, 0, qd);
+    } else {
+      tc[t] = load_tile_codes<QT>(mats[t], cols, trow[t] + lr, 0, qd);
+    }
+  }
   const XRegs x0 = stage_load(xbase, x_stride, my_row, 0);
   if (store_tables) tables_store(tr, QT, TL, lds, threadIdx.x, blockDim.x, false);
   stage_store(x0, xbuf, xbuf + kXHalves);
@@ -216,7 +283,13 @@ __device__ __forceinline__ void mfma_pass(const QMat (&mats)[kMfTiles], const in
     if (more) {
       xn = stage_load(xbase, x_stride, my_row, (sb + 1) * 256);
 #pragma unroll
-      for (int t = 0; t < kMfTiles; t++) nx[t] = load_tile_codes<QT>(mats[t], cols, trow[t] + lr, sb + 1, qd);
+      for (int t = 0; t < kMfTiles; t++)
+        nx[t] = SMALL ? load_tile_codes_only<QT>(mats[t], cols, trow[t] + lr, sb + 1, qd)
+                      : load_tile_codes<QT>(mats[t], cols, trow[t] + lr, sb + 1, qd);
+    }
+    if constexpr (SMALL) {
+#pragma unroll
+      for (int t = 0; t < kMfTiles; t++) fill_tile_small<QT>(tc[t], sm[t], sb, lr);
     }
     mfma_step<QT>(tc, xhi, xlo, lds, TL, qd, lr, Ct);
     if (more) {
@@ -250,7 +323,7 @@ __device__ __forceinline__ int pass_token_row(const int32_t *sorted_slot, int pp
   return j == 0 ? r[0] : (j == 1 ? r[1] : (j == 2 ? r[2] : r[3]));
 }
 
-template <int QT>
+template <int QT, bool SMALL>
 __device__ __forceinline__ void gateup_tile(const LayerArgs &L, const float *__restrict__ x, int kprime,
                                             const int32_t *__restrict__ sorted_slot, const WorkRec &W,
                                             const BankArgs &B, int rb, const TableLayout &TL, uint8_t *lds,
@@ -267,8 +340,8 @@ __device__ __forceinline__ void gateup_tile(const LayerArgs &L, const float *__r
   for (int pp = W.p0; pp < W.p1; pp += kMfPass) {
     const int n = min(kMfPass, W.p1 - pp);
     f4 Ct[kMfTiles];
-    mfma_pass<QT>(mats, trow, H, x, H, pass_token_row(sorted_slot, pp, n, kprime), tr, pp == W.p0, lds, TL, xbuf,
-                  Ct);
+    mfma_pass<QT, SMALL>(mats, trow, H, x, H, pass_token_row(sorted_slot, pp, n, kprime), tr, pp == W.p0, lds, TL,
+                         xbuf, Ct);
     if (lr < n) {
 #pragma unroll
       for (int j = 0; j < 2; j++) {
@@ -284,8 +357,9 @@ __device__ __forceinline__ void gateup_tile(const LayerArgs &L, const float *__r
 }
 
 // One launch for the layer's formats FMT (MOE_Q_* bits): a workgroup runs the format of
-// its tile's expert, so a layer with both formats has one launch and one tail.
-template <int FMT>
+// its tile's expert, so a layer with both formats has one launch and one tail.  SMALL
+// (hidden >= 512): the rows' small per-super-block words are loaded once per pass.
+template <int FMT, bool SMALL>
 __global__ void __launch_bounds__(256) k_gateup_mfma(LayerArgs L, const float *__restrict__ x, int kprime,
                                                      const int32_t *__restrict__ sorted_slot,
                                                      const WorkRec *__restrict__ work, int n_ids,
@@ -298,11 +372,11 @@ __global__ void __launch_bounds__(256) k_gateup_mfma(LayerArgs L, const float *_
   const BankArgs &B = bank_of(L, W.e);
   const TableLayout TL = table_layout(FMT);
   if constexpr (FMT == MOE_Q_IQ2XS_LIKE || FMT == MOE_Q_IQ1M_LIKE) {
-    gateup_tile<FMT>(L, x, kprime, sorted_slot, W, B, rb, TL, lds, h);
+    gateup_tile<FMT, SMALL>(L, x, kprime, sorted_slot, W, B, rb, TL, lds, h);
   } else if (B.qtype == MOE_Q_IQ2XS_LIKE) {
-    gateup_tile<MOE_Q_IQ2XS_LIKE>(L, x, kprime, sorted_slot, W, B, rb, TL, lds, h);
+    gateup_tile<MOE_Q_IQ2XS_LIKE, SMALL>(L, x, kprime, sorted_slot, W, B, rb, TL, lds, h);
   } else {
-    gateup_tile<MOE_Q_IQ1M_LIKE>(L, x, kprime, sorted_slot, W, B, rb, TL, lds, h);
+    gateup_tile<MOE_Q_IQ1M_LIKE, SMALL>(L, x, kprime, sorted_slot, W, B, rb, TL, lds, h);
   }
 }
 
@@ -452,7 +526,19 @@ hipError_t launch_gateup_mfma(const LayerArgs &L, const float *x, int T, int kpr
   const long n = max_mfma_tiles(T, kprime, n_ids);
   if (n == 0) return hipSuccess;
   const dim3 grid((unsigned)(n * (L.inter / 128)));
-  MOE_MFMA_FMT(k_gateup_mfma, L, x, kprime, sorted_slot, work, n_ids, h);
+  const size_t bytes = mfma_lds_bytes(L.formats);
+  const bool small = L.hidden >= 512;
+#define MOE_GU_LAUNCH(F, SM) \
+  hipLaunchKernelGGL((k_gateup_mfma<F, SM>), grid, dim3(256), bytes, s, L, x, kprime, sorted_slot, work, n_ids, h)
+  if (L.formats == MOE_Q_IQ2XS_LIKE) {
+    if (small) MOE_GU_LAUNCH(MOE_Q_IQ2XS_LIKE, true); else MOE_GU_LAUNCH(MOE_Q_IQ2XS_LIKE, false);
+  } else if (L.formats == MOE_Q_IQ1M_LIKE) {
+    if (small) MOE_GU_LAUNCH(MOE_Q_IQ1M_LIKE, true); else MOE_GU_LAUNCH(MOE_Q_IQ1M_LIKE, false);
+  } else {
+    if (small) MOE_GU_LAUNCH(MOE_Q_IQ2XS_LIKE | MOE_Q_IQ1M_LIKE, true);
+    else MOE_GU_LAUNCH(MOE_Q_IQ2XS_LIKE | MOE_Q_IQ1M_LIKE, false);
+  }
+#undef MOE_GU_LAUNCH
   return hipGetLastError();
 }
 
