@@ -72,7 +72,8 @@ k_gateup_dec(LayerArgs L, const float *__restrict__ x, int T, int kprime, const 
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ float xinv[8];
   __shared__ __align__(16) uint32_t wmax[8 * 16];
-  __shared__ int4 uinfo[kDecWaves];        // per unit slot of a round: (active, p0, ntok, rb)
+  __shared__ int4 uinfo[2][kDecWaves];     // per unit slot of a round: (active, p0, ntok, rb), by round parity
+  __shared__ __align__(16) _Float16 zero8[8];  // the A fragment of a missing token
   __shared__ WorkRec recs[kDecMaxSlots + 1];  // the work list's record 0 and first set
   __shared__ int tok_of[kDecMaxSlots];     // sorted position -> token
   const int H = L.hidden, I = L.inter, tid = threadIdx.x;
@@ -103,7 +104,10 @@ k_gateup_dec(LayerArgs L, const float *__restrict__ x, int T, int kprime, const 
   GuUnit<NSB> cur = gu_issue<QT, NSB>(L, load_work(work, 1 + a0), u - a0 * rbs, u < total, kp);
   const int XR = stage_row_halves(H);
   _Float16 *xs = (_Float16 *)(lds + D.bytes);
-  float *red = (float *)(xs + (size_t)2 * T * XR);  // [UPR][KP][8 tokens][16 columns]
+  // partials [2 (round parity)][UPR][KP][8 tokens][16 columns]: a round writes one half
+  // while the previous round's epilogue may still read the other, so one barrier a round
+  float *red = (float *)(xs + (size_t)2 * T * XR);
+  if (tid < 8) zero8[tid] = (_Float16)0.0f;
   // unconditional stores (a conditional one lets the compiler move the load into the
   // branch, where it waits for every older load): threads past the counts write
   // entries never read, or at the clamped last index the value that entry holds
@@ -146,25 +150,28 @@ k_gateup_dec(LayerArgs L, const float *__restrict__ x, int T, int kprime, const 
     const WorkRec Wn{uniform(recs[1 + an].e), uniform(recs[1 + an].p0), uniform(recs[1 + an].p1), 0};
     return gu_issue<QT, NSB>(L, Wn, uu - an * rbs, uu < total, kp);
   };
-  // one round: the unit's partials, then the parts added in order and h written
-  auto round = [&](const GuUnit<NSB> &U) __attribute__((always_inline)) {
+  // one round: the unit's partials, then the parts added in order and h written; buf
+  // (the round's parity) picks the half of the partials and unit information
+  auto round = [&](const GuUnit<NSB> &U, int buf) __attribute__((always_inline)) {
+    float *redb = red + (size_t)buf * UPR * KP * 8 * 16;
     if (U.active) {
       const int ti = n >> 1;
       const int arow = ti < U.ntok ? 2 * tok_of[U.p0 + ti] + (n & 1) : -1;
       float r0 = 0.0f, r1 = 0.0f;
-      dot_sb<QT, SB>(U.c, kp * SB, xs, XR, arow, q, lds, D, r0, r1);
-      float *rp = red + (size_t)(us * KP + kp) * 8 * 16;
+      dot_sb<QT, SB>(U.c, kp * SB, xs, XR, arow, q, lds, D, zero8, r0, r1);
+      float *rp = redb + (size_t)(us * KP + kp) * 8 * 16;
       if (2 * q < U.ntok) rp[(2 * q) * 16 + n] = r0;
       if (2 * q + 1 < U.ntok) rp[(2 * q + 1) * 16 + n] = r1;
     }
-    if (kp == 0 && lane == 0) uinfo[us] = make_int4(U.active, U.p0, U.ntok, U.rb);
+    if (kp == 0 && lane == 0) uinfo[buf][us] = make_int4(U.active, U.p0, U.ntok, U.rb);
     lds_barrier();
-    // epilogue: thread (unit slot, token i, row r) adds the parts in order
+    // epilogue: thread (unit slot, token i, row r) adds the parts in order; the next
+    // round writes the other half, so no barrier follows
     const int us2 = tid >> 6, i = (tid >> 3) & 7, r = tid & 7;
     if (us2 < UPR) {
-      const int4 inf = uinfo[us2];
+      const int4 inf = uinfo[buf][us2];
       if (inf.x && i < inf.z) {
-        const float *rp = red + (size_t)us2 * KP * 8 * 16 + i * 16;
+        const float *rp = redb + (size_t)us2 * KP * 8 * 16 + i * 16;
         float g = rp[r], vu = rp[8 + r];
         for (int p = 1; p < KP; p++) {
           g += rp[p * 8 * 16 + r];
@@ -174,18 +181,17 @@ k_gateup_dec(LayerArgs L, const float *__restrict__ x, int T, int kprime, const 
         h[(size_t)(inf.y + i) * I + 8 * inf.w + r] = silu(g * inv) * (vu * inv);
       }
     }
-    lds_barrier();
   };
   // unrolled by two: each unit keeps its own registers while the other's loads travel
   // (a copy of in-flight registers would wait for their loads)
   GuUnit<NSB> nxt;
   for (int rd = 0;;) {
     nxt = issue_ahead(u + stride);
-    round(cur);
+    round(cur, 0);
     if (++rd >= rounds) break;
     u += stride;
     cur = issue_ahead(u + stride);
-    round(nxt);
+    round(nxt, 1);
     if (++rd >= rounds) break;
     u += stride;
   }
@@ -204,7 +210,7 @@ bool dec_path_ok(const LayerArgs &L, int T) { return T >= 2 && T <= kDecMaxToken
 size_t gateup_dec_lds(const LayerArgs &L, int qt, int T) {
   const int H = L.hidden, KP = (H >> 8) >= 2 ? (H >> 8) / 2 : 1, UPR = kDecWaves / KP;
   return dec_tables(qt).bytes + (size_t)2 * T * stage_row_halves(H) * sizeof(_Float16) +
-         (size_t)UPR * KP * 8 * 16 * sizeof(float);
+         (size_t)2 * UPR * KP * 8 * 16 * sizeof(float);
 }
 
 hipError_t launch_gateup_dec(const LayerArgs &L, const float *x, int T, int kprime, const int32_t *sorted_slot,

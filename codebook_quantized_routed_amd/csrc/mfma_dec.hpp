@@ -336,11 +336,12 @@ __device__ __forceinline__ void stage4(_Float16 *hi_row, _Float16 *lo_row, int c
 }
 
 // The A fragment of step s of super-block sb: row m of the fragment is the staged row
-// `row_of_m` (hi or lo of a vector), zero when row_of_m < 0.
-__device__ __forceinline__ h8 load_a(const _Float16 *staged, int row_halves, int row_of_m, int sb, int q, int s) {
-  if (row_of_m < 0) return h8{0, 0, 0, 0, 0, 0, 0, 0};
-  const _Float16 *p = staged + (size_t)row_of_m * row_halves + stage_col(sb * 256 + 64 * q) + 8 * s;
-  return *(const h8 *)p;
+// `row_of_m` (hi or lo of a vector); when row_of_m < 0 it reads the 16 zero bytes at
+// `zero` instead (an address select, not a branch around the read).
+__device__ __forceinline__ h8 load_a(const _Float16 *staged, int row_halves, int row_of_m, int sb, int q, int s,
+                                     const _Float16 *zero) {
+  const _Float16 *p = staged + (size_t)max(row_of_m, 0) * row_halves + stage_col(sb * 256 + 64 * q) + 8 * s;
+  return *(const h8 *)(row_of_m < 0 ? zero : p);
 }
 
 // ----------------------------------------------------------------------------- one row block
@@ -351,8 +352,8 @@ __device__ __forceinline__ h8 load_a(const _Float16 *staged, int row_halves, int
 // vectors 2 (lane / 16) and 2 (lane / 16) + 1.
 template <int QT, int NSB>
 __device__ __forceinline__ void dot_sb(const SbCodes (&c)[NSB], int sb0, const _Float16 *staged, int row_halves,
-                                       int row_of_m, int q, const uint8_t *lds, const DecTables &D, float &r0,
-                                       float &r1) {
+                                       int row_of_m, int q, const uint8_t *lds, const DecTables &D,
+                                       const _Float16 *zero, float &r0, float &r1) {
   f4 acc[NSB];
 #pragma unroll
   for (int i = 0; i < NSB; i++) acc[i] = f4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -360,14 +361,14 @@ __device__ __forceinline__ void dot_sb(const SbCodes (&c)[NSB], int sb0, const _
   // reads of step k + 1 are issued before the MFMA of step k
   StepRaw cur, nxt;
   fetch_b<QT>(c[0], 0, q, lds, D, cur);
-  cur.a = load_a(staged, row_halves, row_of_m, sb0, q, 0);
+  cur.a = load_a(staged, row_halves, row_of_m, sb0, q, 0, zero);
 #pragma unroll
   for (int k = 0; k < 8 * NSB; k++) {
     const int i = k >> 3;
     if (k + 1 < 8 * NSB) {
       const int i1 = (k + 1) >> 3, s1 = (k + 1) & 7;
       fetch_b<QT>(c[i1], s1, q, lds, D, nxt);
-      nxt.a = load_a(staged, row_halves, row_of_m, sb0 + i1, q, s1);
+      nxt.a = load_a(staged, row_halves, row_of_m, sb0 + i1, q, s1, zero);
     }
     acc[i] = mfma16(cur.a, combine_b<QT>(cur), acc[i]);
     cur = nxt;
