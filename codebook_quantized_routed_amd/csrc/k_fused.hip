@@ -182,9 +182,10 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
   // ---- 1. routing, in every workgroup, by wave 0; the other waves expand the grid
   // tables into LDS meanwhile
   if (wave == 0) {
-    TopkSlot ts{0x7FFFFFFF, -1, 0.0f};
     if (logits) {
-      ts = topk_select<8, 1, 16>(tv, E, k, add_shared, blockIdx.x == 0 ? ids : nullptr, w, S.ids, S.w, S.topk);
+      // the selection only: the router weights are needed by the accumulation alone,
+      // so they are computed later, while the wave waits for h
+      topk_choose<8, 1, 16>(tv, E, k, S.topk);
     } else {
       if (lane < k) {
         S.ids[lane] = ids[lane];
@@ -200,16 +201,18 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
       }
     }
     __builtin_amdgcn_wave_barrier();
-    // routed: the slot, its position and weight are still in the lanes; explicit: as
-    // copied to LDS above, positions by counting
-    const int my = logits ? ts.id : (lane < kprime ? S.ids[lane] : 0x7FFFFFFF);
-    const int rank = logits ? ts.pos : slot_rank(my, lane);
-    const float wt = logits ? ts.w : (lane < kprime ? S.w[lane] : 0.0f);
+    // routed: slot j's expert and position as the selection left them (the shared
+    // expert last); explicit: as copied to LDS above, positions by counting
+    const bool shared_lane = add_shared && lane == k;
+    const int my = logits ? (lane < k ? S.topk.sel_id[lane] : (shared_lane ? E : 0x7FFFFFFF))
+                          : (lane < kprime ? S.ids[lane] : 0x7FFFFFFF);
+    const int rank = logits ? (lane < k ? S.topk.sel_pos[lane] : (shared_lane ? k : -1)) : slot_rank(my, lane);
     if (lane < kprime) {
+      if (logits) S.ids[lane] = my;
       S.pos_of[lane] = rank;
       S.slot_at[rank] = lane;
       S.pos[rank] = PosRec{my, lane, bank_index(L, my), 0};
-      S.wpos[rank] = wt;
+      if (!logits) S.wpos[rank] = S.w[lane];
     }
   } else {
     tables_store(tr, formats, TL, lds, threadIdx.x - 64, blockDim.x - 64, false);
@@ -231,15 +234,18 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
   const int item0 = blockIdx.x * kFusedWaves + wave;
   WideItem It;
   int cur_tok = 0;
+  // the bank's bases and sizes come from the kernel arguments (scalar loads), so the
+  // only LDS read before the loads leave is the position's record
   auto issue = [&](int item) {
     const int p = item / ipe;
     const int e = uniform(S.pos[p].e), slot = uniform(S.pos[p].slot);
-    const BankLds &B = S.banks[uniform(S.pos[p].bank)];
+    const BankArgs &B = bank_of(L, e);
     It.W = WorkRec{e, p, p + 1, slot};
+    const QMat Wg = global_mat(expert_mat(B, e, kGate, I, H)), Wu = global_mat(expert_mat(B, e, kUp, I, H));
     if constexpr (FMT == MOE_Q_IQ2XS_LIKE || FMT == MOE_Q_IQ1M_LIKE)
-      wide_issue_fmt<FMT>(It, bank_mat(B, e, kGate), bank_mat(B, e, kUp), H, item - p * ipe, q);
+      wide_issue_fmt<FMT>(It, Wg, Wu, H, item - p * ipe, q);
     else
-      wide_issue_mats(It, bank_mat(B, e, kGate), bank_mat(B, e, kUp), uniform(B.qt), H, item - p * ipe, q);
+      wide_issue_mats(It, Wg, Wu, uniform(B.qtype), H, item - p * ipe, q);
   };
   // the first item's loads leave before the activations are read from LDS (its
   // addresses need only the routing records)
@@ -275,6 +281,12 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
   }
   float acc_in = 0.0f;
   if (threadIdx.x < RPP && tile < tiles) acc_in = acc[tile * RPP + threadIdx.x];
+  // wave 0: the router weights of the selection (the arithmetic of topk_select), read
+  // by the accumulation after the down phase's barrier
+  if (wave == 0 && logits) {
+    const TopkSlot ts = topk_weights(E, k, add_shared, blockIdx.x == 0 ? ids : nullptr, w, nullptr, S.w, S.topk);
+    if (lane < kprime) S.wpos[ts.pos] = ts.w;
+  }
 
   // ---- 4. down + accumulation, block by block of RPP output rows; a wave takes slots
   // wave, wave + kDownWaves, ... one after the other

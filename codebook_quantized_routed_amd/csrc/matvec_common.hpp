@@ -203,6 +203,17 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t v) {
          (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
 }
 
+// The same matrix with its stream bases marked global (loads through them are global
+// loads, which do not count against the LDS wait counter as flat loads would).
+__device__ __forceinline__ QMat global_mat(const QMat &m) {
+  typedef const __attribute__((address_space(1))) uint8_t gbyte;
+  QMat g;
+  g.s0 = (const uint8_t *)(gbyte *)m.s0;
+  g.s1 = (const uint8_t *)(gbyte *)m.s1;
+  g.s2 = (const uint8_t *)(gbyte *)m.s2;
+  return g;
+}
+
 // Matrix w of expert e in bank B (the same bases and offsets as expert_mat), in scalar
 // registers; the bases are marked global again (loads through them are global loads).
 __device__ __forceinline__ QMat bank_mat(const BankLds &B, int e, int w) {

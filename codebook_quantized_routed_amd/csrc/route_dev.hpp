@@ -128,10 +128,12 @@ __device__ __forceinline__ TopkVals<VPL> topk_load(const float *__restrict__ l, 
 // busy waves (the next layer's routing inside the stack kernel).  TAU_LOW: tau's bits
 // below this one are not searched (stay zero); every caller takes 16, measured the
 // faster (or as fast) in each kernel.  The selection is the same.
+//
+// topk_choose makes the selection and leaves it in S: sel_key / sel_id / sel_pos by rank
+// (rank j = slot j; sel_pos = the position in ascending expert id); topk_weights then
+// computes the router weights from it.
 template <int VPL, int TAU_BITS = 1, int TAU_LOW = 0>
-__device__ __forceinline__ TopkSlot topk_select(const TopkVals<VPL> &tv, int E, int k, int add_shared,
-                                            int32_t *__restrict__ ids, float *__restrict__ w, int32_t *ids_copy,
-                                            float *w_copy, TopkLds &S) {
+__device__ __forceinline__ void topk_choose(const TopkVals<VPL> &tv, int E, int k, TopkLds &S) {
   int lane = threadIdx.x & 63;
   asm volatile("" : "+v"(lane));
   uint32_t key[VPL], lmax = 0u;
@@ -206,7 +208,13 @@ __device__ __forceinline__ TopkSlot topk_select(const TopkVals<VPL> &tv, int E, 
     for (int j = 0; j < k; j++) pos += __builtin_amdgcn_readlane(sid, j) < sid ? 1 : 0;
     if (lane < k) S.sel_pos[lane] = pos;
   }
-  __builtin_amdgcn_wave_barrier();
+}
+
+__device__ __forceinline__ TopkSlot topk_weights(int E, int k, int add_shared, int32_t *__restrict__ ids,
+                                                 float *__restrict__ w, int32_t *ids_copy, float *w_copy,
+                                                 const TopkLds &S) {
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
   // weights: lane j exponentiates selection j; the sum runs over j in order
   float ex = 0.0f, top = 0.0f;
   int myid = 0, mypos = -1;
@@ -242,6 +250,15 @@ __device__ __forceinline__ TopkSlot topk_select(const TopkVals<VPL> &tv, int E, 
   if (lane < k) return TopkSlot{myid, mypos, wl};
   if (add_shared && lane == k) return TopkSlot{E, k, 1.0f};
   return TopkSlot{0x7FFFFFFF, -1, 0.0f};
+}
+
+template <int VPL, int TAU_BITS = 1, int TAU_LOW = 0>
+__device__ __forceinline__ TopkSlot topk_select(const TopkVals<VPL> &tv, int E, int k, int add_shared,
+                                            int32_t *__restrict__ ids, float *__restrict__ w, int32_t *ids_copy,
+                                            float *w_copy, TopkLds &S) {
+  topk_choose<VPL, TAU_BITS, TAU_LOW>(tv, E, k, S);
+  __builtin_amdgcn_wave_barrier();
+  return topk_weights(E, k, add_shared, ids, w, ids_copy, w_copy, S);
 }
 
 template <int VPL>
