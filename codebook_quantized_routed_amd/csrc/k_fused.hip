@@ -231,15 +231,14 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
   const int q = lane, lq = lane % LPR, sub = lane / LPR;
   constexpr int ipe = 64 * LPR / kWideRows;  // items per expert (inter = 64 LPR rows)
   const int n_items = kprime * ipe, nw = gridDim.x * kFusedWaves;
-  const int item0 = blockIdx.x * kFusedWaves + wave;
+  // wave w of workgroup b takes item (w / 4) G + 4 b + w % 4 (G = 4 x grid): the waves
+  // w / 4 = g of the grid (one per SIMD) hold the items of positions 4g .. 4g + 3
+  const int item0 = (wave >> 2) * (4 * (int)gridDim.x) + blockIdx.x * 4 + (wave & 3);
   WideItem It;
   int cur_tok = 0;
   // the bank's bases and sizes come from the kernel arguments (scalar loads), so the
   // only LDS read before the loads leave is the position's record
-  auto issue = [&](int item) {
-    const int p = item / ipe;
-    const int e = uniform(S.pos[p].e), slot = uniform(S.pos[p].slot);
-    const BankArgs &B = bank_of(L, e);
+  auto issue_bank = [&](const BankArgs &B, int e, int p, int slot, int item) {
     It.W = WorkRec{e, p, p + 1, slot};
     const QMat Wg = global_mat(expert_mat(B, e, kGate, I, H)), Wu = global_mat(expert_mat(B, e, kUp, I, H));
     if constexpr (FMT == MOE_Q_IQ2XS_LIKE || FMT == MOE_Q_IQ1M_LIKE)
@@ -247,9 +246,27 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
     else
       wide_issue_mats(It, Wg, Wu, uniform(B.qtype), H, item - p * ipe, q);
   };
+  // a layer of one bank (the usual layout) addresses its experts from fixed argument
+  // offsets, which the scalar loads can fetch before the expert is known
+  auto issue = [&](int item) {
+    const int p = item / ipe;
+    const int e = uniform(S.pos[p].e), slot = uniform(S.pos[p].slot);
+    if (L.n_banks == 1)
+      issue_bank(L.banks[0], e, p, slot, item);
+    else
+      issue_bank(bank_of(L, e), e, p, slot, item);
+  };
   // the first item's loads leave before the activations are read from LDS (its
   // addresses need only the routing records)
   if (item0 < n_items) issue(item0);
+  // on each SIMD the wave of the lowest positions goes first, so those positions' h rows
+  // are complete early and their down dots overlap the other waves' gate / up
+  if (wave < 4)
+    __builtin_amdgcn_s_setprio(3);
+  else if (wave < 8)
+    __builtin_amdgcn_s_setprio(2);
+  else
+    __builtin_amdgcn_s_setprio(1);
   X32 X;
 #pragma unroll
   for (int i = 0; i < 8; i++) {
@@ -272,7 +289,7 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
   RowRaw Rd0;
   int dqt0 = 0;
   if (down_wave && wave < kprime && tile < tiles) {
-    const PosRec &P = S.pos[uniform(S.pos_of[wave])];
+    const PosRec &P = S.pos[wave];
     const BankLds &B = S.banks[uniform(P.bank)];
     const QMat Wd = bank_mat(B, uniform(P.e), kDown);
     dqt0 = uniform(B.qt);
@@ -293,9 +310,8 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
   for (bool first = true; tile < tiles; tile += gridDim.x, first = false) {
 #pragma unroll 1
     for (int i = 0; i < kFusedSlotsPerWave; i++) {
-      const int j = wave + kDownWaves * i;
-      if (!down_wave || j >= kprime) break;
-      const int pj = uniform(S.pos_of[j]);
+      const int pj = wave + kDownWaves * i;  // sorted position
+      if (!down_wave || pj >= kprime) break;
       RowRaw R;
       int qt;
       if (first && i == 0) {
@@ -491,12 +507,24 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_stack_decode(
   };
   // ---- 1. the wave's first gate / up item of layer 0 (of later layers: issued during
   // the previous layer's accumulation, as soon as that layer's routing is visible)
-  if (item_wave && blockIdx.x * kDownWaves + wave < n_items) issue(S.route[0], S.banks[0], blockIdx.x * kDownWaves + wave, lane);
+  // item of wave w of workgroup b: waves 0-3, 4-7 and 8-10 (one per SIMD each) take the
+  // items of positions 0-3, 4-7 and 8-10 in that order of priority, so those positions'
+  // h rows are complete in turn and their down dots overlap the later items
+  auto first_item = [&](int b, int wv) {
+    return wv < 8 ? (wv >> 2) * (4 * (int)gridDim.x) + 4 * b + (wv & 3) : 8 * (int)gridDim.x + 3 * b + (wv - 8);
+  };
+  if (wave < 4)
+    __builtin_amdgcn_s_setprio(3);
+  else if (wave < 8)
+    __builtin_amdgcn_s_setprio(2);
+  else
+    __builtin_amdgcn_s_setprio(1);
+  if (item_wave && first_item(blockIdx.x, wave) < n_items) issue(S.route[0], S.banks[0], first_item(blockIdx.x, wave), lane);
   int cur = 0;
   for (int l = 0; l < n_layers; l++, cur ^= 1) {
     // the lane and item indices are hidden from loop-invariant code motion: hoisted out
     // of the layer loop, every address derived from them stayed live for all layers
-    int q = lane, item0 = blockIdx.x * kDownWaves + wave, tid = threadIdx.x;
+    int q = lane, item0 = first_item(blockIdx.x, wave), tid = threadIdx.x;
     asm volatile("" : "+v"(q));
     asm volatile("" : "+s"(item0));
     asm volatile("" : "+v"(tid));
@@ -553,9 +581,8 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_stack_decode(
     auto tile_down = [&](int tile) {
 #pragma unroll 1
       for (int i = 0; i < kFusedSlotsPerWave; i++) {
-        const int j = wave + kDownWaves * i;
-        if (!item_wave || j >= kprime) break;
-        const int pj = uniform(R.pos_of[j]);
+        const int pj = wave + kDownWaves * i;  // sorted position
+        if (!item_wave || pj >= kprime) break;
         const PosRec &P = R.pos[pj];
         const BankLds &B = Bk[uniform(P.bank)];
         const QMat Wd = bank_mat(B, uniform(P.e), kDown);
