@@ -243,6 +243,11 @@ LAYER_CASES = {
     "dec_h1024_iq1_t4_zipf": ([(IQ1, 16)], 1024, 512, 16, 0, 4, 4, 1.0),
     # every expert takes all 8 tokens: the 16-row A operand full
     "dec_every_expert_all_tokens": ([(IQ2, 4)], 2048, 512, 4, 1, 8, 4, 0.0),
+    # one token, 16 experts + the shared one: 17 x 256 gate / up items, more than the
+    # one-launch grid has waves (second items), and two sorted positions per down wave;
+    # one bank (addresses from fixed argument offsets) and two banks
+    "decode_top16_shared_iq2": ([(IQ2, 64)], 2048, 512, 64, 1, 1, 16, 0.0),
+    "decode_top16_shared_mixed": ([(IQ2, 32), (IQ1, 32)], 2048, 512, 64, 1, 1, 16, 0.0),
 }
 
 
@@ -383,7 +388,8 @@ def call_counts(ws):
 
 
 FUSED_CASES = ["decode_iq2_top10_shared", "tiny16_top4_iq2", "mixed_h2048_t24_zipf", "decode_mixed_i256_shared",
-               "decode_iq1s_top10_shared", "decode_iq1_i256", "decode_iq2_i256"]
+               "decode_iq1s_top10_shared", "decode_iq1_i256", "decode_iq2_i256", "decode_top16_shared_iq2",
+               "decode_top16_shared_mixed"]
 
 
 @pytest.mark.parametrize("name", FUSED_CASES)
