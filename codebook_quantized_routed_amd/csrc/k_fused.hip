@@ -281,6 +281,31 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
       wide_run<MOE_Q_IQ1M_LIKE, true>(L, It, X, cur_tok, q, kprime, XSource{x, H, 32}, sorted_slot, lds, TL, h, tag);
   }
 
+  // ---- the grouping outputs of moe_route_group (one token: every count is 0 or 1),
+  // from the last wave, which takes no down position, while the others run the down
+  // phase: counts and offsets spread over the workgroups, the rest from workgroup 0
+  if (wave == kFusedWaves - 1) {
+    for (int e = blockIdx.x + gridDim.x * lane; e < n_ids; e += gridDim.x * 64) {
+      int below = 0, at = 0;
+      for (int j = 0; j < kprime; j++) {
+        below += S.ids[j] < e ? 1 : 0;
+        at += S.ids[j] == e ? 1 : 0;
+      }
+      counts[e] = at;
+      offsets[e] = below;
+    }
+    if (blockIdx.x == 0 && lane < kprime) {
+      const int p = lane, slot = S.slot_at[p];
+      sorted_slot[p] = slot;
+      slot_pos[slot] = p;
+      work[1 + p] = WorkRec{S.ids[slot], p, p + 1, slot};
+      if (p == 0) {
+        offsets[n_ids] = kprime;
+        work[0] = WorkRec{kprime, kprime, 0, 0};
+      }
+    }
+  }
+
   // ---- 3. the down rows of the wave's first slot (slot = wave) in the workgroup's first
   // block, and its acc values, are loaded as soon as the wave's gate / up work is done
   const int tiles = H / RPP;
@@ -353,28 +378,6 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
       acc[r] = a;
     }
     __syncthreads();
-  }
-
-  // ---- 5. the grouping outputs of moe_route_group (one token: every count is 0 or 1):
-  // counts and offsets spread over the workgroups, the rest from workgroup 0
-  for (int e = blockIdx.x + gridDim.x * threadIdx.x; e < n_ids; e += gridDim.x * blockDim.x) {
-    int below = 0, at = 0;
-    for (int j = 0; j < kprime; j++) {
-      below += S.ids[j] < e ? 1 : 0;
-      at += S.ids[j] == e ? 1 : 0;
-    }
-    counts[e] = at;
-    offsets[e] = below;
-  }
-  if (blockIdx.x == 0 && threadIdx.x < kprime) {
-    const int p = threadIdx.x, slot = S.slot_at[p];
-    sorted_slot[p] = slot;
-    slot_pos[slot] = p;
-    work[1 + p] = WorkRec{S.ids[slot], p, p + 1, slot};
-    if (p == 0) {
-      offsets[n_ids] = kprime;
-      work[0] = WorkRec{kprime, kprime, 0, 0};
-    }
   }
 }
 
