@@ -7,14 +7,15 @@
 //
 //  1. every workgroup selects the same experts (top-k of the token's logits, or the
 //     caller's explicit list) -- no exchange is needed for routing; the routing
-//     outputs of moe_route_group are written at the end;
-//  2. gate / up items (2 rows of one expert) are dealt to the waves of the whole grid;
-//     each h value goes to global memory in sorted order, paired with the call's tag
-//     in one 64-bit agent-scope atomic store;
+//     outputs of moe_route_group are written by a wave with no down work meanwhile;
+//  2. gate / up items (2 rows of one expert) are dealt to the waves of the whole grid,
+//     the items of the first sorted positions to the waves of the highest issue
+//     priority; each h value goes to global memory in sorted order, paired with the
+//     call's tag in one 64-bit agent-scope atomic store;
 //  3. down + the weighted accumulation in ascending expert id for the workgroup's
-//     block of output rows: a wave reads the h row of its slot as soon as its own
-//     gate / up work is done, and reads again the values whose tag is not yet the
-//     call's (their writers have not finished), so no grid-wide barrier is needed.
+//     block of output rows: a wave reads the h row of its sorted position as soon as
+//     its own gate / up work is done, and reads again the values whose tag is not yet
+//     the call's (their writers have not finished), so no grid-wide barrier is needed.
 // The call's tag comes from a per-call count: each workgroup adds one to its group's
 // counter at the start, and every launch on a device has the same number of
 // workgroups, so each call moves every counter by exactly one round.
@@ -306,8 +307,9 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
     }
   }
 
-  // ---- 3. the down rows of the wave's first slot (slot = wave) in the workgroup's first
-  // block, and its acc values, are loaded as soon as the wave's gate / up work is done
+  // ---- 3. the down rows of the wave's first sorted position (position = wave) in the
+  // workgroup's first block, and its acc values, are loaded as soon as the wave's
+  // gate / up work is done
   const int tiles = H / RPP;
   int tile = blockIdx.x;
   const bool down_wave = wave < kDownWaves;
@@ -330,8 +332,8 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
     if (lane < kprime) S.wpos[ts.pos] = ts.w;
   }
 
-  // ---- 4. down + accumulation, block by block of RPP output rows; a wave takes slots
-  // wave, wave + kDownWaves, ... one after the other
+  // ---- 4. down + accumulation, block by block of RPP output rows; a wave takes the
+  // sorted positions wave, wave + kDownWaves, ... one after the other
   for (bool first = true; tile < tiles; tile += gridDim.x, first = false) {
 #pragma unroll 1
     for (int i = 0; i < kFusedSlotsPerWave; i++) {
