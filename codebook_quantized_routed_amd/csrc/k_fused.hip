@@ -88,7 +88,6 @@ struct FusedLds {
   int32_t ids[kFusedMaxSlots];         // slot j -> expert
   float w[kFusedMaxSlots];             // slot j -> router weight
   int32_t slot_at[kFusedMaxSlots];     // sorted position p -> slot
-  int32_t pos_of[kFusedMaxSlots];      // slot j -> sorted position
   float wpos[kFusedMaxSlots];          // sorted position p -> router weight
   float ydot[kFusedMaxSlots][16];      // down outputs of the block's rows, per sorted position
   float xs[64 * kXsRow];               // the token's activations, lane l's 32 at l * kXsRow
@@ -210,7 +209,6 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
     const int rank = logits ? (lane < k ? S.topk.sel_pos[lane] : (shared_lane ? k : -1)) : slot_rank(my, lane);
     if (lane < kprime) {
       if (logits) S.ids[lane] = my;
-      S.pos_of[lane] = rank;
       S.slot_at[rank] = lane;
       S.pos[rank] = PosRec{my, lane, bank_index(L, my), 0};
       if (!logits) S.wpos[rank] = S.w[lane];
@@ -328,7 +326,7 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
   // wave 0: the router weights of the selection (the arithmetic of topk_select), read
   // by the accumulation after the down phase's barrier
   if (wave == 0 && logits) {
-    const TopkSlot ts = topk_weights(E, k, add_shared, blockIdx.x == 0 ? ids : nullptr, w, nullptr, S.w, S.topk);
+    const TopkSlot ts = topk_weights(E, k, add_shared, blockIdx.x == 0 ? ids : nullptr, w, nullptr, nullptr, S.topk);
     if (lane < kprime) S.wpos[ts.pos] = ts.w;
   }
 
@@ -406,11 +404,7 @@ __global__ void __launch_bounds__(64 * kFusedWaves) k_layer_decode(LayerArgs L, 
 // k_rmsnorm followed by k_layer_decode, so the result is the same bits as that chain.
 
 struct RouteLds {
-  PosRec pos[kFusedMaxSlots];
-  int32_t ids[kFusedMaxSlots];
-  float w[kFusedMaxSlots];
-  int32_t slot_at[kFusedMaxSlots];
-  int32_t pos_of[kFusedMaxSlots];
+  PosRec pos[kFusedMaxSlots];  // sorted position -> its expert
   float wpos[kFusedMaxSlots];  // sorted position -> router weight
 };
 
@@ -433,12 +427,10 @@ __device__ inline void route_wave(const float *logits, const LayerArgs &L, int E
   const TopkVals<8> tv = topk_load<8>(logits, E);
   // positions by counting, not the ones the top-k returns: with those, this kernel (at
   // its register limit) was scheduled 8 % slower
-  const TopkSlot ts = topk_select<8, 2, 16>(tv, E, k, add_shared, ids_out, w_out, R.ids, R.w, T);
+  const TopkSlot ts = topk_select<8, 2, 16>(tv, E, k, add_shared, ids_out, w_out, nullptr, nullptr, T);
   const int my = ts.id;
   const int rank = slot_rank(my, lane);
   if (lane < kprime) {
-    R.pos_of[lane] = rank;
-    R.slot_at[rank] = lane;
     R.pos[rank] = PosRec{my, lane, bank_index(L, my), 0};
     R.wpos[rank] = ts.w;
   }
